@@ -1,0 +1,189 @@
+/*
+ * wide.h -- C ABI of the masked group-mask layer library (libwide.so).
+ *
+ * The library executes the routed operators of one transformer layer whose
+ * tokens carry binary group masks, as defined in "WIDE: Boosting Adaptive LLM
+ * Inference via Token-level Dynamic Width Pruning" (arXiv 2607.28418):
+ *   - mask reordering            (section 3.3, Eq. 7; Appendix B, Algorithm 1)
+ *   - GEMM-MN, N-axis routing    (Figure 1; Appendix B, Algorithm 2)
+ *   - GEMM-K, K-axis routing     (Appendix B, Eq. 21 and Algorithm 3)
+ *   - head-group-masked attention (section 3.1, Eq. 2; Appendix B, Algorithm 4)
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * Common conventions
+ *   - Every pointer argument is a DEVICE pointer owned by the caller. The
+ *     library never allocates, frees or keeps caller memory; its only scratch
+ *     is the attention workspace the caller passes in.
+ *   - bf16 tensors are raw IEEE bfloat16 bits (wide_bf16). Matrices are
+ *     row-major with the given leading dimension (in elements). Weights are
+ *     [out_features][in_features], so every GEMM computes C = A * B^T with
+ *     A [M][K] and B [N][K] (section 3.3).
+ *   - Masks are uint8, token-major [rows][groups]; any nonzero byte means the
+ *     group is active for that token (class 0 of the router, section 3.1,
+ *     Eq. 5).
+ *   - All work is enqueued on `stream` (a hipStream_t; NULL = default stream)
+ *     and is asynchronous. The library never synchronises the stream and never
+ *     reads mask-derived values on the host, so the calls can be captured in a
+ *     HIP graph (section 3.3 names the device-to-host sync of the naive method
+ *     as its first cost).
+ *   - Each call returns a wide_status. Arguments are validated on the host
+ *     before anything is launched; on an error nothing is launched and no
+ *     output is touched.
+ *   - Floating-point products accumulate in fp32 on the MFMA units; softmax
+ *     runs in fp32.
+ */
+#ifndef WIDE_H
+#define WIDE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef uint16_t wide_bf16;     /* raw bfloat16 bits */
+typedef void *wide_stream_t;    /* hipStream_t */
+
+typedef enum {
+  WIDE_OK = 0,
+  WIDE_ERR_INVALID_ARG = -1,   /* null pointer, bad size, misalignment, aliasing */
+  WIDE_ERR_UNSUPPORTED = -2,   /* valid request this build does not implement */
+  WIDE_ERR_NO_DEVICE = -3,     /* no usable HIP device */
+  WIDE_ERR_LAUNCH = -4         /* the HIP runtime rejected a kernel launch */
+} wide_status;
+
+typedef enum { WIDE_DTYPE_BF16 = 0, WIDE_DTYPE_F32 = 1 } wide_dtype;
+
+/*
+ * wide_reorder -- mask reordering (section 3.3, Eq. 7; Appendix B,
+ * Algorithm 1).
+ *
+ * For every routing column (b, g), stable-partitions the row indices so that
+ * the rows whose mask byte is nonzero come first, in ascending order, followed
+ * by the other rows in ascending order. The reordered mask of the page is then
+ * implied: it is 1 exactly at the first counts[b][g] positions.
+ *
+ *   mask   [batch][rows][groups] uint8, nonzero = active.
+ *   perm   out, [batch][groups][rows] int32: perm[b][g][j] is the physical row
+ *          of logical row j of column (b, g).
+ *   counts out, [batch][groups] int32: number of active rows of column (b, g).
+ *
+ * For the GEMMs the token dimension is flattened (batch = 1, rows = B*T); for
+ * attention each sequence keeps its own column (batch = B, rows = Tq). With
+ * B = 1 the two coincide and one call serves both.
+ * Errors: WIDE_ERR_INVALID_ARG for null pointers, batch/rows/groups < 1, or
+ * rows >= 2^31; WIDE_ERR_LAUNCH if the launch fails.
+ */
+int wide_reorder(const uint8_t *mask, int64_t batch, int64_t rows, int64_t groups,
+                 int32_t *perm, int32_t *counts, wide_stream_t stream);
+
+/*
+ * wide_gemm_mn -- N-axis routed GEMM, GEMM-MN (Figure 1; Appendix B,
+ * Algorithm 2).
+ *
+ *   C[m][n] = sum_k A[m][k] * B[n][k]   if token m keeps group g = n / G,
+ *   C[m][n] is NOT written              otherwise.
+ *
+ *   A  [M][K] bf16, leading dim lda;  B [N][K] bf16, leading dim ldb.
+ *   C  [M][N], leading dim ldc, element type c_dtype (WIDE_DTYPE_BF16: one
+ *      round-to-nearest-even of the fp32 sum; WIDE_DTYPE_F32: the fp32 sum).
+ *   G  group size; N must be a multiple of G.
+ *   perm, counts: the output of wide_reorder(mask, 1, M, N/G, ...). Row tiles
+ *      wholly past counts[g] exit at once; rows past it are neither loaded
+ *      nor multiplied.
+ *   mask [M][N/G]: used only when perm == NULL, which selects the
+ *      matrix-vector path for M <= 4 (one decode step needs no reorder).
+ * Entries of inactive (token, group) pairs are left untouched: the caller
+ * zero-initialises C when it needs zeros there (Algorithm 2 takes a
+ * zero-initialised C).
+ * Requirements: K % 8 == 0; lda, ldb >= K and multiples of 8; ldc >= N;
+ * A, B, C 16-byte aligned; G % 64 == 0 (WIDE_ERR_UNSUPPORTED otherwise);
+ * C must not overlap A or B.
+ */
+int wide_gemm_mn(const wide_bf16 *A, int64_t lda, const wide_bf16 *B, int64_t ldb,
+                 void *C, int64_t ldc, int c_dtype, int64_t M, int64_t N, int64_t K,
+                 int64_t G, const int32_t *perm, const int32_t *counts,
+                 const uint8_t *mask, wide_stream_t stream);
+
+/*
+ * wide_gemm_mn_swiglu -- the FFN gate and up projections fused with the
+ * activation (section 3.1, Eq. 3, with phi = SiLU):
+ *
+ *   H[m][n] = SiLU(sum_k A[m][k] Wg[n][k]) * (sum_k A[m][k] Wu[n][k])
+ *   for active (m, n / G); other entries are not written.
+ *
+ * Both products accumulate in fp32; the activation is applied in fp32 and H
+ * is rounded once to h_dtype. Wg and Wu are [N][K] with the same leading dim
+ * ldb. Arguments and requirements otherwise as wide_gemm_mn.
+ */
+int wide_gemm_mn_swiglu(const wide_bf16 *A, int64_t lda, const wide_bf16 *Wg,
+                        const wide_bf16 *Wu, int64_t ldb, void *H, int64_t ldh,
+                        int h_dtype, int64_t M, int64_t N, int64_t K, int64_t G,
+                        const int32_t *perm, const int32_t *counts,
+                        const uint8_t *mask, wide_stream_t stream);
+
+/*
+ * wide_gemm_k -- K-axis routed GEMM, GEMM-K (Appendix B, Eq. 21 and
+ * Algorithm 3):
+ *
+ *   C[m][n] = beta * C[m][n]
+ *           + sum_g mask[m][g] * sum_{k in [gG, (g+1)G)} A[m][k] * B[n][k]
+ *
+ *   A [M][K] bf16 (lda), B [N][K] bf16 (ldb), C [M][N] fp32 (ldc).
+ *   mask [M][K/G] uint8. beta is 0 or 1. With beta = 0 every entry of C is
+ *   written, exact 0 for rows with no active group.
+ * Each output tile compacts the active rows of every K-group from the mask
+ * itself, so no reorder output is needed. Summation order is fixed: results
+ * are bitwise reproducible run to run.
+ * Requirements: K % G == 0; G % 64 == 0; N % 64 == 0; lda, ldb >= K and
+ * multiples of 8; ldc >= N; 16-byte aligned A, B, C; C must not overlap A or B.
+ */
+int wide_gemm_k(const wide_bf16 *A, int64_t lda, const wide_bf16 *B, int64_t ldb,
+                float *C, int64_t ldc, int beta, int64_t M, int64_t N, int64_t K,
+                int64_t G, const uint8_t *mask, wide_stream_t stream);
+
+/*
+ * wide_attn -- head-group-masked causal GQA attention (section 3.1, Eq. 2;
+ * Appendix B, Algorithm 4 and its decoding paragraph).
+ *
+ *   Q [B][Tq][Hq][d], K and V [B][Tk][Hk][d] bf16, contiguous.
+ *   O [B][Tq][Hq][d], element type o_dtype (bf16 or fp32).
+ * Query head h reads KV head g = h / (Hq/Hk) and is gated by routing group g
+ * (the attention group size is (Hq/Hk)*d). For an active (b, t, g) and every
+ * head h of group g:
+ *   O[b][t][h] = sum_j softmax_j(scale * <Q[b][t][h], K[b][j][g]>) V[b][j][g]
+ * over the valid keys j in [jmin, jmax): jmin = leftpad[b] (0 if leftpad is
+ * NULL); jmax = t + (Tk - Tq) + 1 if causal (bottom-right aligned), else Tk.
+ * A row with no valid key gets O = 0. Rows of inactive groups are not written.
+ *   scale: softmax scale; 0 selects 1/sqrt(d).
+ *   perm, counts: wide_reorder(mask, B, Tq, Hk, ...) output ([B][Hk][Tq] and
+ *     [B][Hk]); required for Tq > 1.
+ *   mask [B][Tq][Hk]: used when perm == NULL; then Tq must be 1 (decoding
+ *     reads the routing bytes directly; no reorder runs).
+ *   workspace: device scratch of at least wide_attn_workspace_bytes(...)
+ *     bytes (0 bytes for Tq > 1); may be NULL when that is 0.
+ * Requirements: d == 128; Hq % Hk == 0; Tk >= Tq >= 1; 16-byte aligned
+ * Q, K, V, O; O must not overlap Q, K or V.
+ */
+int wide_attn(const wide_bf16 *Q, const wide_bf16 *K, const wide_bf16 *V, void *O,
+              int o_dtype, int64_t B, int64_t Tq, int64_t Tk, int64_t Hq, int64_t Hk,
+              int64_t d, int causal, float scale, const int32_t *leftpad,
+              const int32_t *perm, const int32_t *counts, const uint8_t *mask,
+              void *workspace, size_t workspace_bytes, wide_stream_t stream);
+
+/* Bytes of device workspace wide_attn needs for these sizes (0 if none). */
+size_t wide_attn_workspace_bytes(int64_t B, int64_t Tq, int64_t Tk, int64_t Hq,
+                                 int64_t Hk, int64_t d);
+
+/* Static, human-readable text for a wide_status value. */
+const char *wide_status_string(int status);
+
+/* ABI version: bumped on any incompatible change of the declarations above. */
+int wide_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WIDE_H */

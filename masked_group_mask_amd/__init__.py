@@ -1,0 +1,13 @@
+"""Masked group-mask layer execution (WIDE) for AMD Instinct MI355X.
+
+The compute lives in libwide.so (hand-written HIP kernels for gfx950 behind
+the C ABI of include/wide.h); this package holds that library, its ctypes
+binding and the seeded synthetic workload generators.
+"""
+from ._lib import (  # noqa: F401
+    WideError, attn, attn_workspace_bytes, gemm_k, gemm_mn, gemm_mn_swiglu, load, reorder,
+    status_string,
+)
+
+__all__ = ["WideError", "attn", "attn_workspace_bytes", "gemm_k", "gemm_mn", "gemm_mn_swiglu",
+           "load", "reorder", "status_string"]

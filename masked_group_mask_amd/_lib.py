@@ -1,0 +1,257 @@
+"""ctypes binding of libwide.so.
+
+Argument marshalling only: tensors are checked for device, dtype, shape and
+layout, and their device pointers and the current HIP stream are handed to the
+C ABI declared in include/wide.h. Every computation runs in the library's HIP
+kernels; there is no fallback. If the library is missing, loading raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libwide.so")
+
+WIDE_DTYPE_BF16 = 0
+WIDE_DTYPE_F32 = 1
+
+_i64 = ctypes.c_int64
+_int = ctypes.c_int
+_ptr = ctypes.c_void_p
+_size = ctypes.c_size_t
+_f32 = ctypes.c_float
+
+_SIGS = {
+    "wide_reorder": [_ptr, _i64, _i64, _i64, _ptr, _ptr, _ptr],
+    "wide_gemm_mn": [_ptr, _i64, _ptr, _i64, _ptr, _i64, _int, _i64, _i64, _i64, _i64,
+                     _ptr, _ptr, _ptr, _ptr],
+    "wide_gemm_mn_swiglu": [_ptr, _i64, _ptr, _ptr, _i64, _ptr, _i64, _int, _i64, _i64, _i64,
+                            _i64, _ptr, _ptr, _ptr, _ptr],
+    "wide_gemm_k": [_ptr, _i64, _ptr, _i64, _ptr, _i64, _int, _i64, _i64, _i64, _i64, _ptr, _ptr],
+    "wide_attn": [_ptr, _ptr, _ptr, _ptr, _int, _i64, _i64, _i64, _i64, _i64, _i64, _int, _f32,
+                  _ptr, _ptr, _ptr, _ptr, _ptr, _size, _ptr],
+    "wide_attn_workspace_bytes": [_i64] * 6,
+    "wide_status_string": [_int],
+    "wide_abi_version": [],
+}
+_RESTYPES = {"wide_attn_workspace_bytes": _size, "wide_status_string": ctypes.c_char_p}
+
+EXPORTED = tuple(_SIGS)
+
+_lib = None
+
+
+class WideError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed: {status_string(status)} ({status})")
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libwide.so (once). Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with masked_group_mask_amd.build.build()")
+    lib = ctypes.CDLL(path)
+    for name, args in _SIGS.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = _RESTYPES.get(name, _int)
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().wide_status_string(status).decode()
+
+
+def _call(name: str, *args) -> None:
+    st = getattr(load(), name)(*args)
+    if st != 0:
+        raise WideError(name, st)
+
+
+def _p(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream() -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype, ndim: Optional[int] = None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions, got {t.dim()}")
+
+
+def _rowmajor(t: torch.Tensor, name: str) -> int:
+    """Leading dimension of a 2-D tensor whose rows are contiguous."""
+    if t.stride(1) != 1:
+        raise ValueError(f"{name} rows must be contiguous")
+    return t.stride(0)
+
+
+def _dt(dtype) -> int:
+    if dtype == torch.bfloat16:
+        return WIDE_DTYPE_BF16
+    if dtype == torch.float32:
+        return WIDE_DTYPE_F32
+    raise TypeError(f"unsupported output dtype {dtype}")
+
+
+# ---------------------------------------------------------------------------
+
+
+def reorder(mask: torch.Tensor, perm: Optional[torch.Tensor] = None,
+            counts: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """mask [B][T][NG] uint8 -> (perm [B][NG][T] int32, counts [B][NG] int32)."""
+    _need(mask, "mask", torch.uint8, 3)
+    mask = mask.contiguous()
+    B, T, NG = mask.shape
+    if perm is None:
+        perm = torch.empty((B, NG, T), dtype=torch.int32, device=mask.device)
+    if counts is None:
+        counts = torch.empty((B, NG), dtype=torch.int32, device=mask.device)
+    _need(perm, "perm", torch.int32, 3)
+    _need(counts, "counts", torch.int32, 2)
+    if tuple(perm.shape) != (B, NG, T) or tuple(counts.shape) != (B, NG):
+        raise ValueError("perm/counts shape mismatch")
+    if not (perm.is_contiguous() and counts.is_contiguous()):
+        raise ValueError("perm/counts must be contiguous")
+    _call("wide_reorder", _p(mask), B, T, NG, _p(perm), _p(counts), _stream())
+    return perm, counts
+
+
+def _mn_common(A, G, perm, counts, mask):
+    _need(A, "A", torch.bfloat16, 2)
+    lda = _rowmajor(A, "A")
+    if perm is not None:
+        _need(perm, "perm", torch.int32)
+        _need(counts, "counts", torch.int32)
+        if not (perm.is_contiguous() and counts.is_contiguous()):
+            raise ValueError("perm/counts must be contiguous")
+    if mask is not None:
+        _need(mask, "mask", torch.uint8)
+        if not mask.is_contiguous():
+            raise ValueError("mask must be contiguous")
+    return lda
+
+
+def gemm_mn(A: torch.Tensor, B: torch.Tensor, G: int, perm: Optional[torch.Tensor] = None,
+            counts: Optional[torch.Tensor] = None, mask: Optional[torch.Tensor] = None,
+            out: Optional[torch.Tensor] = None, out_dtype=torch.bfloat16) -> torch.Tensor:
+    """C = A B^T on the active (token, group) entries; others keep `out`'s values
+    (zeros if `out` is allocated here)."""
+    lda = _mn_common(A, G, perm, counts, mask)
+    _need(B, "B", torch.bfloat16, 2)
+    ldb = _rowmajor(B, "B")
+    M, K = A.shape
+    N = B.shape[0]
+    if B.shape[1] != K:
+        raise ValueError("A and B disagree on K")
+    if out is None:
+        out = torch.zeros((M, N), dtype=out_dtype, device=A.device)
+    _need(out, "out", out.dtype, 2)
+    if tuple(out.shape) != (M, N):
+        raise ValueError("out shape mismatch")
+    _call("wide_gemm_mn", _p(A), lda, _p(B), ldb, _p(out), _rowmajor(out, "out"), _dt(out.dtype),
+          M, N, K, G, _p(perm), _p(counts), _p(mask), _stream())
+    return out
+
+
+def gemm_mn_swiglu(A: torch.Tensor, Wg: torch.Tensor, Wu: torch.Tensor, G: int,
+                   perm: Optional[torch.Tensor] = None, counts: Optional[torch.Tensor] = None,
+                   mask: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                   out_dtype=torch.bfloat16) -> torch.Tensor:
+    """H = SiLU(A Wg^T) * (A Wu^T) on the active entries."""
+    lda = _mn_common(A, G, perm, counts, mask)
+    _need(Wg, "Wg", torch.bfloat16, 2)
+    _need(Wu, "Wu", torch.bfloat16, 2)
+    ldb = _rowmajor(Wg, "Wg")
+    if Wu.shape != Wg.shape or _rowmajor(Wu, "Wu") != ldb:
+        raise ValueError("Wg and Wu must have the same shape and leading dimension")
+    M, K = A.shape
+    N = Wg.shape[0]
+    if Wg.shape[1] != K:
+        raise ValueError("A and Wg disagree on K")
+    if out is None:
+        out = torch.zeros((M, N), dtype=out_dtype, device=A.device)
+    if tuple(out.shape) != (M, N):
+        raise ValueError("out shape mismatch")
+    _call("wide_gemm_mn_swiglu", _p(A), lda, _p(Wg), _p(Wu), ldb, _p(out),
+          _rowmajor(out, "out"), _dt(out.dtype), M, N, K, G, _p(perm), _p(counts), _p(mask),
+          _stream())
+    return out
+
+
+def gemm_k(A: torch.Tensor, B: torch.Tensor, G: int, mask: torch.Tensor,
+           out: Optional[torch.Tensor] = None, beta: int = 0) -> torch.Tensor:
+    """C = beta*C + sum over active K-groups of A B^T (fp32 output)."""
+    _need(A, "A", torch.bfloat16, 2)
+    _need(B, "B", torch.bfloat16, 2)
+    _need(mask, "mask", torch.uint8)
+    if not mask.is_contiguous():
+        raise ValueError("mask must be contiguous")
+    M, K = A.shape
+    N = B.shape[0]
+    if B.shape[1] != K:
+        raise ValueError("A and B disagree on K")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=A.device)
+        beta = 0
+    _need(out, "out", torch.float32, 2)
+    if tuple(out.shape) != (M, N):
+        raise ValueError("out shape mismatch")
+    _call("wide_gemm_k", _p(A), _rowmajor(A, "A"), _p(B), _rowmajor(B, "B"), _p(out),
+          _rowmajor(out, "out"), int(beta), M, N, K, G, _p(mask), _stream())
+    return out
+
+
+def attn_workspace_bytes(B: int, Tq: int, Tk: int, Hq: int, Hk: int, d: int) -> int:
+    return int(load().wide_attn_workspace_bytes(B, Tq, Tk, Hq, Hk, d))
+
+
+def attn(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, perm: Optional[torch.Tensor] = None,
+         counts: Optional[torch.Tensor] = None, mask: Optional[torch.Tensor] = None,
+         causal: bool = True, scale: float = 0.0, leftpad: Optional[torch.Tensor] = None,
+         out: Optional[torch.Tensor] = None, out_dtype=torch.bfloat16,
+         workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Head-group-masked GQA attention; Q [B][Tq][Hq][d], K/V [B][Tk][Hk][d]."""
+    for t, n in ((Q, "Q"), (K, "K"), (V, "V")):
+        _need(t, n, torch.bfloat16, 4)
+        if not t.is_contiguous():
+            raise ValueError(f"{n} must be contiguous")
+    B, Tq, Hq, d = Q.shape
+    Bk, Tk, Hk, dk = K.shape
+    if Bk != B or dk != d or tuple(V.shape) != tuple(K.shape):
+        raise ValueError("Q/K/V shapes disagree")
+    for t, n, dt in ((perm, "perm", torch.int32), (counts, "counts", torch.int32),
+                     (mask, "mask", torch.uint8), (leftpad, "leftpad", torch.int32)):
+        if t is not None:
+            _need(t, n, dt)
+            if not t.is_contiguous():
+                raise ValueError(f"{n} must be contiguous")
+    if out is None:
+        out = torch.zeros((B, Tq, Hq, d), dtype=out_dtype, device=Q.device)
+    if tuple(out.shape) != (B, Tq, Hq, d) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [B][Tq][Hq][d] tensor")
+    need = attn_workspace_bytes(B, Tq, Tk, Hq, Hk, d)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=Q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _call("wide_attn", _p(Q), _p(K), _p(V), _p(out), _dt(out.dtype), B, Tq, Tk, Hq, Hk, d,
+          int(bool(causal)), float(scale), _p(leftpad), _p(perm), _p(counts), _p(mask),
+          _p(workspace), ws_bytes, _stream())
+    return out

@@ -1,0 +1,198 @@
+// C ABI of libwide.so: host-side argument validation and dispatch.
+// Every check runs before any HIP call, so an invalid request returns an
+// error without touching the device or the caller's buffers.
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <atomic>
+
+#include "launch.hpp"
+
+namespace {
+
+constexpr int64_t kI32Max = 2147483647;
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Half-open byte ranges [p, p + n) and [q, q + m) intersect.
+bool overlap(const void *p, size_t n, const void *q, size_t m) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p), b = reinterpret_cast<uintptr_t>(q);
+  return a < b + m && b < a + n;
+}
+
+size_t span_bytes(int64_t rows, int64_t cols, int64_t ld, size_t esize) {
+  return (size_t)((rows - 1) * ld + cols) * esize;
+}
+
+// 1 = device present, 0 = none; probed once.
+int device_ok() {
+  static std::atomic<int> state{-1};
+  int s = state.load();
+  if (s < 0) {
+    int n = 0;
+    s = (hipGetDeviceCount(&n) == hipSuccess && n > 0) ? 1 : 0;
+    state.store(s);
+  }
+  return s;
+}
+
+bool valid_dtype(int t) { return t == WIDE_DTYPE_BF16 || t == WIDE_DTYPE_F32; }
+
+int check_mn(const wide_bf16 *A, int64_t lda, const wide_bf16 *B0, const wide_bf16 *B1,
+             int64_t ldb, const void *C, int64_t ldc, int c_dtype, int64_t M, int64_t N,
+             int64_t K, int64_t G, const int32_t *perm, const int32_t *counts,
+             const uint8_t *mask) {
+  if (!A || !B0 || !C) return WIDE_ERR_INVALID_ARG;
+  if (M < 1 || N < 1 || K < 1 || G < 1) return WIDE_ERR_INVALID_ARG;
+  if (M > kI32Max || N > kI32Max || K > kI32Max) return WIDE_ERR_INVALID_ARG;
+  if (N % G != 0 || K % 8 != 0) return WIDE_ERR_INVALID_ARG;
+  if (lda < K || ldb < K || lda % 8 != 0 || ldb % 8 != 0 || ldc < N) return WIDE_ERR_INVALID_ARG;
+  if (!valid_dtype(c_dtype)) return WIDE_ERR_INVALID_ARG;
+  if (!aligned16(A) || !aligned16(B0) || !aligned16(C) || (B1 && !aligned16(B1)))
+    return WIDE_ERR_INVALID_ARG;
+  if (perm == nullptr) {
+    if (mask == nullptr || M > 4) return WIDE_ERR_INVALID_ARG;
+  } else if (counts == nullptr) {
+    return WIDE_ERR_INVALID_ARG;
+  }
+  const size_t cb = span_bytes(M, N, ldc, c_dtype == WIDE_DTYPE_F32 ? 4 : 2);
+  if (overlap(C, cb, A, span_bytes(M, K, lda, 2)) || overlap(C, cb, B0, span_bytes(N, K, ldb, 2)) ||
+      (B1 && overlap(C, cb, B1, span_bytes(N, K, ldb, 2))))
+    return WIDE_ERR_INVALID_ARG;
+  if (G % 64 != 0) return WIDE_ERR_UNSUPPORTED;
+  return WIDE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int wide_abi_version(void) { return 1; }
+
+const char *wide_status_string(int status) {
+  switch (status) {
+    case WIDE_OK: return "ok";
+    case WIDE_ERR_INVALID_ARG: return "invalid argument";
+    case WIDE_ERR_UNSUPPORTED: return "unsupported shape or mode";
+    case WIDE_ERR_NO_DEVICE: return "no HIP device";
+    case WIDE_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int wide_reorder(const uint8_t *mask, int64_t batch, int64_t rows, int64_t groups,
+                 int32_t *perm, int32_t *counts, wide_stream_t stream) {
+  if (!mask || !perm || !counts) return WIDE_ERR_INVALID_ARG;
+  if (batch < 1 || rows < 1 || groups < 1) return WIDE_ERR_INVALID_ARG;
+  if (rows > kI32Max || groups > kI32Max || batch > 65535) return WIDE_ERR_INVALID_ARG;
+  if ((groups + 7) / 8 > kI32Max) return WIDE_ERR_INVALID_ARG;
+  const size_t mb = (size_t)batch * rows * groups;
+  if (overlap(perm, mb * 4, mask, mb) || overlap(counts, (size_t)batch * groups * 4, mask, mb) ||
+      overlap(counts, (size_t)batch * groups * 4, perm, mb * 4))
+    return WIDE_ERR_INVALID_ARG;
+  if (!device_ok()) return WIDE_ERR_NO_DEVICE;
+  return wide::launch_reorder(mask, (int)batch, (int)rows, (int)groups, perm, counts,
+                              reinterpret_cast<hipStream_t>(stream));
+}
+
+int wide_gemm_mn(const wide_bf16 *A, int64_t lda, const wide_bf16 *B, int64_t ldb, void *C,
+                 int64_t ldc, int c_dtype, int64_t M, int64_t N, int64_t K, int64_t G,
+                 const int32_t *perm, const int32_t *counts, const uint8_t *mask,
+                 wide_stream_t stream) {
+  const int st = check_mn(A, lda, B, nullptr, ldb, C, ldc, c_dtype, M, N, K, G, perm, counts, mask);
+  if (st != WIDE_OK) return st;
+  if (!device_ok()) return WIDE_ERR_NO_DEVICE;
+  wide::MnArgs a{A, lda, B, nullptr, ldb, C, ldc, c_dtype == WIDE_DTYPE_F32, (int)M, (int)N,
+                 (int)K, (int)G, perm, counts, mask};
+  return wide::launch_gemm_mn(a, reinterpret_cast<hipStream_t>(stream));
+}
+
+int wide_gemm_mn_swiglu(const wide_bf16 *A, int64_t lda, const wide_bf16 *Wg, const wide_bf16 *Wu,
+                        int64_t ldb, void *H, int64_t ldh, int h_dtype, int64_t M, int64_t N,
+                        int64_t K, int64_t G, const int32_t *perm, const int32_t *counts,
+                        const uint8_t *mask, wide_stream_t stream) {
+  if (!Wu) return WIDE_ERR_INVALID_ARG;
+  const int st = check_mn(A, lda, Wg, Wu, ldb, H, ldh, h_dtype, M, N, K, G, perm, counts, mask);
+  if (st != WIDE_OK) return st;
+  if (!device_ok()) return WIDE_ERR_NO_DEVICE;
+  wide::MnArgs a{A, lda, Wg, Wu, ldb, H, ldh, h_dtype == WIDE_DTYPE_F32, (int)M, (int)N,
+                 (int)K, (int)G, perm, counts, mask};
+  return wide::launch_gemm_mn(a, reinterpret_cast<hipStream_t>(stream));
+}
+
+int wide_gemm_k(const wide_bf16 *A, int64_t lda, const wide_bf16 *B, int64_t ldb, float *C,
+                int64_t ldc, int beta, int64_t M, int64_t N, int64_t K, int64_t G,
+                const uint8_t *mask, wide_stream_t stream) {
+  if (!A || !B || !C || !mask) return WIDE_ERR_INVALID_ARG;
+  if (M < 1 || N < 1 || K < 1 || G < 1) return WIDE_ERR_INVALID_ARG;
+  if (M > kI32Max || N > kI32Max || K > kI32Max) return WIDE_ERR_INVALID_ARG;
+  if (K % G != 0 || lda < K || ldb < K || lda % 8 != 0 || ldb % 8 != 0) return WIDE_ERR_INVALID_ARG;
+  if (ldc < N || ldc % 4 != 0 || (beta != 0 && beta != 1)) return WIDE_ERR_INVALID_ARG;
+  if (!aligned16(A) || !aligned16(B) || !aligned16(C)) return WIDE_ERR_INVALID_ARG;
+  const size_t cb = span_bytes(M, N, ldc, 4);
+  if (overlap(C, cb, A, span_bytes(M, K, lda, 2)) || overlap(C, cb, B, span_bytes(N, K, ldb, 2)) ||
+      overlap(C, cb, mask, (size_t)M * (K / G)))
+    return WIDE_ERR_INVALID_ARG;
+  if (G % 64 != 0 || K / G > 512 || N % 128 != 0) return WIDE_ERR_UNSUPPORTED;
+  if (!device_ok()) return WIDE_ERR_NO_DEVICE;
+  wide::KArgs a{A, lda, B, ldb, C, ldc, beta, (int)M, (int)N, (int)K, (int)G, mask};
+  return wide::launch_gemm_k(a, reinterpret_cast<hipStream_t>(stream));
+}
+
+size_t wide_attn_workspace_bytes(int64_t B, int64_t Tq, int64_t Tk, int64_t Hq, int64_t Hk,
+                                 int64_t d) {
+  if (B < 1 || Tq < 1 || Tk < 1 || Hq < 1 || Hk < 1 || d < 1) return 0;
+  return wide::attn_workspace_bytes(B, Tq, Tk, Hq, Hk, d);
+}
+
+int wide_attn(const wide_bf16 *Q, const wide_bf16 *K, const wide_bf16 *V, void *O, int o_dtype,
+              int64_t B, int64_t Tq, int64_t Tk, int64_t Hq, int64_t Hk, int64_t d, int causal,
+              float scale, const int32_t *leftpad, const int32_t *perm, const int32_t *counts,
+              const uint8_t *mask, void *workspace, size_t workspace_bytes,
+              wide_stream_t stream) {
+  if (!Q || !K || !V || !O) return WIDE_ERR_INVALID_ARG;
+  if (B < 1 || Tq < 1 || Tk < 1 || Hq < 1 || Hk < 1 || d < 1) return WIDE_ERR_INVALID_ARG;
+  if (B > 65535 || Hq > 65535 || Tq > kI32Max || Tk > kI32Max) return WIDE_ERR_INVALID_ARG;
+  if (Hq % Hk != 0 || Tk < Tq || !valid_dtype(o_dtype)) return WIDE_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return WIDE_ERR_INVALID_ARG;
+  if (!(scale >= 0.f) || !isfinite(scale)) return WIDE_ERR_INVALID_ARG;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O)) return WIDE_ERR_INVALID_ARG;
+  if (Tq > 1 && (!perm || !counts)) return WIDE_ERR_INVALID_ARG;
+  if (Tq == 1 && !perm && !mask) return WIDE_ERR_INVALID_ARG;
+  if (Tq == 1 && perm && !counts) return WIDE_ERR_INVALID_ARG;
+  const size_t need = wide::attn_workspace_bytes(B, Tq, Tk, Hq, Hk, d);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return WIDE_ERR_INVALID_ARG;
+  const size_t ob = (size_t)B * Tq * Hq * d * (o_dtype == WIDE_DTYPE_F32 ? 4 : 2);
+  const size_t qb = (size_t)B * Tq * Hq * d * 2, kb = (size_t)B * Tk * Hk * d * 2;
+  if (overlap(O, ob, Q, qb) || overlap(O, ob, K, kb) || overlap(O, ob, V, kb))
+    return WIDE_ERR_INVALID_ARG;
+  if (need > 0 && (overlap(workspace, need, O, ob) || overlap(workspace, need, Q, qb) ||
+                   overlap(workspace, need, K, kb) || overlap(workspace, need, V, kb)))
+    return WIDE_ERR_INVALID_ARG;
+  if (d != 128) return WIDE_ERR_UNSUPPORTED;
+  if (Tq == 1 && Hq / Hk > 8) return WIDE_ERR_UNSUPPORTED;
+  if (!device_ok()) return WIDE_ERR_NO_DEVICE;
+  wide::AttnArgs a{};
+  a.Q = Q;
+  a.K = K;
+  a.V = V;
+  a.O = O;
+  a.o_f32 = o_dtype == WIDE_DTYPE_F32;
+  a.B = (int)B;
+  a.Tq = (int)Tq;
+  a.Tk = (int)Tk;
+  a.Hq = (int)Hq;
+  a.Hk = (int)Hk;
+  a.d = (int)d;
+  a.causal = causal;
+  a.scale = scale == 0.f ? 1.0f / sqrtf((float)d) : scale;
+  a.leftpad = leftpad;
+  a.perm = perm;
+  a.counts = counts;
+  a.mask = perm ? nullptr : mask;
+  a.workspace = workspace;
+  return wide::launch_attn(a, reinterpret_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,59 @@
+// Shared device helpers for the gfx950 kernels: bf16 packing, MFMA wrappers,
+// wave-level primitives. Internal to libwide.so.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace wide {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+// D[16x16] += A[16x32] * B[32x16], bf16 inputs, fp32 accumulate.
+// Lane l supplies row (l % 16) of A and column (l % 16) of B, each with 8
+// reduction elements; the hardware pairs A's element i of lane l with B's
+// element i of lane l, so any reduction-index assignment shared by A and B is
+// valid. The result lands in lane l as column (l % 16), rows 4*(l/16) + v.
+__device__ __forceinline__ f32x4 mfma16x16x32(const u32x4 &a, const u32x4 &b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// fp32 -> bf16 bits, round to nearest even (finite values).
+__device__ __forceinline__ uint16_t f2bf(float x) {
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
+}
+
+// Two fp32 -> packed bf16x2 (low half = a).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return (uint32_t)f2bf(a) | ((uint32_t)f2bf(b) << 16);
+}
+
+__device__ __forceinline__ float bf2f(uint16_t b) {
+  return __builtin_bit_cast(float, (uint32_t)b << 16);
+}
+
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
+
+__device__ __forceinline__ u32x4 ld16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
+__device__ __forceinline__ void st16(void *p, const u32x4 &v) { *reinterpret_cast<u32x4 *>(p) = v; }
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+// Number of set bits of `m` below this lane (a wave-wide exclusive rank).
+__device__ __forceinline__ int rank_below(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+}
+
+// Read-only value shared by the whole wave (keeps it in a scalar register).
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+__device__ __forceinline__ float silu(float x) { return x / (1.0f + __expf(-x)); }
+
+}  // namespace wide

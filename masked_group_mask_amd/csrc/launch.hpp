@@ -1,0 +1,75 @@
+// Internal launcher declarations shared by the kernels and the C ABI layer.
+// Launchers assume the C ABI layer has validated every argument.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/wide.h"
+
+namespace wide {
+
+inline int check_launch() {
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? WIDE_OK : WIDE_ERR_LAUNCH;
+}
+
+// Workgroup id -> logical tile id such that consecutive logical ids run on the
+// same XCD (the dispatcher deals workgroups to the 8 XCDs round-robin), so
+// tiles that share an operand share that XCD's L2.
+__device__ __forceinline__ int xcd_remap(int p, int total) {
+  const int per = total / 8, rem = total % 8;
+  const int x = p % 8, i = p / 8;
+  return x * per + (x < rem ? x : rem) + i;
+}
+
+int launch_reorder(const uint8_t *mask, int batch, int rows, int groups, int32_t *perm,
+                   int32_t *counts, hipStream_t stream);
+
+struct MnArgs {
+  const uint16_t *A;
+  int64_t lda;
+  const uint16_t *B0;  // [N][K] weights (gate for the SwiGLU variant)
+  const uint16_t *B1;  // up weights for the SwiGLU variant, else null
+  int64_t ldb;
+  void *C;
+  int64_t ldc;
+  int c_f32;           // output is fp32 (else bf16)
+  int M, N, K, G;
+  const int32_t *perm;
+  const int32_t *counts;
+  const uint8_t *mask;
+};
+int launch_gemm_mn(const MnArgs &a, hipStream_t stream);
+
+struct KArgs {
+  const uint16_t *A;
+  int64_t lda;
+  const uint16_t *B;
+  int64_t ldb;
+  float *C;
+  int64_t ldc;
+  int beta;
+  int M, N, K, G;
+  const uint8_t *mask;
+};
+int launch_gemm_k(const KArgs &a, hipStream_t stream);
+
+struct AttnArgs {
+  const uint16_t *Q, *K, *V;
+  void *O;
+  int o_f32;
+  int B, Tq, Tk, Hq, Hk, d;
+  int causal;
+  float scale;
+  const int32_t *leftpad;
+  const int32_t *perm, *counts;
+  const uint8_t *mask;
+  void *workspace;
+};
+int launch_attn(const AttnArgs &a, hipStream_t stream);
+size_t attn_workspace_bytes(int64_t B, int64_t Tq, int64_t Tk, int64_t Hq, int64_t Hk,
+                            int64_t d);
+
+}  // namespace wide

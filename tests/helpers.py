@@ -1,0 +1,60 @@
+"""Test helpers: moving seeded numpy inputs to the device and comparing results
+with the oracle at the stated tolerances."""
+import sys
+
+import numpy as np
+
+from oracle import wide_ref as ref
+
+# GEMM outputs (fp32 stores): max |err| <= GEMM_RTOL * RMS(oracle over all entries).
+GEMM_RTOL = 1e-2
+# Attention outputs (fp32 stores): max |err| <= ATTN_ATOL.
+ATTN_ATOL = 2e-2
+
+
+def say(*a):
+    """Name the GPU case about to run (flushed, so a crash still shows it)."""
+    print("[gpu]", *a, file=sys.stderr, flush=True)
+
+
+def to_dev(x, torch):
+    """numpy array -> device tensor; uint16 arrays are bf16 bit patterns."""
+    x = np.ascontiguousarray(x)
+    if x.dtype == np.uint16:
+        return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(x).cuda()
+
+
+def bits_of(t):
+    """bf16 device tensor -> numpy uint16 bit patterns."""
+    import torch
+    return t.detach().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def f32_of(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def check_gemm(got, want, what=""):
+    rms = float(np.sqrt(np.mean(want ** 2))) if want.size else 0.0
+    err = float(np.max(np.abs(got - want))) if want.size else 0.0
+    assert err <= GEMM_RTOL * rms + 1e-30, f"{what}: max|err| {err:.3e} > 1e-2 x RMS {rms:.3e}"
+    return err, rms
+
+
+def check_attn(got, want, what=""):
+    err = float(np.max(np.abs(got - want))) if want.size else 0.0
+    assert err <= ATTN_ATOL, f"{what}: max|err| {err:.3e} > {ATTN_ATOL}"
+    return err
+
+
+def check_bf16_store(got_bits, want64, what=""):
+    """A bf16-stored result is within one bf16 step of the oracle's rounded value."""
+    want_bits = ref.to_bf16_bits(want64).astype(np.int32)
+    g = got_bits.astype(np.int32)
+    same_sign = (g >> 15) == (want_bits >> 15)
+    step = np.abs(g - want_bits)
+    ok = (same_sign & (step <= 1)) | (np.abs(ref.from_bf16(got_bits) - want64) <= 2.0 ** -8 * np.abs(want64) + 1e-30)
+    bad = np.count_nonzero(~ok)
+    assert bad == 0, f"{what}: {bad} bf16 outputs more than one step from the oracle"
+    return float(np.mean(g != want_bits))

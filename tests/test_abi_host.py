@@ -1,0 +1,139 @@
+"""Host-side checks of the C ABI (no GPU needed, no kernel is launched).
+
+The library must load, export every function declared in include/wide.h, and
+reject invalid arguments on the host before touching the device.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from masked_group_mask_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "wide.h")
+
+INVALID, UNSUPPORTED, NO_DEVICE = -1, -2, -3
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(wide_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail("libwide.so is not built; run masked_group_mask_amd.build.build()")
+    return _lib.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert {"wide_reorder", "wide_gemm_mn", "wide_gemm_k", "wide_attn"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(_lib.EXPORTED)
+
+
+def test_status_strings(lib):
+    assert _lib.status_string(0) == "ok"
+    assert _lib.status_string(INVALID) == "invalid argument"
+    assert _lib.status_string(UNSUPPORTED) == "unsupported shape or mode"
+    assert _lib.status_string(12345) == "unknown status"
+    assert lib.wide_abi_version() == 1
+
+
+FAKE = 1 << 20      # a 16-byte aligned, non-null address that is never dereferenced
+
+
+def P(i=0):
+    return ctypes.c_void_p(FAKE * (i + 1))
+
+
+def test_reorder_validation(lib):
+    assert lib.wide_reorder(None, 1, 8, 2, P(1), P(2), None) == INVALID
+    assert lib.wide_reorder(P(0), 0, 8, 2, P(1), P(2), None) == INVALID
+    assert lib.wide_reorder(P(0), 1, 8, 0, P(1), P(2), None) == INVALID
+    assert lib.wide_reorder(P(0), 1, 1 << 31, 2, P(1), P(2), None) == INVALID
+    assert lib.wide_reorder(P(0), 1, 64, 2, P(0), P(2), None) == INVALID     # perm aliases mask
+
+
+def mn(lib, **kw):
+    a = dict(A=P(0), lda=64, B=P(1), ldb=64, C=P(2), ldc=256, dt=0, M=32, N=256, K=64, G=128,
+             perm=P(3), counts=P(4), mask=None)
+    a.update(kw)
+    return lib.wide_gemm_mn(a["A"], a["lda"], a["B"], a["ldb"], a["C"], a["ldc"], a["dt"], a["M"],
+                            a["N"], a["K"], a["G"], a["perm"], a["counts"], a["mask"], None)
+
+
+def test_gemm_mn_validation(lib):
+    assert mn(lib, A=None) == INVALID
+    assert mn(lib, N=200) == INVALID                 # N % G
+    assert mn(lib, K=60, lda=64, ldb=64) == INVALID  # K % 8
+    assert mn(lib, lda=32) == INVALID                # lda < K
+    assert mn(lib, ldc=100) == INVALID               # ldc < N
+    assert mn(lib, dt=7) == INVALID
+    assert mn(lib, A=ctypes.c_void_p(FAKE + 2)) == INVALID        # misaligned
+    assert mn(lib, perm=None, mask=None) == INVALID
+    assert mn(lib, perm=None, mask=P(5), M=5) == INVALID          # mask path needs M <= 4
+    assert mn(lib, counts=None) == INVALID
+    assert mn(lib, C=P(0)) == INVALID                             # C aliases A
+    assert mn(lib, G=32, N=256) == UNSUPPORTED
+
+
+def test_gemm_mn_swiglu_validation(lib):
+    f = lib.wide_gemm_mn_swiglu
+    assert f(P(0), 64, P(1), None, 64, P(2), 256, 0, 32, 256, 64, 128, P(3), P(4), None, None) == INVALID
+    assert f(P(0), 64, P(1), P(2), 64, P(2), 256, 0, 32, 256, 64, 128, P(3), P(4), None, None) == INVALID
+
+
+def gk(lib, **kw):
+    a = dict(A=P(0), lda=256, B=P(1), ldb=256, C=P(2), ldc=128, beta=0, M=32, N=128, K=256,
+             G=128, mask=P(3))
+    a.update(kw)
+    return lib.wide_gemm_k(a["A"], a["lda"], a["B"], a["ldb"], a["C"], a["ldc"], a["beta"],
+                           a["M"], a["N"], a["K"], a["G"], a["mask"], None)
+
+
+def test_gemm_k_validation(lib):
+    assert gk(lib, mask=None) == INVALID
+    assert gk(lib, K=200, lda=256, ldb=256) == INVALID     # K % G
+    assert gk(lib, beta=2) == INVALID
+    assert gk(lib, ldc=130) == INVALID                      # ldc % 4
+    assert gk(lib, C=P(1)) == INVALID                       # C aliases B
+    assert gk(lib, G=32, K=256) == UNSUPPORTED
+    assert gk(lib, N=64, ldc=64) == UNSUPPORTED
+
+
+def at(lib, **kw):
+    a = dict(Q=P(0), K=P(1), V=P(2), O=P(3), dt=0, B=1, Tq=16, Tk=16, Hq=8, Hk=2, d=128, causal=1,
+             scale=0.0, leftpad=None, perm=P(4), counts=P(5), mask=None, ws=None, wsb=0)
+    a.update(kw)
+    return lib.wide_attn(a["Q"], a["K"], a["V"], a["O"], a["dt"], a["B"], a["Tq"], a["Tk"], a["Hq"],
+                         a["Hk"], a["d"], a["causal"], a["scale"], a["leftpad"], a["perm"],
+                         a["counts"], a["mask"], a["ws"], a["wsb"], None)
+
+
+def test_attn_validation(lib):
+    assert at(lib, Q=None) == INVALID
+    assert at(lib, Hq=6, Hk=4) == INVALID          # Hq % Hk
+    assert at(lib, Tk=8) == INVALID                 # Tk < Tq
+    assert at(lib, perm=None) == INVALID            # prefill needs the reorder
+    assert at(lib, scale=-1.0) == INVALID
+    assert at(lib, causal=3) == INVALID
+    assert at(lib, d=64) == UNSUPPORTED
+    # decode needs a workspace of the advertised size
+    need = lib.wide_attn_workspace_bytes(1, 1, 4096, 8, 2, 128)
+    assert need > 0 and lib.wide_attn_workspace_bytes(1, 16, 16, 8, 2, 128) == 0
+    assert at(lib, Tq=1, Tk=4096, perm=None, counts=None, mask=P(6)) == INVALID
+    assert at(lib, Tq=1, Tk=4096, perm=None, counts=None, mask=P(6), ws=P(7), wsb=need - 4) == INVALID
+
+
+def test_valid_call_without_device_reports_no_device(lib):
+    torch = pytest.importorskip("torch")
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present; this checks the host-only path")
+    assert mn(lib) == NO_DEVICE

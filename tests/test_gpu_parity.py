@@ -1,0 +1,340 @@
+"""GPU parity: every HIP entry point against the CPU oracle, through the C ABI.
+
+Bars: reorder perm/counts bit-exact; GEMM fp32 outputs max|err| <= 1e-2 x RMS
+of the oracle; attention fp32 outputs max|err| <= 2e-2; bf16-stored outputs
+within one bf16 step of the oracle's rounded value; entries the method does not
+compute are left bitwise untouched (the tests pre-zero them).
+"""
+import numpy as np
+import pytest
+
+from oracle import wide_ref as ref
+from masked_group_mask_amd import workloads as wl
+
+from helpers import (bits_of, check_attn, check_bf16_store, check_gemm, f32_of, say, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import masked_group_mask_amd as mg
+    mg.load()   # raises if libwide.so is missing: no fallback exists
+    return mg
+
+
+def W():
+    import masked_group_mask_amd as mg
+    return mg
+
+
+# ---------------------------------------------------------------------------
+# Reorder
+# ---------------------------------------------------------------------------
+
+REORDER_CASES = [
+    (1, 64, 8, 0.5), (1, 1, 3, 0.5), (1, 513, 112, 0.28), (2, 1031, 5, 0.7), (3, 700, 68, 0.5),
+    (1, 4096, 64, 0.5), (1, 2000, 136, 0.0), (1, 2000, 17, 1.0), (4, 257, 8, 0.34),
+]
+
+
+@pytest.mark.parametrize("B,T,NG,p", REORDER_CASES)
+def test_reorder_bit_exact(B, T, NG, p):
+    say("reorder", B, T, NG, p)
+    mask = wl.random_mask(100 + T + NG, (B, T, NG), p)
+    if p == 0.5:
+        mask[mask == 1] = 255       # any nonzero byte means active
+    perm, counts = W().reorder(to_dev(mask, torch))
+    torch.cuda.synchronize()
+    want_p, want_c = ref.reorder(mask)
+    assert np.array_equal(counts.cpu().numpy(), want_c)
+    assert np.array_equal(perm.cpu().numpy(), want_p)
+
+
+def test_reorder_full_size_llama8b_ffn_and_attention():
+    s = wl.shape("llama8b_prefill")
+    m = wl.draw_mask(np.random.default_rng(7), s.M, s.NG_ffn, s.p_ffn, "bern")[None]
+    a = wl.draw_mask(np.random.default_rng(8), s.M, s.Hk, s.p_attn, "bern")[None]
+    for mask in (m, a):
+        say("reorder full", mask.shape)
+        perm, counts = W().reorder(to_dev(mask, torch))
+        torch.cuda.synchronize()
+        want_c = mask.astype(bool).sum(axis=1).astype(np.int32)
+        assert np.array_equal(counts.cpu().numpy(), want_c)
+        # stable partition, checked per column with the library routine
+        want_p = np.argsort(mask[0].T == 0, axis=1, kind="stable")
+        assert np.array_equal(perm.cpu().numpy()[0], want_p)
+
+
+def test_reorder_deterministic():
+    mask = wl.random_mask(9, (1, 3000, 40), 0.5)
+    d = to_dev(mask, torch)
+    p1, c1 = W().reorder(d)
+    p2, c2 = W().reorder(d)
+    assert torch.equal(p1, p2) and torch.equal(c1, c2)
+
+
+# ---------------------------------------------------------------------------
+# GEMM-MN
+# ---------------------------------------------------------------------------
+
+def run_mn(A, B, mask2d, G, out_dtype, swiglu_up=None):
+    say("gemm_mn", A.shape, B.shape, G, out_dtype, "swiglu" if swiglu_up is not None else "")
+    md = to_dev(mask2d[None], torch)
+    perm, counts = W().reorder(md)
+    Ad, Bd = to_dev(A, torch), to_dev(B, torch)
+    if swiglu_up is None:
+        out = W().gemm_mn(Ad, Bd, G, perm=perm[0], counts=counts[0], out_dtype=out_dtype)
+    else:
+        out = W().gemm_mn_swiglu(Ad, Bd, to_dev(swiglu_up, torch), G, perm=perm[0],
+                                 counts=counts[0], out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return out
+
+
+MN_CASES = [  # M, N, K, G
+    (64, 1024, 256, 128), (300, 512, 320, 128), (300, 512, 200, 64), (1000, 1280, 640, 640),
+    (129, 256, 72, 256), (5, 128, 64, 128),
+]
+
+
+@pytest.mark.parametrize("M,N,K,G", MN_CASES)
+def test_gemm_mn_fp32(M, N, K, G):
+    A = wl.random_bf16(M + 1, (M, K))
+    B = wl.random_bf16(N + 2, (N, K), 0.05)
+    mask = wl.random_mask(M + N, (M, N // G), 0.5)
+    out = run_mn(A, B, mask, G, torch.float32)
+    got = f32_of(out)
+    want = ref.gemm_mn(A, B, mask, G)
+    check_gemm(got, want, f"gemm_mn {M}x{N}x{K} G{G}")
+    off = ~ref.expand(mask, G)
+    assert (out.cpu().numpy().view(np.uint32)[off] == 0).all(), "inactive entries were written"
+
+
+@pytest.mark.parametrize("p", [0.0, 1.0])
+def test_gemm_mn_all_or_nothing(p):
+    M, N, K, G = 200, 256, 128, 128
+    A = wl.random_bf16(1, (M, K))
+    B = wl.random_bf16(2, (N, K), 0.05)
+    mask = np.full((M, N // G), int(p), np.uint8)
+    got = f32_of(run_mn(A, B, mask, G, torch.float32))
+    if p == 0:
+        assert (got == 0).all()
+    else:
+        dense = ref.from_bf16(A) @ ref.from_bf16(B).T
+        check_gemm(got, dense, "all-ones = dense")
+
+
+def test_gemm_mn_bf16_store():
+    M, N, K, G = 257, 384, 256, 128
+    A = wl.random_bf16(3, (M, K))
+    B = wl.random_bf16(4, (N, K), 0.05)
+    mask = wl.random_mask(5, (M, N // G), 0.5)
+    out = run_mn(A, B, mask, G, torch.bfloat16)
+    want = ref.gemm_mn(A, B, mask, G)
+    keep = ref.expand(mask, G)
+    flips = check_bf16_store(bits_of(out)[keep], want[keep], "gemm_mn bf16")
+    assert flips < 0.02
+    assert (bits_of(out)[~keep] == 0).all()
+
+
+@pytest.mark.parametrize("M,N,K,G", [(64, 1024, 256, 128), (300, 512, 192, 64), (77, 640, 512, 128)])
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_gemm_mn_swiglu(M, N, K, G, dt):
+    A = wl.random_bf16(6, (M, K))
+    Wg = wl.random_bf16(7, (N, K), 0.05)
+    Wu = wl.random_bf16(8, (N, K), 0.05)
+    mask = wl.random_mask(9, (M, N // G), 0.5)
+    out = run_mn(A, Wg, mask, G, torch.float32 if dt == "f32" else torch.bfloat16, swiglu_up=Wu)
+    want = ref.swiglu(ref.gemm_mn(A, Wg, mask, G), ref.gemm_mn(A, Wu, mask, G))
+    keep = ref.expand(mask, G)
+    if dt == "f32":
+        check_gemm(f32_of(out), want, "swiglu f32")
+        assert (out.cpu().numpy().view(np.uint32)[~keep] == 0).all()
+    else:
+        check_bf16_store(bits_of(out)[keep], want[keep], "swiglu bf16")
+        assert (bits_of(out)[~keep] == 0).all()
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 4])
+@pytest.mark.parametrize("swiglu", [False, True])
+def test_gemv_mn_mask_direct(M, swiglu):
+    N, K, G = 1024, 512, 128
+    A = wl.random_bf16(10 + M, (M, K))
+    B = wl.random_bf16(11, (N, K), 0.05)
+    U = wl.random_bf16(12, (N, K), 0.05)
+    mask = wl.random_mask(13 + M, (M, N // G), 0.5)
+    say("gemv_mn", M, swiglu)
+    Ad, Bd, md = to_dev(A, torch), to_dev(B, torch), to_dev(mask, torch)
+    if swiglu:
+        out = W().gemm_mn_swiglu(Ad, Bd, to_dev(U, torch), G, mask=md, out_dtype=torch.float32)
+        want = ref.swiglu(ref.gemm_mn(A, B, mask, G), ref.gemm_mn(A, U, mask, G))
+    else:
+        out = W().gemm_mn(Ad, Bd, G, mask=md, out_dtype=torch.float32)
+        want = ref.gemm_mn(A, B, mask, G)
+    torch.cuda.synchronize()
+    check_gemm(f32_of(out), want, "gemv_mn")
+    assert (out.cpu().numpy().view(np.uint32)[~ref.expand(mask, G)] == 0).all()
+
+
+# ---------------------------------------------------------------------------
+# GEMM-K
+# ---------------------------------------------------------------------------
+
+K_CASES = [  # M, N, K, G
+    (64, 256, 1024, 128), (300, 256, 512, 128), (300, 384, 640, 64), (1000, 128, 2560, 640),
+    (129, 128, 512, 256), (5, 256, 256, 128),
+]
+
+
+@pytest.mark.parametrize("M,N,K,G", K_CASES)
+def test_gemm_k(M, N, K, G):
+    A = wl.random_bf16(M + 3, (M, K))
+    B = wl.random_bf16(N + 4, (N, K), 0.05)
+    mask = wl.random_mask(M + K, (M, K // G), 0.5)
+    say("gemm_k", M, N, K, G)
+    out = W().gemm_k(to_dev(A, torch), to_dev(B, torch), G, to_dev(mask, torch))
+    torch.cuda.synchronize()
+    want = ref.gemm_k(A, B, mask, G)
+    check_gemm(f32_of(out), want, f"gemm_k {M}x{N}x{K} G{G}")
+    none = ~mask.any(axis=1)
+    assert (out.cpu().numpy()[none] == 0).all()
+
+
+def test_gemm_k_beta_and_determinism():
+    M, N, K, G = 333, 256, 1024, 128
+    A = wl.random_bf16(20, (M, K))
+    B = wl.random_bf16(21, (N, K), 0.05)
+    mask = wl.random_mask(22, (M, K // G), 0.4)
+    C0 = wl.random_bf16(23, (M, N)).view(np.uint16)
+    C0 = ref.from_bf16(C0).astype(np.float32)
+    say("gemm_k beta")
+    Ad, Bd, md = to_dev(A, torch), to_dev(B, torch), to_dev(mask, torch)
+    out = to_dev(C0, torch)
+    W().gemm_k(Ad, Bd, G, md, out=out, beta=1)
+    r1 = W().gemm_k(Ad, Bd, G, md)
+    r2 = W().gemm_k(Ad, Bd, G, md)
+    torch.cuda.synchronize()
+    want = ref.gemm_k(A, B, mask, G)
+    check_gemm(f32_of(out), want + C0, "gemm_k beta=1")
+    assert torch.equal(r1, r2), "GEMM-K is not bitwise reproducible"
+
+
+@pytest.mark.parametrize("p", [0.0, 1.0])
+def test_gemm_k_all_or_nothing(p):
+    M, N, K, G = 150, 128, 512, 128
+    A = wl.random_bf16(24, (M, K))
+    B = wl.random_bf16(25, (N, K), 0.05)
+    mask = np.full((M, K // G), int(p), np.uint8)
+    out = W().gemm_k(to_dev(A, torch), to_dev(B, torch), G, to_dev(mask, torch))
+    torch.cuda.synchronize()
+    got = f32_of(out)
+    if p == 0:
+        assert (got == 0).all()
+    else:
+        check_gemm(got, ref.from_bf16(A) @ ref.from_bf16(B).T, "all-ones = dense")
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 4])
+def test_gemv_k(M):
+    N, K, G = 512, 2048, 128
+    A = wl.random_bf16(30 + M, (M, K))
+    B = wl.random_bf16(31, (N, K), 0.05)
+    mask = wl.random_mask(32 + M, (M, K // G), 0.5)
+    say("gemv_k", M)
+    out = W().gemm_k(to_dev(A, torch), to_dev(B, torch), G, to_dev(mask, torch))
+    torch.cuda.synchronize()
+    check_gemm(f32_of(out), ref.gemm_k(A, B, mask, G), "gemv_k")
+
+
+# ---------------------------------------------------------------------------
+# Attention
+# ---------------------------------------------------------------------------
+
+def run_attn(Q, K, V, mask, causal=True, leftpad=None, out_dtype=torch.float32):
+    B, Tq, Hq, d = Q.shape
+    say("attn", Q.shape, K.shape, causal, leftpad, out_dtype)
+    perm, counts = W().reorder(to_dev(mask, torch))
+    lp = None if leftpad is None else to_dev(np.array(leftpad, np.int32), torch)
+    out = W().attn(to_dev(Q, torch), to_dev(K, torch), to_dev(V, torch), perm=perm, counts=counts,
+                   causal=causal, leftpad=lp, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return out
+
+
+ATTN_CASES = [  # B, Tq, Tk, Hq, Hk
+    (1, 64, 64, 4, 1), (2, 300, 300, 8, 2), (1, 200, 333, 8, 2), (1, 257, 257, 10, 2),
+    (1, 130, 130, 32, 8),
+]
+
+
+@pytest.mark.parametrize("B,Tq,Tk,Hq,Hk", ATTN_CASES)
+@pytest.mark.parametrize("causal", [True, False])
+def test_attention_prefill(B, Tq, Tk, Hq, Hk, causal):
+    d = 128
+    Q = wl.random_bf16(40 + Tq, (B, Tq, Hq, d), 1.0)
+    K = wl.random_bf16(41 + Tk, (B, Tk, Hk, d), 1.0)
+    V = wl.random_bf16(42 + Tk, (B, Tk, Hk, d), 1.0)
+    mask = wl.random_mask(43 + Hq, (B, Tq, Hk), 0.5)
+    out = run_attn(Q, K, V, mask, causal)
+    want = ref.attention(Q, K, V, mask, causal=causal)
+    check_attn(f32_of(out), want, "attn prefill")
+    keep = np.repeat(mask != 0, Hq // Hk, axis=2)
+    assert (out.cpu().numpy().view(np.uint32)[~keep] == 0).all()
+
+
+def test_attention_leftpad_and_bf16():
+    B, T, Hq, Hk, d = 2, 200, 8, 2, 128
+    Q = wl.random_bf16(50, (B, T, Hq, d), 1.0)
+    K = wl.random_bf16(51, (B, T, Hk, d), 1.0)
+    V = wl.random_bf16(52, (B, T, Hk, d), 1.0)
+    mask = wl.random_mask(53, (B, T, Hk), 0.6)
+    lp = [0, 77]
+    want = ref.attention(Q, K, V, mask, leftpad=lp)
+    check_attn(f32_of(run_attn(Q, K, V, mask, leftpad=lp)), want, "leftpad")
+    keep = np.repeat(mask != 0, Hq // Hk, axis=2)
+    out = run_attn(Q, K, V, mask, leftpad=lp, out_dtype=torch.bfloat16)
+    check_bf16_store(bits_of(out)[keep], want[keep], "attn bf16")
+
+
+@pytest.mark.parametrize("Hq,Hk,Tk", [(32, 8, 1000), (40, 8, 4097), (8, 8, 256)])
+@pytest.mark.parametrize("mode", ["mask", "counts"])
+def test_attention_decode(Hq, Hk, Tk, mode):
+    B, d = 2, 128
+    Q = wl.random_bf16(60, (B, 1, Hq, d), 1.0)
+    K = wl.random_bf16(61, (B, Tk, Hk, d), 1.0)
+    V = wl.random_bf16(62, (B, Tk, Hk, d), 1.0)
+    mask = wl.random_mask(63, (B, 1, Hk), 0.5)
+    mask[0, 0, 0] = 1
+    say("decode", Hq, Hk, Tk, mode)
+    md = to_dev(mask, torch)
+    if mode == "mask":
+        out = W().attn(to_dev(Q, torch), to_dev(K, torch), to_dev(V, torch), mask=md,
+                       out_dtype=torch.float32)
+    else:
+        perm, counts = W().reorder(md)
+        out = W().attn(to_dev(Q, torch), to_dev(K, torch), to_dev(V, torch), perm=perm,
+                       counts=counts, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    want = ref.attention(Q, K, V, mask)
+    check_attn(f32_of(out), want, "decode")
+    keep = np.repeat(mask != 0, Hq // Hk, axis=2)
+    assert (out.cpu().numpy().view(np.uint32)[~keep] == 0).all()
+
+
+def test_attention_decode_leftpad():
+    B, Tk, Hq, Hk, d = 2, 700, 16, 4, 128
+    Q = wl.random_bf16(70, (B, 1, Hq, d), 1.0)
+    K = wl.random_bf16(71, (B, Tk, Hk, d), 1.0)
+    V = wl.random_bf16(72, (B, Tk, Hk, d), 1.0)
+    mask = np.ones((B, 1, Hk), np.uint8)
+    lp = [300, 0]
+    say("decode leftpad")
+    out = W().attn(to_dev(Q, torch), to_dev(K, torch), to_dev(V, torch), mask=to_dev(mask, torch),
+                   leftpad=to_dev(np.array(lp, np.int32), torch), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    check_attn(f32_of(out), ref.attention(Q, K, V, mask, leftpad=lp), "decode leftpad")
