@@ -1,0 +1,300 @@
+#!/usr/bin/env python3
+"""Benchmark of the masked group-mask layer on one MI355X.
+
+One step = one pass of the whole routed path of a transformer layer over one
+batch of seeded synthetic input resident in HBM: reorder of the attention and
+FFN masks, q_proj (GEMM-MN), head-group-masked causal GQA attention, o_proj
+(GEMM-K), gate/up projections fused with SwiGLU (GEMM-MN) and down_proj
+(GEMM-K). Default workload: Qwen3-14B-shaped layer prefill, T=8192, 50% of
+the attention groups and 50% of the FFN groups inactive, FFN group size 128.
+
+Prints one JSON line: active-FLOP TFLOP/s of the masked layer, the speedup
+over the same kernels run with all-ones masks, the roofline of the dominant
+kernel (timed with HIP events on the launch stream), a one-token decode step
+of the Llama3.1-8B shape (HBM bytes/s), and the CPU oracle timed on a sample
+of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "active-FLOP TFLOP/s & speedup vs dense per masked layer at 50% sparsity"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def to_dev(x, torch):
+    x = np.ascontiguousarray(x)
+    if x.dtype == np.uint16:
+        return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(x).cuda()
+
+
+class PrefillLayer:
+    """Device buffers and the step of one masked prefill layer."""
+
+    def __init__(self, s, host, torch, mg):
+        self.s, self.torch, self.mg = s, torch, mg
+        d = lambda k: to_dev(host[k], torch)  # noqa: E731
+        self.x, self.wq, self.wo = d("x"), d("w_q"), d("w_o")
+        self.wg, self.wu, self.wd = d("w_gate"), d("w_up"), d("w_down")
+        self.k, self.v = d("k"), d("v")
+        self.masks = {"masked": (d("mask_attn"), d("mask_ffn")),
+                      "dense": (torch.ones_like(d("mask_attn")), torch.ones_like(d("mask_ffn")))}
+        dev = self.x.device
+        M, B, T = s.M, s.B, s.T
+        i32 = torch.int32
+        self.perm_a = torch.empty((B, s.Hk, T), dtype=i32, device=dev)
+        self.cnt_a = torch.empty((B, s.Hk), dtype=i32, device=dev)
+        self.perm_f = torch.empty((1, s.NG_ffn, M), dtype=i32, device=dev)
+        self.cnt_f = torch.empty((1, s.NG_ffn), dtype=i32, device=dev)
+        # Consumers read only active entries, so the outputs need no clearing.
+        self.q = torch.empty((M, s.Hq * s.d), dtype=torch.bfloat16, device=dev)
+        self.o = torch.empty((B, T, s.Hq, s.d), dtype=torch.bfloat16, device=dev)
+        self.h = torch.empty((M, s.Dff), dtype=torch.bfloat16, device=dev)
+        self.y_attn = torch.empty((M, s.D), dtype=torch.float32, device=dev)
+        self.y_ffn = torch.empty((M, s.D), dtype=torch.float32, device=dev)
+        self.ops = ["reorder", "q_proj", "attention", "o_proj", "gate_up_swiglu", "down_proj"]
+
+    def step(self, which, events=None):
+        s, mg = self.s, self.mg
+        ma, mf = self.masks[which]
+        rec = (lambda i: events[i].record()) if events is not None else (lambda i: None)
+        rec(0)
+        mg.reorder(ma, self.perm_a, self.cnt_a)
+        mg.reorder(mf.view(1, s.M, s.NG_ffn), self.perm_f, self.cnt_f)
+        rec(1)
+        # B = 1: the attention reorder is also the flattened reorder of the GEMMs.
+        mg.gemm_mn(self.x, self.wq, s.G_attn, perm=self.perm_a[0], counts=self.cnt_a[0], out=self.q)
+        rec(2)
+        mg.attn(self.q.view(s.B, s.T, s.Hq, s.d), self.k, self.v, perm=self.perm_a,
+                counts=self.cnt_a, out=self.o)
+        rec(3)
+        mg.gemm_k(self.o.view(s.M, s.Hq * s.d), self.wo, s.G_attn, ma.view(s.M, s.Hk),
+                  out=self.y_attn)
+        rec(4)
+        mg.gemm_mn_swiglu(self.x, self.wg, self.wu, s.G_ffn, perm=self.perm_f[0],
+                          counts=self.cnt_f[0], out=self.h)
+        rec(5)
+        mg.gemm_k(self.h, self.wd, s.G_ffn, mf.view(s.M, s.NG_ffn), out=self.y_ffn)
+        rec(6)
+
+
+def time_steps(layer, which, steps, warmup, torch):
+    for _ in range(warmup):
+        layer.step(which)
+    torch.cuda.synchronize()
+    n_ev = len(layer.ops) + 1
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        layer.step(which, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_op = {op: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(steps)]))
+              for j, op in enumerate(layer.ops)}
+    return wall / steps * 1e3, per_op
+
+
+def bench_decode(torch, mg, wl, metrics, steps=50, sets=3):
+    """One-token decode step of the Llama3.1-8B shape, KV cache of 16384, half
+    of the attention and FFN groups off. Weight/KV sets rotate so the 256 MB
+    Infinity Cache cannot hold the active set across steps."""
+    s = wl.shape("llama8b_decode")
+    host = wl.make_layer(s, seed=1)
+    ma = host["mask_attn"]
+    mf = host["mask_ffn"]
+    nbytes = metrics.decode_bytes(s, ma, mf)
+    dev = lambda k: to_dev(host[k], torch)  # noqa: E731
+    base = {k: dev(k) for k in ("w_q", "w_o", "w_gate", "w_up", "w_down", "k", "v")}
+    wsets = [base] + [{k: t.clone() for k, t in base.items()} for _ in range(sets - 1)]
+    x = dev("x")
+    mad = to_dev(ma, torch)
+    mfd = to_dev(mf.reshape(1, s.NG_ffn), torch)
+    q = torch.empty((1, s.Hq * s.d), dtype=torch.bfloat16, device=x.device)
+    o = torch.empty((1, 1, s.Hq, s.d), dtype=torch.bfloat16, device=x.device)
+    h = torch.empty((1, s.Dff), dtype=torch.bfloat16, device=x.device)
+    y1 = torch.empty((1, s.D), dtype=torch.float32, device=x.device)
+    y2 = torch.empty((1, s.D), dtype=torch.float32, device=x.device)
+    ws = torch.empty(mg.attn_workspace_bytes(1, 1, s.Tk, s.Hq, s.Hk, s.d), dtype=torch.uint8,
+                     device=x.device)
+    ops = ["q_proj", "attention", "o_proj", "gate_up_swiglu", "down_proj"]
+
+    def step(w, ev=None):
+        rec = (lambda i: ev[i].record()) if ev is not None else (lambda i: None)
+        rec(0)
+        mg.gemm_mn(x, w["w_q"], s.G_attn, mask=mad.view(1, s.Hk), out=q)
+        rec(1)
+        mg.attn(q.view(1, 1, s.Hq, s.d), w["k"], w["v"], mask=mad, out=o, workspace=ws)
+        rec(2)
+        mg.gemm_k(o.view(1, s.Hq * s.d), w["w_o"], s.G_attn, mad.view(1, s.Hk), out=y1)
+        rec(3)
+        mg.gemm_mn_swiglu(x, w["w_gate"], w["w_up"], s.G_ffn, mask=mfd, out=h)
+        rec(4)
+        mg.gemm_k(h, w["w_down"], s.G_ffn, mfd, out=y2)
+        rec(5)
+
+    for i in range(5):
+        step(wsets[i % sets])
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(ops) + 1)] for _ in range(steps)]
+    for i in range(steps):
+        step(wsets[i % sets], evs[i])
+    torch.cuda.synchronize()
+    per_op = {op: float(np.median([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(steps)]))
+              for j, op in enumerate(ops)}
+    gpu_ms = sum(per_op.values())
+    total = sum(nbytes.values())
+    return {
+        "workload": "llama8b_decode (B=1, KV 16384, 4/8 attention and 56/112 FFN groups on)",
+        "active_bytes": total,
+        "kernel_ms_per_step": gpu_ms,
+        "GB_per_s": total / (gpu_ms * 1e-3) / 1e9,
+        "frac_of_hbm_peak": total / (gpu_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "per_op_ms": per_op,
+        "per_op_GB_per_s": {op: nbytes[op] / (per_op[op] * 1e-3) / 1e9 for op in ops},
+        "timing": "median over %d steps of HIP events around each op, %d rotated weight/KV sets" % (steps, sets),
+    }
+
+
+def cpu_baseline(s, host, rows: int):
+    """The CPU oracle on `rows` token rows of the same layer (all routed ops)."""
+    from oracle import wide_ref as ref
+    from masked_group_mask_amd import metrics
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                       if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover - threadpoolctl missing
+        threads = os.cpu_count() or 1
+    rng = np.random.default_rng(123)
+    sel = np.sort(rng.choice(s.M, size=min(rows, s.M), replace=False))
+    ma = host["mask_attn"].reshape(s.M, s.Hk)[sel]
+    mf = host["mask_ffn"].reshape(s.M, s.NG_ffn)[sel]
+    X = host["x"][sel]
+    t0 = time.perf_counter()
+    q = ref.round_bf16(ref.gemm_mn(X, host["w_q"], ma, s.G_attn))
+    full_mask = host["mask_attn"]
+    # attention needs Q only at the sampled positions; other rows are unused
+    Qs = np.zeros((s.B, s.T, s.Hq, s.d), np.uint16)
+    Qs[0, sel] = ref.to_bf16_bits(q).reshape(len(sel), s.Hq, s.d)
+    o = ref.attention(Qs, host["k"], host["v"], full_mask, queries=[(0, int(t)) for t in sel])
+    ref.gemm_k(ref.to_bf16_bits(ref.round_bf16(o)).reshape(len(sel), -1), host["w_o"], ma, s.G_attn)
+    hh = ref.round_bf16(ref.swiglu(ref.gemm_mn(X, host["w_gate"], mf, s.G_ffn),
+                                   ref.gemm_mn(X, host["w_up"], mf, s.G_ffn)))
+    ref.gemm_k(ref.to_bf16_bits(hh), host["w_down"], mf, s.G_ffn)
+    dt = time.perf_counter() - t0
+    # active FLOPs of exactly the sampled rows
+    fl = (metrics.gemm_mn_flops(ma, s.D, s.G_attn) + metrics.gemm_k_flops(ma, s.D, s.G_attn)
+          + 2 * metrics.gemm_mn_flops(mf, s.D, s.G_ffn) + metrics.gemm_k_flops(mf, s.D, s.G_ffn))
+    rep = s.Hq // s.Hk
+    fl += int(sum(4 * s.d * rep * int(ma[i].sum()) * (int(t) + 1) for i, t in enumerate(sel)))
+    return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{len(sel)} of {s.M} token rows of the same layer (all routed ops, float64), {dt:.1f} s",
+            "seconds": dt}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="qwen14b_prefill")
+    ap.add_argument("--sparsity", type=float, default=0.5)
+    ap.add_argument("--g-ffn", type=int, default=128)
+    ap.add_argument("--cpu-rows", type=int, default=4096)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the masked layer runs on a single MI355X and "
+              "this build has no multi-GPU path (--gpus must be 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import masked_group_mask_amd as mg
+    from masked_group_mask_amd import metrics, workloads as wl
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    mg.load()
+    torch.cuda.set_device(0)
+
+    p = 1.0 - args.sparsity
+    s = wl.shape(args.workload, p_attn=p, p_ffn=p, G_ffn=args.g_ffn)
+    log(f"generating {s.name}: T={s.T} D={s.D} D'={s.Dff} Hq={s.Hq} Hk={s.Hk} G_ffn={s.G_ffn} p={p}")
+    t0 = time.perf_counter()
+    host = wl.make_layer(s, seed=0)
+    log(f"inputs ready in {time.perf_counter() - t0:.1f} s")
+    layer = PrefillLayer(s, host, torch, mg)
+    flops = metrics.layer_flops(s, host["mask_attn"], host["mask_ffn"])
+    ones_a = np.ones_like(host["mask_attn"])
+    ones_f = np.ones_like(host["mask_ffn"])
+    dense_flops = metrics.layer_flops(s, ones_a, ones_f)
+    total_flops = sum(flops.values())
+
+    log("timing masked layer")
+    ms, per_op = time_steps(layer, "masked", args.steps, args.warmup, torch)
+    log(f"masked: {ms:.3f} ms/step  " + " ".join(f"{k}={v:.3f}" for k, v in per_op.items()))
+    dense_ms, dense_per_op = (None, None)
+    if not args.no_dense:
+        dense_ms, dense_per_op = time_steps(layer, "dense", args.steps, args.warmup, torch)
+        log(f"dense:  {dense_ms:.3f} ms/step  " + " ".join(f"{k}={v:.3f}" for k, v in dense_per_op.items()))
+
+    value = total_flops / (ms * 1e-3) / 1e12
+    # Dominant kernel: the routed op with the largest share of the masked step.
+    dom = max((op for op in per_op if op != "reorder"), key=lambda k: per_op[k])
+    achieved = flops[dom] / (per_op[dom] * 1e-3) / 1e12
+    roof = {"kernel": dom, "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+            "flops_per_launch": flops[dom], "avg_launch_ms": per_op[dom]}
+
+    out = {
+        "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": s.name, "B": s.B, "T": s.T, "hidden": s.D, "ffn": s.Dff,
+                   "q_heads": s.Hq, "kv_heads": s.Hk, "head_dim": s.d, "G_attn": s.G_attn,
+                   "G_ffn": s.G_ffn, "sparsity_attn": args.sparsity, "sparsity_ffn": args.sparsity,
+                   "seed": 0},
+        "speedup_vs_dense": (dense_ms / ms) if dense_ms else None,
+        "ideal_speedup": sum(dense_flops.values()) / total_flops,
+        "dense_ms_per_step": dense_ms,
+        "active_gflop_per_step": total_flops / 1e9,
+        "per_op_ms": per_op,
+        "per_op_tflops": {k: flops[k] / (per_op[k] * 1e-3) / 1e12 for k in flops},
+        "dense_per_op_ms": dense_per_op,
+        "roofline": roof,
+    }
+    if not args.no_decode:
+        log("timing decode step")
+        out["decode"] = bench_decode(torch, mg, wl, metrics)
+        log(f"decode: {out['decode']['kernel_ms_per_step'] * 1e3:.1f} us, "
+            f"{out['decode']['GB_per_s']:.0f} GB/s")
+    if not args.no_cpu_baseline:
+        log(f"timing CPU oracle on {args.cpu_rows} rows")
+        out["cpu_baseline"] = cpu_baseline(s, host, args.cpu_rows)
+        log(f"cpu: {out['cpu_baseline']['value'] * 1e3:.2f} GFLOP/s in {out['cpu_baseline']['seconds']:.1f} s")
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

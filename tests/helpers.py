@@ -48,13 +48,33 @@ def check_attn(got, want, what=""):
     return err
 
 
+def check_attn_bf16(got_bits, want64, what=""):
+    """bf16-stored attention output: the fp32 bar plus one bf16 rounding."""
+    err = np.abs(ref.from_bf16(got_bits) - want64)
+    bound = ATTN_ATOL + 2.0 ** -8 * np.abs(want64)
+    bad = np.count_nonzero(err > bound)
+    assert bad == 0, f"{what}: {bad} outputs beyond 2e-2 + one bf16 step (max err {err.max():.3e})"
+    return float(err.max()) if err.size else 0.0
+
+
 def check_bf16_store(got_bits, want64, what=""):
-    """A bf16-stored result is within one bf16 step of the oracle's rounded value."""
+    """A bf16-stored result is within one bf16 step of the oracle's rounded value.
+
+    Where the exact result is small against the output's RMS (cancellation in
+    the fp32 sum), the fp32 accumulation error, not the rounding, dominates;
+    there an absolute error of 1e-3 x RMS is accepted as well.
+    """
     want_bits = ref.to_bf16_bits(want64).astype(np.int32)
     g = got_bits.astype(np.int32)
     same_sign = (g >> 15) == (want_bits >> 15)
     step = np.abs(g - want_bits)
-    ok = (same_sign & (step <= 1)) | (np.abs(ref.from_bf16(got_bits) - want64) <= 2.0 ** -8 * np.abs(want64) + 1e-30)
+    rms = float(np.sqrt(np.mean(want64 ** 2))) if want64.size else 0.0
+    err = np.abs(ref.from_bf16(got_bits) - want64)
+    ok = (same_sign & (step <= 1)) | (err <= 2.0 ** -8 * np.abs(want64) + 1e-3 * rms)
     bad = np.count_nonzero(~ok)
-    assert bad == 0, f"{what}: {bad} bf16 outputs more than one step from the oracle"
+    if bad:
+        i = np.flatnonzero(~ok)[:5]
+        detail = ", ".join(f"got {float(ref.from_bf16(got_bits[j])):.6g} want {float(want64[j]):.6g}" for j in i)
+        raise AssertionError(f"{what}: {bad} bf16 outputs more than one step from the oracle "
+                             f"(RMS {rms:.3g}): {detail}")
     return float(np.mean(g != want_bits))

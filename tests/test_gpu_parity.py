@@ -11,7 +11,8 @@ import pytest
 from oracle import wide_ref as ref
 from masked_group_mask_amd import workloads as wl
 
-from helpers import (bits_of, check_attn, check_bf16_store, check_gemm, f32_of, say, to_dev)
+from helpers import (bits_of, check_attn, check_attn_bf16, check_bf16_store, check_gemm, f32_of,
+                     say, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -298,7 +299,8 @@ def test_attention_leftpad_and_bf16():
     check_attn(f32_of(run_attn(Q, K, V, mask, leftpad=lp)), want, "leftpad")
     keep = np.repeat(mask != 0, Hq // Hk, axis=2)
     out = run_attn(Q, K, V, mask, leftpad=lp, out_dtype=torch.bfloat16)
-    check_bf16_store(bits_of(out)[keep], want[keep], "attn bf16")
+    check_attn_bf16(bits_of(out)[keep], want[keep], "attn bf16")
+    assert (bits_of(out)[~keep] == 0).all()
 
 
 @pytest.mark.parametrize("Hq,Hk,Tk", [(32, 8, 1000), (40, 8, 4097), (8, 8, 256)])
