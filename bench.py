@@ -37,68 +37,12 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
-def to_dev(x, torch):
-    x = np.ascontiguousarray(x)
-    if x.dtype == np.uint16:
-        return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
-    return torch.from_numpy(x).cuda()
-
-
-class PrefillLayer:
-    """Device buffers and the step of one masked prefill layer."""
-
-    def __init__(self, s, host, torch, mg):
-        self.s, self.torch, self.mg = s, torch, mg
-        d = lambda k: to_dev(host[k], torch)  # noqa: E731
-        self.x, self.wq, self.wo = d("x"), d("w_q"), d("w_o")
-        self.wg, self.wu, self.wd = d("w_gate"), d("w_up"), d("w_down")
-        self.k, self.v = d("k"), d("v")
-        self.masks = {"masked": (d("mask_attn"), d("mask_ffn")),
-                      "dense": (torch.ones_like(d("mask_attn")), torch.ones_like(d("mask_ffn")))}
-        dev = self.x.device
-        M, B, T = s.M, s.B, s.T
-        i32 = torch.int32
-        self.perm_a = torch.empty((B, s.Hk, T), dtype=i32, device=dev)
-        self.cnt_a = torch.empty((B, s.Hk), dtype=i32, device=dev)
-        self.perm_f = torch.empty((1, s.NG_ffn, M), dtype=i32, device=dev)
-        self.cnt_f = torch.empty((1, s.NG_ffn), dtype=i32, device=dev)
-        # Consumers read only active entries, so the outputs need no clearing.
-        self.q = torch.empty((M, s.Hq * s.d), dtype=torch.bfloat16, device=dev)
-        self.o = torch.empty((B, T, s.Hq, s.d), dtype=torch.bfloat16, device=dev)
-        self.h = torch.empty((M, s.Dff), dtype=torch.bfloat16, device=dev)
-        self.y_attn = torch.empty((M, s.D), dtype=torch.float32, device=dev)
-        self.y_ffn = torch.empty((M, s.D), dtype=torch.float32, device=dev)
-        self.ops = ["reorder", "q_proj", "attention", "o_proj", "gate_up_swiglu", "down_proj"]
-
-    def step(self, which, events=None):
-        s, mg = self.s, self.mg
-        ma, mf = self.masks[which]
-        rec = (lambda i: events[i].record()) if events is not None else (lambda i: None)
-        rec(0)
-        mg.reorder(ma, self.perm_a, self.cnt_a)
-        mg.reorder(mf.view(1, s.M, s.NG_ffn), self.perm_f, self.cnt_f)
-        rec(1)
-        # B = 1: the attention reorder is also the flattened reorder of the GEMMs.
-        mg.gemm_mn(self.x, self.wq, s.G_attn, perm=self.perm_a[0], counts=self.cnt_a[0], out=self.q)
-        rec(2)
-        mg.attn(self.q.view(s.B, s.T, s.Hq, s.d), self.k, self.v, perm=self.perm_a,
-                counts=self.cnt_a, out=self.o)
-        rec(3)
-        mg.gemm_k(self.o.view(s.M, s.Hq * s.d), self.wo, s.G_attn, ma.view(s.M, s.Hk),
-                  out=self.y_attn)
-        rec(4)
-        mg.gemm_mn_swiglu(self.x, self.wg, self.wu, s.G_ffn, perm=self.perm_f[0],
-                          counts=self.cnt_f[0], out=self.h)
-        rec(5)
-        mg.gemm_k(self.h, self.wd, s.G_ffn, mf.view(s.M, s.NG_ffn), out=self.y_ffn)
-        rec(6)
-
-
 def time_steps(layer, which, steps, warmup, torch):
+    from masked_group_mask_amd.layer import PREFILL_OPS
     for _ in range(warmup):
         layer.step(which)
     torch.cuda.synchronize()
-    n_ev = len(layer.ops) + 1
+    n_ev = len(PREFILL_OPS) + 1
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -107,57 +51,28 @@ def time_steps(layer, which, steps, warmup, torch):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     per_op = {op: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(steps)]))
-              for j, op in enumerate(layer.ops)}
+              for j, op in enumerate(PREFILL_OPS)}
     return wall / steps * 1e3, per_op
 
 
-def bench_decode(torch, mg, wl, metrics, steps=50, sets=3):
+def bench_decode(torch, wl, metrics, steps=50, sets=3):
     """One-token decode step of the Llama3.1-8B shape, KV cache of 16384, half
     of the attention and FFN groups off. Weight/KV sets rotate so the 256 MB
     Infinity Cache cannot hold the active set across steps."""
+    from masked_group_mask_amd.layer import DECODE_OPS, DecodeLayer
     s = wl.shape("llama8b_decode")
     host = wl.make_layer(s, seed=1)
-    ma = host["mask_attn"]
-    mf = host["mask_ffn"]
-    nbytes = metrics.decode_bytes(s, ma, mf)
-    dev = lambda k: to_dev(host[k], torch)  # noqa: E731
-    base = {k: dev(k) for k in ("w_q", "w_o", "w_gate", "w_up", "w_down", "k", "v")}
-    wsets = [base] + [{k: t.clone() for k, t in base.items()} for _ in range(sets - 1)]
-    x = dev("x")
-    mad = to_dev(ma, torch)
-    mfd = to_dev(mf.reshape(1, s.NG_ffn), torch)
-    q = torch.empty((1, s.Hq * s.d), dtype=torch.bfloat16, device=x.device)
-    o = torch.empty((1, 1, s.Hq, s.d), dtype=torch.bfloat16, device=x.device)
-    h = torch.empty((1, s.Dff), dtype=torch.bfloat16, device=x.device)
-    y1 = torch.empty((1, s.D), dtype=torch.float32, device=x.device)
-    y2 = torch.empty((1, s.D), dtype=torch.float32, device=x.device)
-    ws = torch.empty(mg.attn_workspace_bytes(1, 1, s.Tk, s.Hq, s.Hk, s.d), dtype=torch.uint8,
-                     device=x.device)
-    ops = ["q_proj", "attention", "o_proj", "gate_up_swiglu", "down_proj"]
-
-    def step(w, ev=None):
-        rec = (lambda i: ev[i].record()) if ev is not None else (lambda i: None)
-        rec(0)
-        mg.gemm_mn(x, w["w_q"], s.G_attn, mask=mad.view(1, s.Hk), out=q)
-        rec(1)
-        mg.attn(q.view(1, 1, s.Hq, s.d), w["k"], w["v"], mask=mad, out=o, workspace=ws)
-        rec(2)
-        mg.gemm_k(o.view(1, s.Hq * s.d), w["w_o"], s.G_attn, mad.view(1, s.Hk), out=y1)
-        rec(3)
-        mg.gemm_mn_swiglu(x, w["w_gate"], w["w_up"], s.G_ffn, mask=mfd, out=h)
-        rec(4)
-        mg.gemm_k(h, w["w_down"], s.G_ffn, mfd, out=y2)
-        rec(5)
-
+    nbytes = metrics.decode_bytes(s, host["mask_attn"], host["mask_ffn"])
+    layer = DecodeLayer(s, host, sets=sets)
     for i in range(5):
-        step(wsets[i % sets])
+        layer.step(i)
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(ops) + 1)] for _ in range(steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(DECODE_OPS) + 1)] for _ in range(steps)]
     for i in range(steps):
-        step(wsets[i % sets], evs[i])
+        layer.step(i, evs[i])
     torch.cuda.synchronize()
     per_op = {op: float(np.median([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(steps)]))
-              for j, op in enumerate(ops)}
+              for j, op in enumerate(DECODE_OPS)}
     gpu_ms = sum(per_op.values())
     total = sum(nbytes.values())
     return {
@@ -167,7 +82,7 @@ def bench_decode(torch, mg, wl, metrics, steps=50, sets=3):
         "GB_per_s": total / (gpu_ms * 1e-3) / 1e9,
         "frac_of_hbm_peak": total / (gpu_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
         "per_op_ms": per_op,
-        "per_op_GB_per_s": {op: nbytes[op] / (per_op[op] * 1e-3) / 1e9 for op in ops},
+        "per_op_GB_per_s": {op: nbytes[op] / (per_op[op] * 1e-3) / 1e9 for op in DECODE_OPS},
         "timing": "median over %d steps of HIP events around each op, %d rotated weight/KV sets" % (steps, sets),
     }
 
@@ -244,7 +159,8 @@ def main():
     t0 = time.perf_counter()
     host = wl.make_layer(s, seed=0)
     log(f"inputs ready in {time.perf_counter() - t0:.1f} s")
-    layer = PrefillLayer(s, host, torch, mg)
+    from masked_group_mask_amd.layer import PrefillLayer
+    layer = PrefillLayer(s, host, with_dense=not args.no_dense)
     flops = metrics.layer_flops(s, host["mask_attn"], host["mask_ffn"])
     ones_a = np.ones_like(host["mask_attn"])
     ones_f = np.ones_like(host["mask_ffn"])
@@ -286,7 +202,7 @@ def main():
     }
     if not args.no_decode:
         log("timing decode step")
-        out["decode"] = bench_decode(torch, mg, wl, metrics)
+        out["decode"] = bench_decode(torch, wl, metrics)
         log(f"decode: {out['decode']['kernel_ms_per_step'] * 1e3:.1f} us, "
             f"{out['decode']['GB_per_s']:.0f} GB/s")
     if not args.no_cpu_baseline:

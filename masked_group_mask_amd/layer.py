@@ -1,0 +1,122 @@
+"""Device-resident masked layer: buffers and the launch sequence of one step.
+
+A prefill step runs, on the current stream: the reorder of the attention and
+FFN masks, q_proj (GEMM-MN), attention, o_proj (GEMM-K), the gate/up
+projections fused with SwiGLU (GEMM-MN) and down_proj (GEMM-K). A decode step
+runs the matrix-vector variants and split-KV attention on one token, reading
+the mask bytes directly. All buffers are allocated once here; a step launches
+kernels only.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import _lib as mg
+
+PREFILL_OPS = ("reorder", "q_proj", "attention", "o_proj", "gate_up_swiglu", "down_proj")
+DECODE_OPS = ("q_proj", "attention", "o_proj", "gate_up_swiglu", "down_proj")
+
+
+def to_device(x: np.ndarray) -> torch.Tensor:
+    """numpy -> device tensor; uint16 arrays are bf16 bit patterns."""
+    x = np.ascontiguousarray(x)
+    if x.dtype == np.uint16:
+        return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(x).cuda()
+
+
+class PrefillLayer:
+    """One masked layer of shape `s` (workloads.LayerShape) on the GPU."""
+
+    def __init__(self, s, host: dict, with_dense: bool = True):
+        self.s = s
+        d = lambda k: to_device(host[k])  # noqa: E731
+        self.x = d("x")
+        self.wq, self.wo = d("w_q"), d("w_o")
+        self.wg, self.wu, self.wd = d("w_gate"), d("w_up"), d("w_down")
+        self.k, self.v = d("k"), d("v")
+        ma, mf = d("mask_attn"), d("mask_ffn")
+        self.masks = {"masked": (ma, mf)}
+        if with_dense:
+            self.masks["dense"] = (torch.ones_like(ma), torch.ones_like(mf))
+        dev = self.x.device
+        M, B, T = s.M, s.B, s.T
+        i32 = torch.int32
+        self.perm_a = torch.empty((B, s.Hk, T), dtype=i32, device=dev)
+        self.cnt_a = torch.empty((B, s.Hk), dtype=i32, device=dev)
+        self.perm_f = torch.empty((1, s.NG_ffn, M), dtype=i32, device=dev)
+        self.cnt_f = torch.empty((1, s.NG_ffn), dtype=i32, device=dev)
+        # Every consumer reads only the active entries of its input (GEMM-K
+        # compacts active rows per group, attention gathers active rows), so
+        # the intermediate buffers need no zero-initialisation.
+        self.q = torch.empty((M, s.Hq * s.d), dtype=torch.bfloat16, device=dev)
+        self.o = torch.empty((B, T, s.Hq, s.d), dtype=torch.bfloat16, device=dev)
+        self.h = torch.empty((M, s.Dff), dtype=torch.bfloat16, device=dev)
+        self.y_attn = torch.empty((M, s.D), dtype=torch.float32, device=dev)
+        self.y_ffn = torch.empty((M, s.D), dtype=torch.float32, device=dev)
+        if B != 1:
+            raise ValueError("the prefill layer driver flattens tokens with B = 1")
+
+    def step(self, which: str = "masked", events=None) -> None:
+        s = self.s
+        ma, mf = self.masks[which]
+        rec = (lambda i: events[i].record()) if events is not None else (lambda i: None)
+        rec(0)
+        mg.reorder(ma, self.perm_a, self.cnt_a)
+        mg.reorder(mf.view(1, s.M, s.NG_ffn), self.perm_f, self.cnt_f)
+        rec(1)
+        # B = 1: the attention reorder is also the flattened reorder of the GEMMs.
+        mg.gemm_mn(self.x, self.wq, s.G_attn, perm=self.perm_a[0], counts=self.cnt_a[0],
+                   out=self.q)
+        rec(2)
+        mg.attn(self.q.view(s.B, s.T, s.Hq, s.d), self.k, self.v, perm=self.perm_a,
+                counts=self.cnt_a, out=self.o)
+        rec(3)
+        mg.gemm_k(self.o.view(s.M, s.Hq * s.d), self.wo, s.G_attn, ma.view(s.M, s.Hk),
+                  out=self.y_attn)
+        rec(4)
+        mg.gemm_mn_swiglu(self.x, self.wg, self.wu, s.G_ffn, perm=self.perm_f[0],
+                          counts=self.cnt_f[0], out=self.h)
+        rec(5)
+        mg.gemm_k(self.h, self.wd, s.G_ffn, mf.view(s.M, s.NG_ffn), out=self.y_ffn)
+        rec(6)
+
+
+class DecodeLayer:
+    """One-token decode step of shape `s` with `sets` rotated weight/KV copies."""
+
+    def __init__(self, s, host: dict, sets: int = 1):
+        self.s = s
+        d = lambda k: to_device(host[k])  # noqa: E731
+        base = {k: d(k) for k in ("w_q", "w_o", "w_gate", "w_up", "w_down", "k", "v")}
+        self.wsets = [base] + [{k: t.clone() for k, t in base.items()} for _ in range(sets - 1)]
+        self.x = d("x")
+        self.ma = d("mask_attn")                                   # [B=1][1][Hk]
+        self.mf = d("mask_ffn").view(1, s.NG_ffn)
+        dev = self.x.device
+        self.q = torch.empty((1, s.Hq * s.d), dtype=torch.bfloat16, device=dev)
+        self.o = torch.empty((1, 1, s.Hq, s.d), dtype=torch.bfloat16, device=dev)
+        self.h = torch.empty((1, s.Dff), dtype=torch.bfloat16, device=dev)
+        self.y_attn = torch.empty((1, s.D), dtype=torch.float32, device=dev)
+        self.y_ffn = torch.empty((1, s.D), dtype=torch.float32, device=dev)
+        self.ws = torch.empty(mg.attn_workspace_bytes(1, 1, s.Tkv, s.Hq, s.Hk, s.d),
+                              dtype=torch.uint8, device=dev)
+
+    def step(self, i: int = 0, events=None) -> None:
+        s = self.s
+        w = self.wsets[i % len(self.wsets)]
+        rec = (lambda j: events[j].record()) if events is not None else (lambda j: None)
+        rec(0)
+        mg.gemm_mn(self.x, w["w_q"], s.G_attn, mask=self.ma.view(1, s.Hk), out=self.q)
+        rec(1)
+        mg.attn(self.q.view(1, 1, s.Hq, s.d), w["k"], w["v"], mask=self.ma, out=self.o,
+                workspace=self.ws)
+        rec(2)
+        mg.gemm_k(self.o.view(1, s.Hq * s.d), w["w_o"], s.G_attn, self.ma.view(1, s.Hk),
+                  out=self.y_attn)
+        rec(3)
+        mg.gemm_mn_swiglu(self.x, w["w_gate"], w["w_up"], s.G_ffn, mask=self.mf, out=self.h)
+        rec(4)
+        mg.gemm_k(self.h, w["w_down"], s.G_ffn, self.mf, out=self.y_ffn)
+        rec(5)
