@@ -98,8 +98,9 @@ int wide_reorder(const uint8_t *mask, int64_t batch, int64_t rows, int64_t group
  * zero-initialises C when it needs zeros there (Algorithm 2 takes a
  * zero-initialised C).
  * Requirements: K % 8 == 0; lda, ldb >= K and multiples of 8; ldc >= N;
- * A, B, C 16-byte aligned; G % 64 == 0 (WIDE_ERR_UNSUPPORTED otherwise);
- * C must not overlap A or B.
+ * A, B, C 16-byte aligned; C must not overlap A or B. WIDE_ERR_UNSUPPORTED
+ * unless G % 64 == 0 and M * lda * 2 < 2^31 (rows are gathered with 32-bit
+ * byte offsets).
  */
 int wide_gemm_mn(const wide_bf16 *A, int64_t lda, const wide_bf16 *B, int64_t ldb,
                  void *C, int64_t ldc, int c_dtype, int64_t M, int64_t N, int64_t K,
@@ -136,8 +137,10 @@ int wide_gemm_mn_swiglu(const wide_bf16 *A, int64_t lda, const wide_bf16 *Wg,
  * Each output tile compacts the active rows of every K-group from the mask
  * itself, so no reorder output is needed. Summation order is fixed: results
  * are bitwise reproducible run to run.
- * Requirements: K % G == 0; G % 64 == 0; N % 64 == 0; lda, ldb >= K and
- * multiples of 8; ldc >= N; 16-byte aligned A, B, C; C must not overlap A or B.
+ * Requirements: K % G == 0; lda, ldb >= K and multiples of 8; ldc >= N and a
+ * multiple of 4; 16-byte aligned A, B, C; C must not overlap A, B or mask.
+ * WIDE_ERR_UNSUPPORTED unless G % 64 == 0, K / G <= 512, N % 128 == 0 and
+ * lda < 2^23.
  */
 int wide_gemm_k(const wide_bf16 *A, int64_t lda, const wide_bf16 *B, int64_t ldb,
                 float *C, int64_t ldc, int beta, int64_t M, int64_t N, int64_t K,
@@ -163,8 +166,9 @@ int wide_gemm_k(const wide_bf16 *A, int64_t lda, const wide_bf16 *B, int64_t ldb
  *     reads the routing bytes directly; no reorder runs).
  *   workspace: device scratch of at least wide_attn_workspace_bytes(...)
  *     bytes (0 bytes for Tq > 1); may be NULL when that is 0.
- * Requirements: d == 128; Hq % Hk == 0; Tk >= Tq >= 1; 16-byte aligned
- * Q, K, V, O; O must not overlap Q, K or V.
+ * Requirements: Hq % Hk == 0; Tk >= Tq >= 1; 16-byte aligned Q, K, V, O;
+ * O must not overlap Q, K or V. WIDE_ERR_UNSUPPORTED unless d == 128, one
+ * sequence's Q and K each span less than 2^31 bytes, and (decoding) Hq/Hk <= 8.
  */
 int wide_attn(const wide_bf16 *Q, const wide_bf16 *K, const wide_bf16 *V, void *O,
               int o_dtype, int64_t B, int64_t Tq, int64_t Tk, int64_t Hq, int64_t Hk,

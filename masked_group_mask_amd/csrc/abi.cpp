@@ -3,6 +3,7 @@
 // error without touching the device or the caller's buffers.
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <atomic>
@@ -61,6 +62,8 @@ int check_mn(const wide_bf16 *A, int64_t lda, const wide_bf16 *B0, const wide_bf
       (B1 && overlap(C, cb, B1, span_bytes(N, K, ldb, 2))))
     return WIDE_ERR_INVALID_ARG;
   if (G % 64 != 0) return WIDE_ERR_UNSUPPORTED;
+  // Gathered rows are addressed with 32-bit byte offsets into A.
+  if ((uint64_t)M * (uint64_t)lda * 2u > 0x7fffffffull) return WIDE_ERR_UNSUPPORTED;
   return WIDE_OK;
 }
 
@@ -135,8 +138,11 @@ int wide_gemm_k(const wide_bf16 *A, int64_t lda, const wide_bf16 *B, int64_t ldb
       overlap(C, cb, mask, (size_t)M * (K / G)))
     return WIDE_ERR_INVALID_ARG;
   if (G % 64 != 0 || K / G > 512 || N % 128 != 0) return WIDE_ERR_UNSUPPORTED;
+  if ((uint64_t)lda * 256u > 0x7fffffffull) return WIDE_ERR_UNSUPPORTED;  // 32-bit tile offsets
   if (!device_ok()) return WIDE_ERR_NO_DEVICE;
-  wide::KArgs a{A, lda, B, ldb, C, ldc, beta, (int)M, (int)N, (int)K, (int)G, mask};
+  const char *r = getenv("WIDE_GEMMK_RASTER");
+  wide::KArgs a{A, lda, B, ldb, C, ldc, beta, (int)M, (int)N, (int)K, (int)G, mask,
+                r ? atoi(r) : 2};
   return wide::launch_gemm_k(a, reinterpret_cast<hipStream_t>(stream));
 }
 
@@ -171,6 +177,9 @@ int wide_attn(const wide_bf16 *Q, const wide_bf16 *K, const wide_bf16 *V, void *
                    overlap(workspace, need, K, kb) || overlap(workspace, need, V, kb)))
     return WIDE_ERR_INVALID_ARG;
   if (d != 128) return WIDE_ERR_UNSUPPORTED;
+  // Per-sequence Q/K/V are addressed with 32-bit byte offsets.
+  if ((uint64_t)Tq * Hq * d * 2u > 0x7fffffffull || (uint64_t)Tk * Hk * d * 2u > 0x7fffffffull)
+    return WIDE_ERR_UNSUPPORTED;
   if (Tq == 1 && Hq / Hk > 8) return WIDE_ERR_UNSUPPORTED;
   if (!device_ok()) return WIDE_ERR_NO_DEVICE;
   wide::AttnArgs a{};

@@ -87,33 +87,36 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a) {
 
   const size_t q_row = (size_t)a.Hq * kAd;       // elements between tokens of Q/O
   const size_t kv_row = (size_t)a.Hk * kAd;      // elements between tokens of K/V
-  const uint16_t *Qb = a.Q + (size_t)b * a.Tq * q_row + (size_t)h * kAd;
-  const uint16_t *Kb = a.K + (size_t)b * a.Tk * kv_row + (size_t)g * kAd;
-  const uint16_t *Vb = a.V + (size_t)b * a.Tk * kv_row + (size_t)g * kAd;
-
-  const u32x4 zero4 = {0u, 0u, 0u, 0u};
+  // Q, K and V of this batch as buffer resources: inactive query rows and keys
+  // past Tk get out-of-range offsets (zeros, no traffic), so every load is
+  // issued unconditionally.
+  const rsrc_t q_rsrc = make_rsrc(a.Q + (size_t)b * a.Tq * q_row, (uint64_t)a.Tq * q_row * 2);
+  const rsrc_t k_rsrc = make_rsrc(a.K + (size_t)b * a.Tk * kv_row, (uint64_t)a.Tk * kv_row * 2);
+  const rsrc_t v_rsrc = make_rsrc(a.V + (size_t)b * a.Tk * kv_row, (uint64_t)a.Tk * kv_row * 2);
   u32x4 qreg[2][4];
 #pragma unroll
   for (int qf = 0; qf < 2; ++qf)
 #pragma unroll
     for (int ds = 0; ds < 4; ++ds)
-      qreg[qf][ds] = qpos[qf] >= 0 ? ld16(Qb + (size_t)qpos[qf] * q_row + ds * 32 + (lane / 16) * 8) : zero4;
+      qreg[qf][ds] = buf_ld16(q_rsrc, qpos[qf] >= 0
+          ? (uint32_t)(qpos[qf] * q_row + h * kAd + ds * 32 + (lane / 16) * 8) * 2u : kOffNone);
 
   // K/V tile loaders: K rows (tid/16 + 16p), V key pairs (2*(tid/16) + 32p, +1).
   const int kc = tid % 16;
   const int kr = tid / 16;
+  const uint32_t kv_col = (uint32_t)(g * kAd + kc * 8) * 2u;
   u32x4 rk[4], rv[4];
   auto gload = [&](int t) {
     const int j0 = t * kAk;
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       const int j = j0 + kr + 16 * p;
-      rk[p] = j < a.Tk ? ld16(Kb + (size_t)j * kv_row + kc * 8) : zero4;
+      rk[p] = buf_ld16(k_rsrc, j < a.Tk ? (uint32_t)j * (uint32_t)kv_row * 2u + kv_col : kOffNone);
     }
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       const int j = j0 + 32 * (p / 2) + 2 * kr + (p % 2);
-      rv[p] = j < a.Tk ? ld16(Vb + (size_t)j * kv_row + kc * 8) : zero4;
+      rv[p] = buf_ld16(v_rsrc, j < a.Tk ? (uint32_t)j * (uint32_t)kv_row * 2u + kv_col : kOffNone);
     }
   };
   auto lstore = [&](int buf) {

@@ -46,6 +46,22 @@ __device__ __forceinline__ void st16(void *p, const u32x4 &v) { *reinterpret_cas
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
+// Buffer resource over [base, base + bytes) (raw, stride 0). A load whose
+// byte offset lies outside the range returns zeros and touches no memory, so
+// predicated gathers can be issued unconditionally (no branch around the
+// load, which keeps the compiler's load counters exact across prefetches).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr uint32_t kOffNone = 0x80000000u;  // an offset past any valid range
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint64_t bytes) {
+  const uint32_t n = bytes > 0x7fffffffull ? 0x7fffffffu : (uint32_t)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)n, 0x00020000);
+}
+
+__device__ __forceinline__ u32x4 buf_ld16(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+
 // Number of set bits of `m` below this lane (a wave-wide exclusive rank).
 __device__ __forceinline__ int rank_below(uint64_t m) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));

@@ -24,33 +24,78 @@
 //   - C is written once, coalesced, as beta*C + acc.
 // For M <= 4 a matrix-vector kernel streams only the active K-groups of each
 // weight row.
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace wide {
 
-constexpr int kKBM = 128;
-constexpr int kKBN = 128;
-constexpr int kKBK = 64;
-constexpr int kKLds = kKBK + 8;
-constexpr int kKAccLd = kKBN + 4;
+constexpr int kKBM = 128;          // original rows per workgroup tile
+constexpr int kKBN = 128;          // output features per workgroup tile
+constexpr int kKAccLd = kKBN + 4;  // LDS accumulator row stride (fp32)
 constexpr int kKMaxGroups = 512;
-constexpr int kKThreads = 256;
+constexpr int kKThreads = 512;  // 8 waves: two per SIMD
 
+// LDS tiles hold rows of 64 bf16 (128 bytes, 8 chunks of 16 bytes) without
+// padding. Chunk `c` of row `s` sits at position c ^ ((s / 2) % 8): the 16
+// rows one MFMA operand read touches then cover all 64 banks once.
+__device__ __forceinline__ int tile_pos(int s, int c) { return c ^ ((s >> 1) & 7); }
+
+constexpr int kKBK = 64;                       // K depth of one pipeline item
+constexpr int kKTile = 128 * kKBK;             // bf16 elements per 128-row tile
+
+// Logical tile id -> (row tile, feature tile). raster 0: row tiles fastest
+// (consecutive tiles share weights); 1: feature tiles fastest (they share the
+// activation rows); 2: blocks of 4 row tiles x 8 feature tiles, so the 32
+// workgroups an XCD runs at once share both operands in its L2.
+__device__ __forceinline__ void tile_order(int L, int m_tiles, int n_tiles, int raster, int &mt,
+                                           int &nt) {
+  constexpr int SM = 4, SN = 8;
+  if (raster == 2 && m_tiles % SM == 0 && n_tiles % SN == 0) {
+    const int blk = L / (SM * SN), in = L % (SM * SN);
+    const int nb = n_tiles / SN;
+    mt = (blk / nb) * SM + in % SM;
+    nt = (blk % nb) * SN + in / SM;
+  } else if (raster == 1) {
+    mt = L / n_tiles;
+    nt = L % n_tiles;
+  } else {
+    mt = L % m_tiles;
+    nt = L / m_tiles;
+  }
+}
+
+// One workgroup = C[r0:r0+128, n0:n0+128]. The work is a sequence of items
+// (active group, 64-wide slice of its K range). Per item:
+//   - the group's active rows of A (their list is built from the mask two
+//     items ahead) and the 128 weight rows are loaded with whole 128-byte
+//     lines per row and staged in swizzled LDS tiles (double-buffered; the
+//     loads of item i+1 are in flight while item i computes);
+//   - each wave computes D^T[n][slot] = W[n][k] * A[slot][k] for its 32
+//     features and every 16-slot fragment up to the active count, on
+//     v_mfma_f32_16x16x32_bf16, so a lane ends with 4 consecutive features
+//     of one compact row;
+//   - after the group's last slice those 4 values are added into the fp32
+//     LDS accumulator at the row the slot came from (16-byte read-add-write).
 __global__ __launch_bounds__(kKThreads, 1) void gemm_k_kernel(KArgs a) {
+  constexpr int kWaves = kKThreads / kWave;
   __shared__ __attribute__((aligned(16))) float sAcc[kKBM * kKAccLd];
-  __shared__ __attribute__((aligned(16))) uint16_t sA[2][kKBM * kKLds];
-  __shared__ __attribute__((aligned(16))) uint16_t sB[2][kKBN * kKLds];
+  __shared__ __attribute__((aligned(16))) uint16_t sAct[2][kKTile];
+  __shared__ __attribute__((aligned(16))) uint16_t sW[2][kKTile];
   __shared__ uint64_t sBits[kKMaxGroups][2];
   __shared__ uint16_t sGrp[kKMaxGroups];
-  __shared__ uint8_t sRowOf[2][kKBM];
+  __shared__ uint8_t sRowOf[3][kKBM];
   __shared__ int sNact;
+  static_assert(sizeof(sAct) >= 64 * kKMaxGroups, "mask staging needs 64 rows x max groups");
 
   const int n_tiles = a.N / kKBN;
   const int m_tiles = (a.M + kKBM - 1) / kKBM;
   const int L = xcd_remap(blockIdx.x, n_tiles * m_tiles);
-  const int n0 = (L / m_tiles) * kKBN;
-  const int r0 = (L % m_tiles) * kKBM;
+  int mt, nt;
+  tile_order(L, m_tiles, n_tiles, a.raster, mt, nt);
+  const int n0 = nt * kKBN;
+  const int r0 = mt * kKBM;
   const int NG = a.K / a.G;
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
@@ -59,18 +104,31 @@ __global__ __launch_bounds__(kKThreads, 1) void gemm_k_kernel(KArgs a) {
   for (int i = tid * 4; i < kKBM * kKAccLd; i += kKThreads * 4)
     *reinterpret_cast<f32x4 *>(&sAcc[i]) = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // Row sets per group: wave w covers rows (w & 1) * 64 + lane of every
-  // second group starting at w >> 1.
+  // Row sets per group. Each half of the mask tile ([64 rows][NG] bytes, at
+  // most 32 KB) is copied to LDS (the activation buffers are free until the
+  // main loop); then every wave ballots the 64 rows of a quarter of the groups.
   {
-    const int half = wave & 1;
-    const int r = r0 + half * 64 + lane;
-    const uint8_t *mrow = a.mask + (size_t)r * NG;
-    for (int g = wave >> 1; g < NG; g += 2) {
-      const uint64_t b = __ballot(r < a.M && mrow[g] != 0);
-      if (lane == 0) sBits[g][half] = b;
+    uint8_t *sMask = reinterpret_cast<uint8_t *>(&sAct[0][0]);
+    const bool vec = (NG % 16) == 0 && (reinterpret_cast<uintptr_t>(a.mask) % 16) == 0;
+    for (int half = 0; half < 2; ++half) {
+      const int rb = r0 + half * 64;
+      const int rows = max(0, min(64, a.M - rb));
+      const uint8_t *src = a.mask + (size_t)rb * NG;
+      const int nbytes = rows * NG;
+      if (vec) {
+        for (int i = tid * 16; i < nbytes; i += kKThreads * 16) st16(sMask + i, ld16(src + i));
+      } else {
+        for (int i = tid; i < nbytes; i += kKThreads) sMask[i] = src[i];
+      }
+      __syncthreads();
+      for (int g = wave; g < NG; g += kWaves) {
+        const uint64_t bal = __ballot(lane < rows && sMask[lane * NG + g] != 0);
+        if (lane == 0) sBits[g][half] = bal;
+      }
+      __syncthreads();
     }
   }
-  __syncthreads();
+  // Active groups (level 0: a (tile, group) pair with no active row is skipped).
   if (wave == 0) {
     int base = 0;
     for (int g0 = 0; g0 < NG; g0 += kWave) {
@@ -84,95 +142,150 @@ __global__ __launch_bounds__(kKThreads, 1) void gemm_k_kernel(KArgs a) {
   }
   __syncthreads();
 
-  const int kpg = a.G / kKBK;
-  const int nitems = uniform(sNact) * kpg;
-  const int chunk = tid % 8;
-  const int rbase = tid / 8;
-  const int wm = wave / 2, wn = wave % 2;
+  const int ipg = a.G / kKBK;  // items per group
+  const int nact = uniform(sNact);
+  const int nitems = nact * ipg;
 
-  u32x4 ra[4], rb[4];
-  int rslot[4];
-  auto gload = [&](int item) {
-    const int gi = item / kpg, ks = item % kpg;
+  // slot -> row list of active group ordinal gi, into ring slot gi % 3
+  // (waves 0 and 1 each rank 64 rows with a ballot).
+  auto build_list = [&](int gi) {
+    if (gi >= nact || wave >= 2) return;
     const int g = sGrp[gi];
     const uint64_t b0 = sBits[g][0], b1 = sBits[g][1];
+    const uint64_t bw = wave == 0 ? b0 : b1;
+    if ((bw >> lane) & 1ull) {
+      const int slot = (wave == 0 ? 0 : __popcll(b0)) + rank_below(bw);
+      sRowOf[gi % 3][slot] = (uint8_t)(wave * 64 + lane);
+    }
+  };
+
+  const int chunk = tid % 8;
+  const int rsub = tid / 8;  // 0..63
+  const int wm = wave / 4;   // slot fragments wm, wm + 2, ...
+  const int wn = wave % 4;   // features wn * 32 .. + 32
+  const rsrc_t arows = make_rsrc(a.A + (size_t)r0 * a.lda,
+                                 (uint64_t)min(kKBM, a.M - r0) * a.lda * 2);
+  const uint16_t *wbase = a.B + (size_t)n0 * a.ldb + chunk * 8;
+  u32x4 ra[2], rw[2];
+
+  auto issue = [&](int item) {
+    const int gi = item / ipg, ks = item % ipg;
+    const int g = sGrp[gi];
+    const int cnt = __popcll(sBits[g][0]) + __popcll(sBits[g][1]);
     const int kcol = g * a.G + ks * kKBK + chunk * 8;
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const int r = rbase + 32 * p;
-      const uint64_t bits = r < 64 ? b0 : b1;
-      const uint64_t below = bits & ((1ull << (r & 63)) - 1ull);
-      const bool on = (bits >> (r & 63)) & 1ull;
-      rslot[p] = on ? (r < 64 ? 0 : __popcll(b0)) + __popcll(below) : -1;
-      if (on) ra[p] = ld16(a.A + (size_t)(r0 + r) * a.lda + kcol);  // level 1
-      rb[p] = ld16(a.B + (size_t)(n0 + r) * a.ldb + kcol);
+    for (int p = 0; p < 2; ++p) {
+      const int sl = rsub + 64 * p;
+      // level 1: only the active rows are fetched (packed by slot)
+      const uint32_t off = sl < cnt ? (uint32_t)(sRowOf[gi % 3][sl] * a.lda + kcol) * 2u : kOffNone;
+      ra[p] = buf_ld16(arows, off);
     }
-  };
-  auto lstore = [&](int buf, int par) {
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      if (rslot[p] >= 0) {
-        st16(&sA[buf][rslot[p] * kKLds + chunk * 8], ra[p]);
-        if (chunk == 0) sRowOf[par][rslot[p]] = (uint8_t)(rbase + 32 * p);
-      }
-      st16(&sB[buf][(rbase + 32 * p) * kKLds + chunk * 8], rb[p]);
+    for (int p = 0; p < 2; ++p) rw[p] = ld16(wbase + (size_t)(rsub + 64 * p) * a.ldb + (kcol - chunk * 8));
+  };
+  auto stage = [&](int buf) {
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int r = rsub + 64 * p;
+      st16(&sAct[buf][r * kKBK + tile_pos(r, chunk) * 8], ra[p]);
+      st16(&sW[buf][r * kKBK + tile_pos(r, chunk) * 8], rw[p]);
     }
   };
 
-  f32x4 acc[4][4];
+  f32x4 acc[2][4];  // [feature fragment][own slot fragment j: sf = wm + 2j]
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int nf = 0; nf < 2; ++nf)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 4; ++j) acc[nf][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // The slot -> row list of the group of item j is built in iteration j - 2
+  // (before the barrier that precedes the loads of item j, issued in
+  // iteration j - 1); ring slot g % 3 is then free, as group g - 3 has
+  // finished. Items 0 and 1 are covered here.
+  build_list(0);
+  if (ipg == 1) build_list(1);
+  __syncthreads();
   if (nitems > 0) {
-    gload(0);
-    lstore(0, 0);
+    issue(0);
+    stage(0);
   }
   __syncthreads();
+
   for (int it = 0; it < nitems; ++it) {
     const int cur = it & 1;
-    const int gi = it / kpg, ks = it % kpg;
+    const int gi = it / ipg, ks = it % ipg;
     const int g = sGrp[gi];
     const int cnt = uniform(__popcll(sBits[g][0]) + __popcll(sBits[g][1]));
-    if (it + 1 < nitems) gload(it + 1);
+    const int live = (cnt + 15) / 16;
+    const bool more = it + 1 < nitems;
+    const bool last = ks == ipg - 1;
+    const int ring = gi % 3;
+    if (more) issue(it + 1);  // the next item's global loads go out first
+
+    u32x4 wfr[2][2];  // [feature fragment][k step]
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const int koff = kk * 32 + (lane / 16) * 8;
-      u32x4 bf[4];
+    for (int nf = 0; nf < 2; ++nf)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) bf[j] = ld16(&sB[cur][(wn * 64 + 16 * j + lane % 16) * kKLds + koff]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int f = wm + 2 * i;
-        if (16 * f < cnt) {  // level 2
-          const u32x4 af = ld16(&sA[cur][(16 * f + lane % 16) * kKLds + koff]);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) acc[i][j] = mfma16x16x32(af, bf[j], acc[i][j]);
-        }
+      for (int q = 0; q < 2; ++q) {
+        const int r = wn * 32 + nf * 16 + lane % 16;
+        wfr[nf][q] = ld16(&sW[cur][r * kKBK + tile_pos(r, q * 4 + lane / 16) * 8]);
       }
-    }
-    if (ks == kpg - 1) {
-      // Add this group's partial products into the LDS accumulator.
-      const int par = gi & 1;
+    // level 2: only ceil(cnt/16) 16-slot fragments are issued; the body is
+    // specialised on that count (rounded up to even) so all LDS reads of a K
+    // step are issued before its MFMAs, with no branch in between.
+    auto body = [&](auto nsf_c) {
+      constexpr int NJ = decltype(nsf_c)::value / 2;  // own fragments: sf = wm + 2j
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int f = wm + 2 * i;
-        if (16 * f >= cnt) continue;
+      for (int q = 0; q < 2; ++q) {
+        u32x4 act[NJ];
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int slot = 16 * f + 4 * (lane / 16) + v;
-          if (slot < cnt) {
-            float *dst = &sAcc[sRowOf[par][slot] * kKAccLd + wn * 64 + lane % 16];
+        for (int j = 0; j < NJ; ++j) {
+          const int s = (wm + 2 * j) * 16 + lane % 16;
+          act[j] = ld16(&sAct[cur][s * kKBK + tile_pos(s, q * 4 + lane / 16) * 8]);
+        }
 #pragma unroll
-            for (int j = 0; j < 4; ++j) dst[16 * j] += acc[i][j][v];
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+          for (int nf = 0; nf < 2; ++nf) acc[nf][j] = mfma16x16x32(wfr[nf][q], act[j], acc[nf][j]);
+      }
+      if (last) {
+        // Add the group's partial products into the LDS accumulator at the
+        // rows the slots came from (16-byte read-add-write per lane; within a
+        // group every (row, feature) belongs to one lane).
+        int rrow[NJ];
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          const int s = (wm + 2 * j) * 16 + lane % 16;
+          rrow[j] = s < cnt ? (int)sRowOf[ring][s] : -1;
+        }
+        f32x4 old[NJ][2];
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+          for (int nf = 0; nf < 2; ++nf)
+            if (rrow[j] >= 0)
+              old[j][nf] = *reinterpret_cast<const f32x4 *>(
+                  &sAcc[rrow[j] * kKAccLd + wn * 32 + nf * 16 + (lane / 16) * 4]);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+          for (int nf = 0; nf < 2; ++nf) {
+            if (rrow[j] >= 0)
+              *reinterpret_cast<f32x4 *>(&sAcc[rrow[j] * kKAccLd + wn * 32 + nf * 16 + (lane / 16) * 4]) =
+                  old[j][nf] + acc[nf][j];
+            acc[nf][j] = f32x4{0.f, 0.f, 0.f, 0.f};
           }
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
+    };
+    switch ((live + 1) / 2) {
+      case 0: break;
+      case 1: body(std::integral_constant<int, 2>{}); break;
+      case 2: body(std::integral_constant<int, 4>{}); break;
+      case 3: body(std::integral_constant<int, 6>{}); break;
+      default: body(std::integral_constant<int, 8>{}); break;
     }
-    if (it + 1 < nitems) lstore(cur ^ 1, ((it + 1) / kpg) & 1);
+    if ((it + 2) % ipg == 0) build_list((it + 2) / ipg);
+    if (more) stage(cur ^ 1);
     __syncthreads();
   }
 

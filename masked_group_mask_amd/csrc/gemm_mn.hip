@@ -73,34 +73,40 @@ __global__ __launch_bounds__(kMnThreads, 2) void gemm_mn_kernel(MnArgs a) {
 
   const int chunk = tid % 8;
   const int rbase = tid / 8;
-  const uint16_t *a_ptr[A_PASSES];
-  bool a_ok[A_PASSES];
+  // Gathered A rows and the B tile as buffer resources: rows past the count
+  // and the K tail get out-of-range offsets (zeros, no memory traffic), so
+  // every load is issued unconditionally.
+  const rsrc_t ra_rsrc = make_rsrc(a.A, (uint64_t)a.M * a.lda * 2);
+  uint32_t a_off[A_PASSES];
 #pragma unroll
   for (int p = 0; p < A_PASSES; ++p) {
     const int r = rbase + 32 * p;
-    a_ok[p] = r < rows;  // level 1: rows past the count are never loaded
-    a_ptr[p] = a.A + (size_t)sRows[r] * a.lda + chunk * 8;
+    // level 1: rows past the count are never fetched
+    a_off[p] = r < rows ? (uint32_t)(sRows[r] * a.lda + chunk * 8) * 2u : kOffNone;
   }
-  const uint16_t *b_ptr[B_PASSES];
+  rsrc_t rb_rsrc[2];
+  rb_rsrc[0] = make_rsrc(a.B0 + (size_t)n0 * a.ldb, (uint64_t)(SWIGLU ? BNT / 2 : BNT) * a.ldb * 2);
+  rb_rsrc[1] = SWIGLU ? make_rsrc(a.B1 + (size_t)n0 * a.ldb, (uint64_t)(BNT / 2) * a.ldb * 2) : rb_rsrc[0];
+  uint32_t b_off[B_PASSES];
 #pragma unroll
   for (int p = 0; p < B_PASSES; ++p) {
     const int br = rbase + 32 * p;
-    if (SWIGLU)
-      b_ptr[p] = (br < BNT / 2 ? a.B0 + (size_t)(n0 + br) * a.ldb
-                               : a.B1 + (size_t)(n0 + br - BNT / 2) * a.ldb) + chunk * 8;
-    else
-      b_ptr[p] = a.B0 + (size_t)(n0 + br) * a.ldb + chunk * 8;
+    const int lr = (SWIGLU && br >= BNT / 2) ? br - BNT / 2 : br;
+    b_off[p] = (uint32_t)(lr * a.ldb + chunk * 8) * 2u;
   }
 
   const int nk = (a.K + kMnBK - 1) / kMnBK;
   u32x4 ra[A_PASSES], rb[B_PASSES];
-  const u32x4 zero4 = {0u, 0u, 0u, 0u};
   auto gload = [&](int kt) {
     const bool kin = kt * kMnBK + chunk * 8 < a.K;
+    const uint32_t kb = (uint32_t)(kt * kMnBK) * 2u;
 #pragma unroll
-    for (int p = 0; p < A_PASSES; ++p) ra[p] = (a_ok[p] && kin) ? ld16(a_ptr[p] + kt * kMnBK) : zero4;
+    for (int p = 0; p < A_PASSES; ++p) ra[p] = buf_ld16(ra_rsrc, kin ? a_off[p] + kb : kOffNone);
 #pragma unroll
-    for (int p = 0; p < B_PASSES; ++p) rb[p] = kin ? ld16(b_ptr[p] + kt * kMnBK) : zero4;
+    for (int p = 0; p < B_PASSES; ++p) {
+      const int which = (SWIGLU && rbase + 32 * p >= BNT / 2) ? 1 : 0;
+      rb[p] = buf_ld16(which ? rb_rsrc[1] : rb_rsrc[0], kin ? b_off[p] + kb : kOffNone);
+    }
   };
   auto lstore = [&](int buf) {
 #pragma unroll
@@ -134,12 +140,24 @@ __global__ __launch_bounds__(kMnThreads, 2) void gemm_mn_kernel(MnArgs a) {
       u32x4 bf[NF];
 #pragma unroll
       for (int j = 0; j < NF; ++j) bf[j] = ld16(&sB[cur][(brow(j) + lane % 16) * kMnLds + koff]);
+      if (live == MF) {
+        // Fully active rows (every tile of a group but the last): no
+        // predicate, all fragment reads issued together.
+        u32x4 af[MF];
 #pragma unroll
-      for (int i = 0; i < MF; ++i) {
-        if (i < live) {  // level 2: skip fragments past the count
-          const u32x4 af = ld16(&sA[cur][(wm * 64 + 16 * i + lane % 16) * kMnLds + koff]);
+        for (int i = 0; i < MF; ++i) af[i] = ld16(&sA[cur][(wm * 64 + 16 * i + lane % 16) * kMnLds + koff]);
 #pragma unroll
-          for (int j = 0; j < NF; ++j) acc[i][j] = mfma16x16x32(af, bf[j], acc[i][j]);
+        for (int i = 0; i < MF; ++i)
+#pragma unroll
+          for (int j = 0; j < NF; ++j) acc[i][j] = mfma16x16x32(af[i], bf[j], acc[i][j]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < MF; ++i) {
+          if (i < live) {  // level 2: skip fragments past the count
+            const u32x4 af = ld16(&sA[cur][(wm * 64 + 16 * i + lane % 16) * kMnLds + koff]);
+#pragma unroll
+            for (int j = 0; j < NF; ++j) acc[i][j] = mfma16x16x32(af, bf[j], acc[i][j]);
+          }
         }
       }
     }
