@@ -251,7 +251,6 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a) {
 // ---------------------------------------------------------------------------
 
 constexpr int kDecKeys = 256;      // keys per split
-constexpr int kDecMaxRep = 8;      // query heads per KV head supported
 constexpr int kDecPart = kAd + 4;  // floats per partial: o[128], m, z (+pad)
 
 __device__ __forceinline__ bool group_active(const AttnArgs &a, int b, int g) {
@@ -259,11 +258,19 @@ __device__ __forceinline__ bool group_active(const AttnArgs &a, int b, int g) {
   return a.counts[(size_t)b * a.Hk + g] > 0;
 }
 
+// One split = 256 keys of one active (b, g), for all Hq/Hk heads of the
+// group. Lane l of a wave handles key quad slot l / 16 and head-dim chunk
+// l % 16 (8 values), so every 16-byte load of K and V covers whole lines of
+// four key rows; the 16 K loads and 16 V loads of a lane are issued before
+// any is used. Scores are reduced over the 16 lanes of a key, then the
+// split's max and sum per head come from an LDS reduction; the unnormalised
+// output is reduced over the key slots of a wave and then over the waves.
+template <int RMAX>
 __global__ __launch_bounds__(256) void attn_decode_split_kernel(AttnArgs a, int nsplit) {
-  __shared__ float sQ[kDecMaxRep][kAd];
-  __shared__ float sP[kDecMaxRep][kDecKeys];
-  __shared__ float sRed[kDecMaxRep][4];
-  __shared__ float sO[4][kDecMaxRep][kAd];
+  constexpr int IT = kDecKeys / 16;  // key quads per wave (16 x 4 = 64 keys)
+  __shared__ float sP[RMAX][kDecKeys];
+  __shared__ float sRed[RMAX][4];
+  __shared__ float sO[4][RMAX][kAd];
 
   const int split = blockIdx.x;
   const int g = blockIdx.y;
@@ -273,6 +280,7 @@ __global__ __launch_bounds__(256) void attn_decode_split_kernel(AttnArgs a, int 
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
   const int wave = tid / kWave;
+  const int kq = lane / 16, dc = lane % 16;
   const int jmin = a.leftpad ? a.leftpad[b] : 0;
   const int j0 = split * kDecKeys;
   const int jlo = max(j0, jmin);
@@ -280,96 +288,127 @@ __global__ __launch_bounds__(256) void attn_decode_split_kernel(AttnArgs a, int 
   float *ws = reinterpret_cast<float *>(a.workspace);
   const size_t q_row = (size_t)a.Hq * kAd, kv_row = (size_t)a.Hk * kAd;
 
-  if (jlo >= jhi) {
-    if (tid < rep) {
-      float *part = ws + (((size_t)b * a.Hq + g * rep + tid) * nsplit + split) * kDecPart;
-      part[kAd] = -INFINITY;
-      part[kAd + 1] = 0.f;
+  if (jlo >= jhi) {  // every key of the split is before the sequence's left padding
+    for (int i = tid; i < rep * kDecPart; i += 256) {
+      const int r = i / kDecPart, c = i % kDecPart;
+      float *part = ws + (((size_t)b * a.Hq + g * rep + r) * nsplit + split) * kDecPart;
+      part[c] = c == kAd ? -INFINITY : 0.f;
     }
     return;
   }
 
-  const uint16_t *Qb = a.Q + (size_t)b * q_row + (size_t)g * rep * kAd;
-  for (int i = tid; i < rep * kAd; i += 256) sQ[i / kAd][i % kAd] = bf2f(Qb[i]);
-  __syncthreads();
+  const rsrc_t kr = make_rsrc(a.K + (size_t)b * a.Tk * kv_row, (uint64_t)a.Tk * kv_row * 2);
+  const rsrc_t vr = make_rsrc(a.V + (size_t)b * a.Tk * kv_row, (uint64_t)a.Tk * kv_row * 2);
+  u32x4 kreg[IT], vreg[IT];
+  bool kok[IT];
+#pragma unroll
+  for (int i = 0; i < IT; ++i) {
+    const int j = j0 + wave * (kDecKeys / 4) + i * 4 + kq;
+    kok[i] = j >= jlo && j < jhi;
+    const uint32_t off = kok[i] ? (uint32_t)((size_t)j * kv_row + g * kAd + dc * 8) * 2u : kOffNone;
+    kreg[i] = buf_ld16(kr, off);
+  }
+#pragma unroll
+  for (int i = 0; i < IT; ++i) {
+    const int j = j0 + wave * (kDecKeys / 4) + i * 4 + kq;
+    const uint32_t off = kok[i] ? (uint32_t)((size_t)j * kv_row + g * kAd + dc * 8) * 2u : kOffNone;
+    vreg[i] = buf_ld16(vr, off);
+  }
+  // This lane's 8 query values for every head of the group.
+  const uint16_t *Qb = a.Q + (size_t)b * q_row + (size_t)g * rep * kAd + dc * 8;
+  float qv[RMAX][8];
+#pragma unroll
+  for (int r = 0; r < RMAX; ++r) {
+    const u32x4 w = r < rep ? ld16(Qb + r * kAd) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qv[r][e] = (e % 2) ? bf_hi(w[e / 2]) : bf_lo(w[e / 2]);
+  }
 
-  // Scores: one key per thread.
+  // Scores (log2 domain): dot over this lane's chunk, then over the 16 lanes of the key.
   const float sl2 = a.scale * kLog2e;
-  const int j = j0 + tid;
-  const bool ok = j >= jlo && j < jhi;
-  float sc[kDecMaxRep];
 #pragma unroll
-  for (int r = 0; r < kDecMaxRep; ++r) sc[r] = 0.f;
-  if (ok) {
-    const uint16_t *krow = a.K + ((size_t)b * a.Tk + j) * kv_row + (size_t)g * kAd;
-#pragma unroll 4
-    for (int c = 0; c < kAd / 8; ++c) {
-      const u32x4 w = ld16(krow + c * 8);
+  for (int i = 0; i < IT; ++i) {
+    float sc[RMAX];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float kv = (e % 2) ? bf_hi(w[e / 2]) : bf_lo(w[e / 2]);
+    for (int r = 0; r < RMAX; ++r) {
+      float acc = 0.f;
 #pragma unroll
-        for (int r = 0; r < kDecMaxRep; ++r)
-          if (r < rep) sc[r] = fmaf(kv, sQ[r][c * 8 + e], sc[r]);
-      }
+      for (int e = 0; e < 8; ++e) acc = fmaf((e % 2) ? bf_hi(kreg[i][e / 2]) : bf_lo(kreg[i][e / 2]), qv[r][e], acc);
+      sc[r] = acc;
+    }
+#pragma unroll
+    for (int r = 0; r < RMAX; ++r) {
+      if (r >= rep) break;
+#pragma unroll
+      for (int o = 8; o >= 1; o >>= 1) sc[r] += __shfl_xor(sc[r], o, kWave);
+    }
+    if (dc == 0) {
+      const int jl = wave * (kDecKeys / 4) + i * 4 + kq;
+#pragma unroll
+      for (int r = 0; r < RMAX; ++r)
+        if (r < rep) sP[r][jl] = kok[i] ? sc[r] * sl2 : -INFINITY;
     }
   }
-  // Block max and sum per head.
-  float mx[kDecMaxRep];
+  __syncthreads();
+  // Split max and sum per head: thread t owns key t.
+  float mx[RMAX], zs[RMAX];
 #pragma unroll
-  for (int r = 0; r < kDecMaxRep; ++r) {
-    sc[r] = ok ? sc[r] * sl2 : -INFINITY;
-    float v = sc[r];
+  for (int r = 0; r < RMAX; ++r) {
+    float v = r < rep ? sP[r][tid] : -INFINITY;
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
     if (lane == 0) sRed[r][wave] = v;
   }
   __syncthreads();
 #pragma unroll
-  for (int r = 0; r < kDecMaxRep; ++r) {
+  for (int r = 0; r < RMAX; ++r) {
     mx[r] = fmaxf(fmaxf(sRed[r][0], sRed[r][1]), fmaxf(sRed[r][2], sRed[r][3]));
-    const float p = ok ? exp2f(sc[r] - mx[r]) : 0.f;
-    if (r < rep) sP[r][tid] = p;
+    if (r < rep) {
+      const float p = exp2f(sP[r][tid] - mx[r]);  // -inf -> 0; the split has a valid key
+      sP[r][tid] = p;
+      zs[r] = p;
+    } else {
+      zs[r] = 0.f;
+    }
   }
   __syncthreads();
-  float zs[kDecMaxRep];
 #pragma unroll
-  for (int r = 0; r < kDecMaxRep; ++r) {
-    float v = (r < rep) ? sP[r][tid] : 0.f;
+  for (int r = 0; r < RMAX; ++r) {
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
-    zs[r] = v;
+    for (int o = 32; o >= 1; o >>= 1) zs[r] += __shfl_xor(zs[r], o, kWave);
   }
-  __syncthreads();
   if (lane == 0)
 #pragma unroll
-    for (int r = 0; r < kDecMaxRep; ++r) sRed[r][wave] = zs[r];
+    for (int r = 0; r < RMAX; ++r) sRed[r][wave] = zs[r];
 
-  // Unnormalised output: thread = (dim pair, quarter of the keys).
-  const int dp = tid % 64, kq = tid / 64;
-  float o0[kDecMaxRep], o1[kDecMaxRep];
+  // Unnormalised output for this lane's chunk, over this wave's keys.
+  float o[RMAX][8];
 #pragma unroll
-  for (int r = 0; r < kDecMaxRep; ++r) o0[r] = o1[r] = 0.f;
-  const int kb = j0 + kq * 64;
-  for (int jj = 0; jj < 64; ++jj) {
-    const int jk = kb + jj;
-    if (jk < jlo || jk >= jhi) continue;
-    const uint32_t w = *reinterpret_cast<const uint32_t *>(a.V + ((size_t)b * a.Tk + jk) * kv_row +
-                                                          (size_t)g * kAd + 2 * dp);
-    const float v0 = bf_lo(w), v1 = bf_hi(w);
+  for (int r = 0; r < RMAX; ++r)
 #pragma unroll
-    for (int r = 0; r < kDecMaxRep; ++r) {
+    for (int e = 0; e < 8; ++e) o[r][e] = 0.f;
+#pragma unroll
+  for (int i = 0; i < IT; ++i) {
+    const int jl = wave * (kDecKeys / 4) + i * 4 + kq;
+#pragma unroll
+    for (int r = 0; r < RMAX; ++r) {
       if (r >= rep) break;
-      const float p = sP[r][kq * 64 + jj];
-      o0[r] = fmaf(p, v0, o0[r]);
-      o1[r] = fmaf(p, v1, o1[r]);
+      const float p = sP[r][jl];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[r][e] = fmaf(p, (e % 2) ? bf_hi(vreg[i][e / 2]) : bf_lo(vreg[i][e / 2]), o[r][e]);
     }
   }
 #pragma unroll
-  for (int r = 0; r < kDecMaxRep; ++r) {
+  for (int r = 0; r < RMAX; ++r) {
     if (r >= rep) break;
-    sO[kq][r][2 * dp] = o0[r];
-    sO[kq][r][2 * dp + 1] = o1[r];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      o[r][e] += __shfl_xor(o[r][e], 16, kWave);
+      o[r][e] += __shfl_xor(o[r][e], 32, kWave);
+    }
+    if (kq == 0)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sO[wave][r][dc * 8 + e] = o[r][e];
   }
   __syncthreads();
   for (int i = tid; i < rep * kAd; i += 256) {
@@ -383,26 +422,47 @@ __global__ __launch_bounds__(256) void attn_decode_split_kernel(AttnArgs a, int 
   }
 }
 
+// Merge of the splits of one (b, h): weights 2^(m_s - max) from the split
+// maxima (staged in LDS), then the weighted sum of the partial outputs with
+// the reads unrolled.
 template <bool OUT_F32>
 __global__ __launch_bounds__(kAd) void attn_decode_merge_kernel(AttnArgs a, int nsplit) {
+  __shared__ float sW[1024];
+  __shared__ float sZ;
   const int h = blockIdx.x;
   const int b = blockIdx.y;
   const int rep = a.Hq / a.Hk;
   if (!group_active(a, b, h / rep)) return;
   const int d = threadIdx.x;
   const float *ws = reinterpret_cast<const float *>(a.workspace) + ((size_t)b * a.Hq + h) * nsplit * kDecPart;
+  // split maxima -> LDS, global max, weights
+  for (int s = d; s < nsplit; s += kAd) sW[s] = ws[s * kDecPart + kAd];
+  __syncthreads();
   float M = -INFINITY;
-  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, ws[s * kDecPart + kAd]);
-  float Z = 0.f, o = 0.f;
-  if (M != -INFINITY) {
-    for (int s = 0; s < nsplit; ++s) {
-      const float m = ws[s * kDecPart + kAd];
-      if (m == -INFINITY) continue;
-      const float w = exp2f(m - M);
-      Z += w * ws[s * kDecPart + kAd + 1];
-      o += w * ws[s * kDecPart + d];
-    }
+  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, sW[s]);
+  __syncthreads();
+  for (int s = d; s < nsplit; s += kAd) {
+    const float m = sW[s];
+    sW[s] = (M == -INFINITY || m == -INFINITY) ? 0.f : exp2f(m - M);
   }
+  __syncthreads();
+  if (d == 0) {
+    float Z = 0.f;
+    for (int s = 0; s < nsplit; ++s) Z += sW[s] * ws[s * kDecPart + kAd + 1];
+    sZ = Z;
+  }
+  float o = 0.f;
+  int s = 0;
+  for (; s + 8 <= nsplit; s += 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = ws[(s + u) * kDecPart + d];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) o = fmaf(sW[s + u], v[u], o);
+  }
+  for (; s < nsplit; ++s) o = fmaf(sW[s], ws[s * kDecPart + d], o);
+  __syncthreads();
+  const float Z = sZ;
   const float out = Z > 0.f ? o / Z : 0.f;
   const size_t idx = (size_t)b * a.Hq * kAd + (size_t)h * kAd + d;
   if (OUT_F32)
@@ -422,7 +482,16 @@ size_t attn_workspace_bytes(int64_t B, int64_t Tq, int64_t Tk, int64_t Hq, int64
 int launch_attn(const AttnArgs &a, hipStream_t s) {
   if (a.Tq == 1) {
     const int nsplit = (a.Tk + kDecKeys - 1) / kDecKeys;
-    hipLaunchKernelGGL(attn_decode_split_kernel, dim3(nsplit, a.Hk, a.B), dim3(256), 0, s, a, nsplit);
+    const dim3 grid(nsplit, a.Hk, a.B);
+    const int rep = a.Hq / a.Hk;
+    if (rep == 1)
+      hipLaunchKernelGGL(attn_decode_split_kernel<1>, grid, dim3(256), 0, s, a, nsplit);
+    else if (rep == 2)
+      hipLaunchKernelGGL(attn_decode_split_kernel<2>, grid, dim3(256), 0, s, a, nsplit);
+    else if (rep <= 4)
+      hipLaunchKernelGGL(attn_decode_split_kernel<4>, grid, dim3(256), 0, s, a, nsplit);
+    else
+      hipLaunchKernelGGL(attn_decode_split_kernel<8>, grid, dim3(256), 0, s, a, nsplit);
     if (a.o_f32)
       hipLaunchKernelGGL(attn_decode_merge_kernel<true>, dim3(a.Hq, a.B), dim3(kAd), 0, s, a, nsplit);
     else

@@ -315,74 +315,81 @@ __device__ __forceinline__ float dot8k(const u32x4 &w, const u32x4 &x, float acc
   return acc;
 }
 
-// Matrix-vector GEMM-K for M <= 4: a workgroup owns 16 output features and
-// streams, for each, only the K-groups that some token keeps.
+// Matrix-vector GEMM-K for M <= 4. The four waves first list the K-groups
+// some token keeps (one ballot per 64 groups); then each wave owns one output
+// feature and streams only the listed groups' segments of its weight row,
+// 16 bytes per lane with consecutive lanes on consecutive chunks, a block of
+// 8 chunks per lane issued before any is used.
 __global__ __launch_bounds__(256) void gemv_k_kernel(KArgs a) {
+  constexpr int U = 8;
   __shared__ uint16_t sGrp[kKMaxGroups];
   __shared__ uint8_t sOn[kKMaxGroups];
-  __shared__ int sNact;
+  __shared__ int sCnt[4];
   const int NG = a.K / a.G;
   const int lane = threadIdx.x % kWave;
   const int wave = threadIdx.x / kWave;
-  if (wave == 0) {
-    int base = 0;
-    for (int g0 = 0; g0 < NG; g0 += kWave) {
-      const int g = g0 + lane;
-      int on = 0;
-      if (g < NG)
-        for (int m = 0; m < a.M; ++m) on |= (a.mask[(size_t)m * NG + g] != 0) << m;
-      const uint64_t bal = __ballot(on != 0);
-      if (on) {
-        const int pos = base + rank_below(bal);
-        sGrp[pos] = (uint16_t)g;
-        sOn[pos] = (uint8_t)on;
-      }
-      base += __popcll(bal);
+  int base = 0;
+  for (int g0 = 0; g0 < NG; g0 += 4 * kWave) {
+    const int g = g0 + wave * kWave + lane;
+    int on = 0;
+    if (g < NG)
+      for (int m = 0; m < a.M; ++m) on |= (a.mask[(size_t)m * NG + g] != 0) << m;
+    const uint64_t bal = __ballot(on != 0);
+    if (lane == 0) sCnt[wave] = __popcll(bal);
+    __syncthreads();
+    int before = base;
+    for (int w = 0; w < wave; ++w) before += sCnt[w];
+    if (on) {
+      const int pos = before + rank_below(bal);
+      sGrp[pos] = (uint16_t)g;
+      sOn[pos] = (uint8_t)on;
     }
-    if (lane == 0) sNact = base;
+    base += sCnt[0] + sCnt[1] + sCnt[2] + sCnt[3];
+    __syncthreads();
   }
-  __syncthreads();
   const int cpg = a.G / 8;
-  const int nchunks = sNact * cpg;
-  const int nb = blockIdx.x * 16 + wave * 4;
-  float s[4][4];
+  const int nchunks = base * cpg;
+  const int n = blockIdx.x * 4 + wave;
+  const rsrc_t wr = make_rsrc(a.B + (size_t)n * a.ldb, (uint64_t)a.K * 2);
+  float s[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int c0 = 0; c0 < nchunks; c0 += kWave * U) {
+    u32x4 w[U];
+    int kk[U], on[U];
 #pragma unroll
-  for (int m = 0; m < 4; ++m)
+    for (int u = 0; u < U; ++u) {
+      const int c = c0 + u * kWave + lane;
+      const bool ok = c < nchunks;
+      const int gi = ok ? c / cpg : 0;
+      kk[u] = sGrp[gi] * a.G + (c % cpg) * 8;
+      on[u] = ok ? sOn[gi] : 0;
+      w[u] = buf_ld16(wr, ok ? (uint32_t)kk[u] * 2u : kOffNone);
+    }
 #pragma unroll
-    for (int r = 0; r < 4; ++r) s[m][r] = 0.f;
-  for (int c = lane; c < nchunks; c += kWave) {
-    const int gi = c / cpg;
-    const int k = sGrp[gi] * a.G + (c % cpg) * 8;
-    const int on = sOn[gi];
-    u32x4 x[4];
+    for (int m = 0; m < 4; ++m) {
+      if (m >= a.M) break;
+      const rsrc_t xr = make_rsrc(a.A + (size_t)m * a.lda, (uint64_t)a.K * 2);
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
-      if ((on >> m) & 1) x[m] = ld16(a.A + (size_t)m * a.lda + k);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const u32x4 w = ld16(a.B + (size_t)(nb + r) * a.ldb + k);
-#pragma unroll
-      for (int m = 0; m < 4; ++m)
-        if ((on >> m) & 1) s[m][r] = dot8k(w, x[m], s[m][r]);
+      for (int u = 0; u < U; ++u) {
+        const bool use = (on[u] >> m) & 1;
+        const u32x4 x = buf_ld16(xr, use ? (uint32_t)kk[u] * 2u : kOffNone);
+        s[m] = dot8k(w[u], x, s[m]);
+      }
     }
   }
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
     if (m >= a.M) break;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float v = wave_sum_k(s[m][r]);
-      if (lane == 0) {
-        float *dst = a.C + (size_t)m * a.ldc + nb + r;
-        *dst = a.beta ? *dst + v : v;
-      }
+    const float v = wave_sum_k(s[m]);
+    if (lane == 0) {
+      float *dst = a.C + (size_t)m * a.ldc + n;
+      *dst = a.beta ? *dst + v : v;
     }
   }
 }
 
 int launch_gemm_k(const KArgs &a, hipStream_t s) {
   if (a.M <= 4) {
-    hipLaunchKernelGGL(gemv_k_kernel, dim3(a.N / 16), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(gemv_k_kernel, dim3(a.N / 4), dim3(256), 0, s, a);
   } else {
     const int tiles = (a.N / kKBN) * ((a.M + kKBM - 1) / kKBM);
     hipLaunchKernelGGL(gemm_k_kernel, dim3(tiles), dim3(kKThreads), 0, s, a);

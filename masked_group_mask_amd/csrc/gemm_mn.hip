@@ -205,12 +205,17 @@ __device__ __forceinline__ float dot8(const u32x4 &w, const u32x4 &x, float acc)
 }
 
 // Matrix-vector GEMM-MN for M <= 4 reading the mask directly (no reorder).
-// A workgroup owns 16 output features of one group; each wave 4 of them.
+// One wave per output feature n (four per workgroup, all in one group). A
+// workgroup whose group is off for every token exits without reading its
+// weights. The weight row is streamed in 16-byte chunks (consecutive lanes,
+// consecutive chunks: whole cache lines), with a whole block of chunks per
+// lane issued before any is used, so each wave keeps 8 KB per row in flight.
 template <bool SWIGLU, bool OUT_F32>
 __global__ __launch_bounds__(256) void gemv_mn_kernel(MnArgs a) {
-  constexpr int kRowsPerWave = 4;
-  const int n0 = blockIdx.x * 16;
-  const int g = n0 / a.G;
+  constexpr int U = 8;                // 16-byte chunks per lane per block
+  constexpr int BLK = kWave * 8 * U;  // bf16 elements per block
+  const int n = blockIdx.x * 4 + threadIdx.x / kWave;
+  const int g = (blockIdx.x * 4) / a.G;
   const int NG = a.N / a.G;
   bool act[4];
   bool any = false;
@@ -221,42 +226,38 @@ __global__ __launch_bounds__(256) void gemv_mn_kernel(MnArgs a) {
   }
   if (!any) return;  // the whole group is off for every token: its weights are never read
   const int lane = threadIdx.x % kWave;
-  const int wave = threadIdx.x / kWave;
-  const int nb = n0 + wave * kRowsPerWave;
-  float s0[4][kRowsPerWave], s1[4][kRowsPerWave];
+  const rsrc_t w0r = make_rsrc(a.B0 + (size_t)n * a.ldb, (uint64_t)a.K * 2);
+  const rsrc_t w1r = make_rsrc((SWIGLU ? a.B1 : a.B0) + (size_t)n * a.ldb, (uint64_t)a.K * 2);
+  float s0[4] = {0.f, 0.f, 0.f, 0.f}, s1[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int k0 = 0; k0 < a.K; k0 += BLK) {
+    u32x4 w0[U], w1[U];
 #pragma unroll
-  for (int m = 0; m < 4; ++m)
+    for (int u = 0; u < U; ++u) {
+      const int k = k0 + (u * kWave + lane) * 8;
+      const uint32_t off = k < a.K ? (uint32_t)k * 2u : kOffNone;
+      w0[u] = buf_ld16(w0r, off);
+      if (SWIGLU) w1[u] = buf_ld16(w1r, off);
+    }
 #pragma unroll
-    for (int r = 0; r < kRowsPerWave; ++r) s0[m][r] = s1[m][r] = 0.f;
-
-  for (int k = lane * 8; k < a.K; k += kWave * 8) {
-    u32x4 x[4];
+    for (int m = 0; m < 4; ++m) {
+      if (!act[m]) continue;
+      const rsrc_t xr = make_rsrc(a.A + (size_t)m * a.lda, (uint64_t)a.K * 2);
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
-      if (act[m]) x[m] = ld16(a.A + (size_t)m * a.lda + k);
-#pragma unroll
-    for (int r = 0; r < kRowsPerWave; ++r) {
-      const u32x4 w0 = ld16(a.B0 + (size_t)(nb + r) * a.ldb + k);
-      u32x4 w1;
-      if (SWIGLU) w1 = ld16(a.B1 + (size_t)(nb + r) * a.ldb + k);
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        if (!act[m]) continue;
-        s0[m][r] = dot8(w0, x[m], s0[m][r]);
-        if (SWIGLU) s1[m][r] = dot8(w1, x[m], s1[m][r]);
+      for (int u = 0; u < U; ++u) {
+        const int k = k0 + (u * kWave + lane) * 8;
+        const u32x4 x = buf_ld16(xr, k < a.K ? (uint32_t)k * 2u : kOffNone);
+        s0[m] = dot8(w0[u], x, s0[m]);
+        if (SWIGLU) s1[m] = dot8(w1[u], x, s1[m]);
       }
     }
   }
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
     if (!act[m]) continue;
-#pragma unroll
-    for (int r = 0; r < kRowsPerWave; ++r) {
-      const float g0 = wave_sum(s0[m][r]);
-      float out = g0;
-      if (SWIGLU) out = silu(g0) * wave_sum(s1[m][r]);
-      if (lane == 0) store_out<OUT_F32>(a.C, (size_t)m * a.ldc + nb + r, out);
-    }
+    const float g0 = wave_sum(s0[m]);
+    float out = g0;
+    if (SWIGLU) out = silu(g0) * wave_sum(s1[m]);
+    if (lane == 0) store_out<OUT_F32>(a.C, (size_t)m * a.ldc + n, out);
   }
 }
 
@@ -269,7 +270,7 @@ static void launch_tiled(const MnArgs &a, hipStream_t s) {
 
 template <bool SWIGLU, bool F32>
 static void launch_gemv(const MnArgs &a, hipStream_t s) {
-  hipLaunchKernelGGL((gemv_mn_kernel<SWIGLU, F32>), dim3(a.N / 16), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((gemv_mn_kernel<SWIGLU, F32>), dim3(a.N / 4), dim3(256), 0, s, a);
 }
 
 int launch_gemm_mn(const MnArgs &a, hipStream_t s) {
