@@ -134,13 +134,14 @@ int wide_gemm_mn_swiglu(const wide_bf16 *A, int64_t lda, const wide_bf16 *Wg,
  *   A [M][K] bf16 (lda), B [N][K] bf16 (ldb), C [M][N] fp32 (ldc).
  *   mask [M][K/G] uint8. beta is 0 or 1. With beta = 0 every entry of C is
  *   written, exact 0 for rows with no active group.
- * Each output tile compacts the active rows of every K-group from the mask
- * itself, so no reorder output is needed. Summation order is fixed: results
- * are bitwise reproducible run to run.
+ * The mask is read directly (no reorder output is needed): the A segment of
+ * an inactive (row, group) pair is never loaded, and a tile with no active
+ * pair only scales its part of C. Summation order is fixed: results are
+ * bitwise reproducible run to run.
  * Requirements: K % G == 0; lda, ldb >= K and multiples of 8; ldc >= N and a
  * multiple of 4; 16-byte aligned A, B, C; C must not overlap A, B or mask.
- * WIDE_ERR_UNSUPPORTED unless G % 64 == 0, K / G <= 512, N % 128 == 0 and
- * lda < 2^23.
+ * WIDE_ERR_UNSUPPORTED unless G % 64 == 0, K / G <= 512, N % 128 == 0,
+ * lda < 2^22 and ldb < 2^23.
  */
 int wide_gemm_k(const wide_bf16 *A, int64_t lda, const wide_bf16 *B, int64_t ldb,
                 float *C, int64_t ldc, int beta, int64_t M, int64_t N, int64_t K,

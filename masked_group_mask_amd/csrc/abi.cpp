@@ -3,7 +3,6 @@
 // error without touching the device or the caller's buffers.
 #include <math.h>
 #include <stdint.h>
-#include <stdlib.h>
 #include <string.h>
 
 #include <atomic>
@@ -138,11 +137,11 @@ int wide_gemm_k(const wide_bf16 *A, int64_t lda, const wide_bf16 *B, int64_t ldb
       overlap(C, cb, mask, (size_t)M * (K / G)))
     return WIDE_ERR_INVALID_ARG;
   if (G % 64 != 0 || K / G > 512 || N % 128 != 0) return WIDE_ERR_UNSUPPORTED;
-  if ((uint64_t)lda * 256u > 0x7fffffffull) return WIDE_ERR_UNSUPPORTED;  // 32-bit tile offsets
+  // A tile of 256 rows and a B tile of 128 rows are addressed with 32-bit byte offsets.
+  if ((uint64_t)lda * 512u > 0x7fffffffull || (uint64_t)ldb * 256u > 0x7fffffffull)
+    return WIDE_ERR_UNSUPPORTED;
   if (!device_ok()) return WIDE_ERR_NO_DEVICE;
-  const char *r = getenv("WIDE_GEMMK_RASTER");
-  wide::KArgs a{A, lda, B, ldb, C, ldc, beta, (int)M, (int)N, (int)K, (int)G, mask,
-                r ? atoi(r) : 2};
+  wide::KArgs a{A, lda, B, ldb, C, ldc, beta, (int)M, (int)N, (int)K, (int)G, mask};
   return wide::launch_gemm_k(a, reinterpret_cast<hipStream_t>(stream));
 }
 

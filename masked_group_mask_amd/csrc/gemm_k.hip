@@ -1,302 +1,187 @@
-// GEMM-K on gfx950: the K-axis routed projection (W_o, W_down).
+// GEMM-K on gfx950: the K-axis routed projections (W_o, W_down).
 //
-// WIDE (arXiv 2607.28418) Appendix B, Eq. 21 and Algorithm 3:
+// WIDE (arXiv 2607.28418), Appendix B, Eq. 21 and Algorithm 3:
 //   C[m][n] = sum_g mask[m][g] * sum_{k in group g} A[m][k] * B[n][k].
-// The page runs one pipeline per (sorted row tile, K-group) and scatters each
-// fp32 partial into C with global atomics. On MI355X the same work is done
-// with an accumulator that never leaves the chip:
-//   - a workgroup owns C[r0:r0+128, n0:n0+128] in ORIGINAL row order and keeps
-//     it as an fp32 tile in LDS (64 KB of the 160 KB);
-//   - from the mask bytes of its 128 rows it builds, per K-group, a 128-bit
-//     row set (one ballot per 64 rows) and the list of groups with any active
-//     row; an empty (tile, group) pair is skipped outright (level 0);
-//   - for each active group it loads only the active rows of A, packed to the
-//     front of the LDS tile in row order (level 1: the slot of a row is the
-//     popcount of the active rows below it), issues MFMA fragments only up to
-//     the active count (level 2), and adds the 16x16 fp32 results into the LDS
-//     accumulator at the rows they came from. Within one group the rows are
-//     distinct and each (row, column) belongs to one lane, so the adds need no
-//     atomics; groups follow each other between barriers, so the summation
-//     order is fixed and the result is reproducible bit for bit;
-//   - the K loop runs over (active group, 64-wide K step) items with the LDS
-//     double buffer flowing across group boundaries, so short groups do not
-//     drain the pipeline;
-//   - C is written once, coalesced, as beta*C + acc.
-// For M <= 4 a matrix-vector kernel streams only the active K-groups of each
-// weight row.
-#include <type_traits>
-
+// The page gives every (sorted row tile, K-group) pair its own pipeline and
+// scatters each fp32 partial into C with atomics. Under token-level masks the
+// rows a group keeps differ from group to group, so on MI355X that scatter
+// (one fp32 read-add-write per active row and feature per group, through LDS
+// or L2 atomics) costs more than the multiply-adds it saves while the group
+// is short (G = 128 needs 2G = 256 MFMA flops per scattered value; the LDS
+// moves a value in and out more slowly than that). Here C stays in registers:
+//   - a workgroup owns C[m0:m0+256, n0:n0+128] in original row order and runs
+//     the shared 3-stage MFMA main loop over the whole K range;
+//   - the A slice of a row whose group is off for that token is never read
+//     (level 1): its load offset is set out of range, the buffer load moves
+//     no data and the stage holds zeros there, so the product adds exactly 0;
+//   - a tile none of whose rows keeps any group writes beta*C and exits
+//     (level 0);
+//   - the per-row predicates come from a bit table built once per tile from
+//     the mask bytes: bit r of word i of group g = row 32i + r keeps group g;
+//   - the summation order is fixed, so results are reproducible bit for bit.
+// For M <= 4 a matrix-vector kernel streams only the K-groups some token
+// keeps.
 #include "common.hpp"
 #include "launch.hpp"
+#include "mma_engine.hpp"
 
 namespace wide {
 
-constexpr int kKBM = 128;          // original rows per workgroup tile
-constexpr int kKBN = 128;          // output features per workgroup tile
-constexpr int kKAccLd = kKBN + 4;  // LDS accumulator row stride (fp32)
 constexpr int kKMaxGroups = 512;
-constexpr int kKThreads = 512;  // 8 waves: two per SIMD
+constexpr int kKBN = 128;  // output features per tile
+using KShape = eng::Shape<kKBN>;
 
-// LDS tiles hold rows of 64 bf16 (128 bytes, 8 chunks of 16 bytes) without
-// padding. Chunk `c` of row `s` sits at position c ^ ((s / 2) % 8): the 16
-// rows one MFMA operand read touches then cover all 64 banks once.
-__device__ __forceinline__ int tile_pos(int s, int c) { return c ^ ((s >> 1) & 7); }
-
-constexpr int kKBK = 64;                       // K depth of one pipeline item
-constexpr int kKTile = 128 * kKBK;             // bf16 elements per 128-row tile
-
-// Logical tile id -> (row tile, feature tile). raster 0: row tiles fastest
-// (consecutive tiles share weights); 1: feature tiles fastest (they share the
-// activation rows); 2: blocks of 4 row tiles x 8 feature tiles, so the 32
-// workgroups an XCD runs at once share both operands in its L2.
-__device__ __forceinline__ void tile_order(int L, int m_tiles, int n_tiles, int raster, int &mt,
-                                           int &nt) {
-  constexpr int SM = 4, SN = 8;
-  if (raster == 2 && m_tiles % SM == 0 && n_tiles % SN == 0) {
-    const int blk = L / (SM * SN), in = L % (SM * SN);
-    const int nb = n_tiles / SN;
-    mt = (blk / nb) * SM + in % SM;
-    nt = (blk % nb) * SN + in / SM;
-  } else if (raster == 1) {
-    mt = L / n_tiles;
-    nt = L % n_tiles;
+// Builds the tile's bit table: thread t reads the mask row of tile row t and
+// each wave turns one group column of its 64 rows into two words by ballot.
+// Returns whether any row of the tile keeps any group. `flag` is one word of
+// LDS that is free during the prologue.
+__device__ __forceinline__ bool build_bits(const KArgs &a, int m0, WIDE_LDS uint32_t *bits, WIDE_LDS int *flag) {
+  const int NG = a.K / a.G;
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int m = m0 + tid;
+  const uint8_t *row = a.mask + (size_t)m * NG;
+  const bool valid = m < a.M;
+  if (tid == 0) *flag = 0;
+  __syncthreads();
+  int any = 0;
+  auto put = [&](int g, bool on) {
+    const uint64_t bal = __ballot(on);
+    any |= bal != 0;
+    if (lane == 0) {
+      bits[g * 8 + wave * 2] = (uint32_t)bal;
+      bits[g * 8 + wave * 2 + 1] = (uint32_t)(bal >> 32);
+    }
+  };
+  if (NG % 4 == 0 && reinterpret_cast<uintptr_t>(a.mask) % 4 == 0) {
+    const uint32_t *row4 = reinterpret_cast<const uint32_t *>(row);
+    for (int g0 = 0; g0 < NG; g0 += 32) {
+      uint32_t w[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) w[u] = (valid && g0 + 4 * u < NG) ? row4[g0 / 4 + u] : 0u;
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (g0 + 4 * u + e < NG) put(g0 + 4 * u + e, ((w[u] >> (8 * e)) & 0xffu) != 0);
+    }
   } else {
-    mt = L % m_tiles;
-    nt = L / m_tiles;
+    for (int g0 = 0; g0 < NG; g0 += 8) {
+      uint8_t v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = (valid && g0 + u < NG) ? row[g0 + u] : 0;
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (g0 + u < NG) put(g0 + u, v[u] != 0);
+    }
   }
+  if (any && lane == 0) *flag = 1;
+  __syncthreads();
+  return *flag != 0;
 }
 
-// One workgroup = C[r0:r0+128, n0:n0+128]. The work is a sequence of items
-// (active group, 64-wide slice of its K range). Per item:
-//   - the group's active rows of A (their list is built from the mask two
-//     items ahead) and the 128 weight rows are loaded with whole 128-byte
-//     lines per row and staged in swizzled LDS tiles (double-buffered; the
-//     loads of item i+1 are in flight while item i computes);
-//   - each wave computes D^T[n][slot] = W[n][k] * A[slot][k] for its 32
-//     features and every 16-slot fragment up to the active count, on
-//     v_mfma_f32_16x16x32_bf16, so a lane ends with 4 consecutive features
-//     of one compact row;
-//   - after the group's last slice those 4 values are added into the fp32
-//     LDS accumulator at the row the slot came from (16-byte read-add-write).
-__global__ __launch_bounds__(kKThreads, 1) void gemm_k_kernel(KArgs a) {
-  constexpr int kWaves = kKThreads / kWave;
-  __shared__ __attribute__((aligned(16))) float sAcc[kKBM * kKAccLd];
-  __shared__ __attribute__((aligned(16))) uint16_t sAct[2][kKTile];
-  __shared__ __attribute__((aligned(16))) uint16_t sW[2][kKTile];
-  __shared__ uint64_t sBits[kKMaxGroups][2];
-  __shared__ uint16_t sGrp[kKMaxGroups];
-  __shared__ uint8_t sRowOf[3][kKBM];
-  __shared__ int sNact;
-  static_assert(sizeof(sAct) >= 64 * kKMaxGroups, "mask staging needs 64 rows x max groups");
+// Stage loader of the tile: A rows predicated by the bit table (the
+// predicates of the next stage are read one stage ahead), B rows dense.
+struct KLoader {
+  rsrc_t ar, br, none;
+  uint32_t aoff[KShape::AI], boff[KShape::BI];
+  const WIDE_LDS uint32_t *bits;
+  int nk, steps_per_group, NG, wave, lane;
+  uint32_t pred;  // bit i: A row of load instruction i is live at stage `next`
+  int next;
 
-  const int n_tiles = a.N / kKBN;
-  const int m_tiles = (a.M + kKBM - 1) / kKBM;
-  const int L = xcd_remap(blockIdx.x, n_tiles * m_tiles);
-  int mt, nt;
-  tile_order(L, m_tiles, n_tiles, a.raster, mt, nt);
-  const int n0 = nt * kKBN;
-  const int r0 = mt * kKBM;
-  const int NG = a.K / a.G;
-  const int tid = threadIdx.x;
-  const int lane = tid % kWave;
-  const int wave = tid / kWave;
-
-  for (int i = tid * 4; i < kKBM * kKAccLd; i += kKThreads * 4)
-    *reinterpret_cast<f32x4 *>(&sAcc[i]) = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // Row sets per group. Each half of the mask tile ([64 rows][NG] bytes, at
-  // most 32 KB) is copied to LDS (the activation buffers are free until the
-  // main loop); then every wave ballots the 64 rows of a quarter of the groups.
-  {
-    uint8_t *sMask = reinterpret_cast<uint8_t *>(&sAct[0][0]);
-    const bool vec = (NG % 16) == 0 && (reinterpret_cast<uintptr_t>(a.mask) % 16) == 0;
-    for (int half = 0; half < 2; ++half) {
-      const int rb = r0 + half * 64;
-      const int rows = max(0, min(64, a.M - rb));
-      const uint8_t *src = a.mask + (size_t)rb * NG;
-      const int nbytes = rows * NG;
-      if (vec) {
-        for (int i = tid * 16; i < nbytes; i += kKThreads * 16) st16(sMask + i, ld16(src + i));
-      } else {
-        for (int i = tid; i < nbytes; i += kKThreads) sMask[i] = src[i];
-      }
-      __syncthreads();
-      for (int g = wave; g < NG; g += kWaves) {
-        const uint64_t bal = __ballot(lane < rows && sMask[lane * NG + g] != 0);
-        if (lane == 0) sBits[g][half] = bal;
-      }
-      __syncthreads();
-    }
-  }
-  // Active groups (level 0: a (tile, group) pair with no active row is skipped).
-  if (wave == 0) {
-    int base = 0;
-    for (int g0 = 0; g0 < NG; g0 += kWave) {
-      const int g = g0 + lane;
-      const bool nz = g < NG && (sBits[g][0] | sBits[g][1]) != 0ull;
-      const uint64_t bal = __ballot(nz);
-      if (nz) sGrp[base + rank_below(bal)] = (uint16_t)g;
-      base += __popcll(bal);
-    }
-    if (lane == 0) sNact = base;
-  }
-  __syncthreads();
-
-  const int ipg = a.G / kKBK;  // items per group
-  const int nact = uniform(sNact);
-  const int nitems = nact * ipg;
-
-  // slot -> row list of active group ordinal gi, into ring slot gi % 3
-  // (waves 0 and 1 each rank 64 rows with a ballot).
-  auto build_list = [&](int gi) {
-    if (gi >= nact || wave >= 2) return;
-    const int g = sGrp[gi];
-    const uint64_t b0 = sBits[g][0], b1 = sBits[g][1];
-    const uint64_t bw = wave == 0 ? b0 : b1;
-    if ((bw >> lane) & 1ull) {
-      const int slot = (wave == 0 ? 0 : __popcll(b0)) + rank_below(bw);
-      sRowOf[gi % 3][slot] = (uint8_t)(wave * 64 + lane);
-    }
-  };
-
-  const int chunk = tid % 8;
-  const int rsub = tid / 8;  // 0..63
-  const int wm = wave / 4;   // slot fragments wm, wm + 2, ...
-  const int wn = wave % 4;   // features wn * 32 .. + 32
-  const rsrc_t arows = make_rsrc(a.A + (size_t)r0 * a.lda,
-                                 (uint64_t)min(kKBM, a.M - r0) * a.lda * 2);
-  const uint16_t *wbase = a.B + (size_t)n0 * a.ldb + chunk * 8;
-  u32x4 ra[2], rw[2];
-
-  auto issue = [&](int item) {
-    const int gi = item / ipg, ks = item % ipg;
-    const int g = sGrp[gi];
-    const int cnt = __popcll(sBits[g][0]) + __popcll(sBits[g][1]);
-    const int kcol = g * a.G + ks * kKBK + chunk * 8;
+  __device__ __forceinline__ uint32_t read_pred(int t) const {
+    const int g = min(t / steps_per_group, NG - 1);
+    const u32x4 lo = *(const WIDE_LDS u32x4 *)(bits + g * 8);
+    const u32x4 hi = *(const WIDE_LDS u32x4 *)(bits + g * 8 + 4);
+    const int sh = wave * 8 + lane / 8;  // row % 32 of every load instruction of this lane
+    uint32_t p = 0;
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      const int sl = rsub + 64 * p;
-      // level 1: only the active rows are fetched (packed by slot)
-      const uint32_t off = sl < cnt ? (uint32_t)(sRowOf[gi % 3][sl] * a.lda + kcol) * 2u : kOffNone;
-      ra[p] = buf_ld16(arows, off);
-    }
+    for (int i = 0; i < 4; ++i) p |= ((lo[i] >> sh) & 1u) << i;
 #pragma unroll
-    for (int p = 0; p < 2; ++p) rw[p] = ld16(wbase + (size_t)(rsub + 64 * p) * a.ldb + (kcol - chunk * 8));
-  };
-  auto stage = [&](int buf) {
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      const int r = rsub + 64 * p;
-      st16(&sAct[buf][r * kKBK + tile_pos(r, chunk) * 8], ra[p]);
-      st16(&sW[buf][r * kKBK + tile_pos(r, chunk) * 8], rw[p]);
-    }
-  };
-
-  f32x4 acc[2][4];  // [feature fragment][own slot fragment j: sf = wm + 2j]
-#pragma unroll
-  for (int nf = 0; nf < 2; ++nf)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[nf][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // The slot -> row list of the group of item j is built in iteration j - 2
-  // (before the barrier that precedes the loads of item j, issued in
-  // iteration j - 1); ring slot g % 3 is then free, as group g - 3 has
-  // finished. Items 0 and 1 are covered here.
-  build_list(0);
-  if (ipg == 1) build_list(1);
-  __syncthreads();
-  if (nitems > 0) {
-    issue(0);
-    stage(0);
-  }
-  __syncthreads();
-
-  for (int it = 0; it < nitems; ++it) {
-    const int cur = it & 1;
-    const int gi = it / ipg, ks = it % ipg;
-    const int g = sGrp[gi];
-    const int cnt = uniform(__popcll(sBits[g][0]) + __popcll(sBits[g][1]));
-    const int live = (cnt + 15) / 16;
-    const bool more = it + 1 < nitems;
-    const bool last = ks == ipg - 1;
-    const int ring = gi % 3;
-    if (more) issue(it + 1);  // the next item's global loads go out first
-
-    u32x4 wfr[2][2];  // [feature fragment][k step]
-#pragma unroll
-    for (int nf = 0; nf < 2; ++nf)
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int r = wn * 32 + nf * 16 + lane % 16;
-        wfr[nf][q] = ld16(&sW[cur][r * kKBK + tile_pos(r, q * 4 + lane / 16) * 8]);
-      }
-    // level 2: only ceil(cnt/16) 16-slot fragments are issued; the body is
-    // specialised on that count (rounded up to even) so all LDS reads of a K
-    // step are issued before its MFMAs, with no branch in between.
-    auto body = [&](auto nsf_c) {
-      constexpr int NJ = decltype(nsf_c)::value / 2;  // own fragments: sf = wm + 2j
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        u32x4 act[NJ];
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-          const int s = (wm + 2 * j) * 16 + lane % 16;
-          act[j] = ld16(&sAct[cur][s * kKBK + tile_pos(s, q * 4 + lane / 16) * 8]);
-        }
-#pragma unroll
-        for (int j = 0; j < NJ; ++j)
-#pragma unroll
-          for (int nf = 0; nf < 2; ++nf) acc[nf][j] = mfma16x16x32(wfr[nf][q], act[j], acc[nf][j]);
-      }
-      if (last) {
-        // Add the group's partial products into the LDS accumulator at the
-        // rows the slots came from (16-byte read-add-write per lane; within a
-        // group every (row, feature) belongs to one lane).
-        int rrow[NJ];
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-          const int s = (wm + 2 * j) * 16 + lane % 16;
-          rrow[j] = s < cnt ? (int)sRowOf[ring][s] : -1;
-        }
-        f32x4 old[NJ][2];
-#pragma unroll
-        for (int j = 0; j < NJ; ++j)
-#pragma unroll
-          for (int nf = 0; nf < 2; ++nf)
-            if (rrow[j] >= 0)
-              old[j][nf] = *reinterpret_cast<const f32x4 *>(
-                  &sAcc[rrow[j] * kKAccLd + wn * 32 + nf * 16 + (lane / 16) * 4]);
-#pragma unroll
-        for (int j = 0; j < NJ; ++j)
-#pragma unroll
-          for (int nf = 0; nf < 2; ++nf) {
-            if (rrow[j] >= 0)
-              *reinterpret_cast<f32x4 *>(&sAcc[rrow[j] * kKAccLd + wn * 32 + nf * 16 + (lane / 16) * 4]) =
-                  old[j][nf] + acc[nf][j];
-            acc[nf][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-          }
-      }
-    };
-    switch ((live + 1) / 2) {
-      case 0: break;
-      case 1: body(std::integral_constant<int, 2>{}); break;
-      case 2: body(std::integral_constant<int, 4>{}); break;
-      case 3: body(std::integral_constant<int, 6>{}); break;
-      default: body(std::integral_constant<int, 8>{}); break;
-    }
-    if ((it + 2) % ipg == 0) build_list((it + 2) / ipg);
-    if (more) stage(cur ^ 1);
-    __syncthreads();
+    for (int i = 0; i < 4; ++i) p |= ((hi[i] >> sh) & 1u) << (i + 4);
+    return p;
   }
 
-  // C = beta * C + acc, 16-byte stores.
-  for (int i = tid; i < kKBM * (kKBN / 4); i += kKThreads) {
-    const int r = i / (kKBN / 4), c = (i % (kKBN / 4)) * 4;
-    if (r0 + r >= a.M) continue;
-    f32x4 v = *reinterpret_cast<const f32x4 *>(&sAcc[r * kKAccLd + c]);
-    f32x4 *dst = reinterpret_cast<f32x4 *>(a.C + (size_t)(r0 + r) * a.ldc + n0 + c);
-    if (a.beta) v += *dst;
-    *dst = v;
+  __device__ __forceinline__ void operator()(int t, eng::lds_u16 *sa, eng::lds_u16 *sb) {
+    const bool live = t < nk;
+    const rsrc_t ra = live ? ar : none, rb = live ? br : none;
+    const uint32_t k0 = (uint32_t)t * eng::kBK * 2u;
+    const uint32_t p = pred;
+#pragma unroll
+    for (int i = 0; i < KShape::AI; ++i)
+      eng::load_lds(ra, sa + (wave + 4 * i) * 512, ((p >> i) & 1u) ? aoff[i] : kOffNone, k0);
+#pragma unroll
+    for (int i = 0; i < KShape::BI; ++i) eng::load_lds(rb, sb + (wave + 4 * i) * 512, boff[i], k0);
+    next = t + 1;
+    pred = read_pred(next);
+  }
+};
+
+__global__ __launch_bounds__(eng::kThreads) void gemm_k_kernel(KArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint16_t sA0[eng::kBM * eng::kBK];
+  __shared__ __attribute__((aligned(1024))) uint16_t sB0[kKBN * eng::kBK];
+  __shared__ __attribute__((aligned(1024))) uint16_t sA1[eng::kBM * eng::kBK];
+  __shared__ __attribute__((aligned(1024))) uint16_t sB1[kKBN * eng::kBK];
+  __shared__ __attribute__((aligned(1024))) uint16_t sA2[eng::kBM * eng::kBK];
+  __shared__ __attribute__((aligned(1024))) uint16_t sB2[kKBN * eng::kBK];
+  __shared__ __attribute__((aligned(16))) uint32_t sBits[kKMaxGroups][8];
+
+  const int MT = (a.M + eng::kBM - 1) / eng::kBM, NT = a.N / kKBN;
+  int mt, tn;
+  eng::tile_of(blockIdx.x, MT, NT, mt, tn);
+  const int m0 = mt * eng::kBM, n0 = tn * kKBN;
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int wm = wave / 2, wn = wave % 2;
+  using S = KShape;
+
+  const bool any = build_bits(a, m0, (WIDE_LDS uint32_t *)&sBits[0][0], (WIDE_LDS int *)sA2);
+  f32x4 acc[S::FN][S::FM];
+#pragma unroll
+  for (int i = 0; i < S::FN; ++i)
+#pragma unroll
+    for (int j = 0; j < S::FM; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  if (any) {  // level 0: otherwise the tile's product is exactly zero
+    KLoader ld;
+    const int rows = min(eng::kBM, a.M - m0);
+    ld.ar = make_rsrc(a.A + (size_t)m0 * a.lda, (uint64_t)rows * a.lda * 2);  // rows past M: out of range
+    ld.br = make_rsrc(a.B + (size_t)n0 * a.ldb, (uint64_t)kKBN * a.ldb * 2);
+    ld.none = make_rsrc(a.A, 0);
+#pragma unroll
+    for (int i = 0; i < S::AI; ++i) {
+      const int r = eng::load_row(wave, i, lane);
+      ld.aoff[i] = (uint32_t)r * (uint32_t)a.lda * 2u + eng::load_chunk_bytes(r, lane);
+    }
+#pragma unroll
+    for (int i = 0; i < S::BI; ++i) {
+      const int r = eng::load_row(wave, i, lane);
+      ld.boff[i] = (uint32_t)r * (uint32_t)a.ldb * 2u + eng::load_chunk_bytes(r, lane);
+    }
+    ld.bits = (const WIDE_LDS uint32_t *)&sBits[0][0];
+    ld.nk = a.K / eng::kBK;
+    ld.steps_per_group = a.G / eng::kBK;
+    ld.NG = a.K / a.G;
+    ld.wave = wave;
+    ld.lane = lane;
+    ld.next = 0;
+    ld.pred = ld.read_pred(0);
+    eng::mainloop<kKBN, false>(ld.nk, ld, (eng::lds_u16 *)sA0, (eng::lds_u16 *)sB0, (eng::lds_u16 *)sA1,
+                               (eng::lds_u16 *)sB1, (eng::lds_u16 *)sA2, (eng::lds_u16 *)sB2, acc, wm, wn, lane);
+  }
+
+  // C = beta * C + acc; a lane holds row (lane % 16) of A fragment j and
+  // features 4 (lane / 16) .. +3 of B fragment i.
+#pragma unroll
+  for (int j = 0; j < S::FM; ++j) {
+    const int m = m0 + wm * S::TM + j * 16 + lane % 16;
+    if (m >= a.M) continue;
+    float *crow = a.C + (size_t)m * a.ldc + n0 + wn * S::TN + 4 * (lane / 16);
+#pragma unroll
+    for (int i = 0; i < S::FN; ++i) {
+      f32x4 v = acc[i][j];
+      if (a.beta) v += *reinterpret_cast<const f32x4 *>(crow + i * 16);
+      *reinterpret_cast<f32x4 *>(crow + i * 16) = v;
+    }
   }
 }
 
@@ -391,8 +276,8 @@ int launch_gemm_k(const KArgs &a, hipStream_t s) {
   if (a.M <= 4) {
     hipLaunchKernelGGL(gemv_k_kernel, dim3(a.N / 4), dim3(256), 0, s, a);
   } else {
-    const int tiles = (a.N / kKBN) * ((a.M + kKBM - 1) / kKBM);
-    hipLaunchKernelGGL(gemm_k_kernel, dim3(tiles), dim3(kKThreads), 0, s, a);
+    const int tiles = ((a.M + eng::kBM - 1) / eng::kBM) * (a.N / kKBN);
+    hipLaunchKernelGGL(gemm_k_kernel, dim3(tiles), dim3(eng::kThreads), 0, s, a);
   }
   return check_launch();
 }

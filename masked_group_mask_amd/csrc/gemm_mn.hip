@@ -1,35 +1,31 @@
-// GEMM-MN on gfx950: the N-axis routed projection (W_q, W_gate, W_up).
+// GEMM-MN on gfx950: the N-axis routed projections (W_q, W_gate, W_up).
 //
-// WIDE (arXiv 2607.28418) Figure 1 and Appendix B, Algorithm 2: C = A B^T with
-// N cut into groups of G output features; token m computes group g only if its
-// mask says so. After the reorder, the rows that keep group g are the first
-// counts[g] entries of perm[g], so a workgroup owning the tile (sorted rows
-// m0..m0+BM, features n0..n0+BN) with BN | G sees one group and, except for
-// at most one boundary tile per group, only fully active rows:
-//   level 0: a tile with m0 >= counts[g] exits before touching memory;
-//   level 1: A rows past counts[g] are not loaded (zero-filled in LDS);
-//   level 2: 16-row MFMA fragments past counts[g] are not issued (the test is
-//            on a scalar, so it is a uniform branch, not a lane vote).
-// The A rows are gathered through perm straight from the original layout and
-// the outputs scattered back through it, so no activation is ever copied.
+// WIDE (arXiv 2607.28418), Figure 1 and Appendix B, Algorithm 2: C = A B^T
+// with N cut into groups of G output features; token m computes group g only
+// if its mask keeps it. After the reorder the rows that keep group g are the
+// first counts[g] entries of perm[g], so a workgroup owning the tile (sorted
+// rows s0 .. s0+256 of group g, features n0 .. n0+BN) sees only active rows
+// except in the last tile of the group:
+//   level 0: a tile with s0 >= counts[g] exits before touching memory;
+//   level 1: A rows past counts[g] are never loaded (their offsets are out of
+//            range, so the buffer loads move no data and leave zeros);
+// and every other row is a full MFMA row. The rows are gathered through perm
+// straight from the original activation layout (the gather is just the
+// per-lane load offset) and the outputs scattered back through it, so no
+// activation is ever copied. Level 2 (skipping MFMA fragments) only matters
+// in the one partial tile per group and is not taken.
 //
-// Tile: 128 sorted rows x 128 B rows (BN = 128 features, or 64 gate + 64 up
-// features for the fused SwiGLU variant), BK = 64, 4 waves in a 2 x 2 layout,
-// v_mfma_f32_16x16x32_bf16, LDS double-buffered with one barrier per K step.
-// Workgroups are remapped so that the row tiles of one feature tile run on the
-// same XCD and share its B tile in that XCD's L2.
+// The tile runs on the shared 3-stage MFMA main loop: 256 sorted rows x BN
+// weight rows (BN = 128, or 64 when G is not a multiple of 128; for the fused
+// SwiGLU variant 64 gate + the matching 64 up rows, giving 64 outputs).
 //
 // For M <= 4 with no reorder (one decode step), a matrix-vector kernel reads
 // the mask bytes directly and streams only the active groups' weight rows.
 #include "common.hpp"
 #include "launch.hpp"
+#include "mma_engine.hpp"
 
 namespace wide {
-
-constexpr int kMnBM = 128;
-constexpr int kMnBK = 64;
-constexpr int kMnLds = kMnBK + 8;  // LDS row stride in bf16 (16-byte pad)
-constexpr int kMnThreads = 256;
 
 template <bool OUT_F32>
 __device__ __forceinline__ void store_out(void *C, size_t idx, float v) {
@@ -39,152 +35,119 @@ __device__ __forceinline__ void store_out(void *C, size_t idx, float v) {
     reinterpret_cast<uint16_t *>(C)[idx] = f2bf(v);
 }
 
-template <int BNT, bool SWIGLU, bool OUT_F32>
-__global__ __launch_bounds__(kMnThreads, 2) void gemm_mn_kernel(MnArgs a) {
-  constexpr int BN_OUT = SWIGLU ? BNT / 2 : BNT;
-  constexpr int WN = BNT / 2;                 // B-tile rows per wave
-  constexpr int NF = WN / 16;                 // column fragments per wave
-  constexpr int MF = 4;                       // row fragments per wave (64 rows)
-  constexpr int A_PASSES = kMnBM * 8 / kMnThreads;
-  constexpr int B_PASSES = BNT * 8 / kMnThreads;
-  static_assert(!SWIGLU || BNT == 128, "SwiGLU tiles pair 64 gate and 64 up rows");
+// Four consecutive outputs; vector stores when the row start allows them.
+template <bool OUT_F32>
+__device__ __forceinline__ void store_out4(void *C, size_t idx, const f32x4 &v, bool vec) {
+  if (vec) {
+    if (OUT_F32)
+      *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(C) + idx) = v;
+    else
+      *reinterpret_cast<u32x2 *>(reinterpret_cast<uint16_t *>(C) + idx) =
+          u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) store_out<OUT_F32>(C, idx + e, v[e]);
+  }
+}
 
-  __shared__ __attribute__((aligned(16))) uint16_t sA[2][kMnBM * kMnLds];
-  __shared__ __attribute__((aligned(16))) uint16_t sB[2][BNT * kMnLds];
-  __shared__ int sRows[kMnBM];
+template <int BN, bool SPLIT>
+struct MnLoader {
+  using S = eng::Shape<BN>;
+  rsrc_t ar, br0, br1, none;
+  uint32_t aoff[S::AI], boff[S::BI];
+  int nk, K, wave;
+  int kchunk;  // first k (elements) of this lane's 16-byte chunk within a stage
 
-  const int n_tiles = a.N / BN_OUT;
-  const int m_tiles = (a.M + kMnBM - 1) / kMnBM;
-  const int L = xcd_remap(blockIdx.x, n_tiles * m_tiles);
-  const int n0 = (L / m_tiles) * BN_OUT;
-  const int m0 = (L % m_tiles) * kMnBM;
-  const int g = n0 / a.G;
+  __device__ __forceinline__ void operator()(int t, eng::lds_u16 *sa, eng::lds_u16 *sb) const {
+    const bool live = t < nk;
+    const uint32_t k0 = (uint32_t)t * eng::kBK * 2u;
+    // K tail: a chunk at or past K is loaded out of range (zeros)
+    const bool in = t * eng::kBK + kchunk < K;
+    const rsrc_t ra = live ? ar : none;
+#pragma unroll
+    for (int i = 0; i < S::AI; ++i) eng::load_lds(ra, sa + (wave + 4 * i) * 512, in ? aoff[i] : kOffNone, k0);
+#pragma unroll
+    for (int i = 0; i < S::BI; ++i) {
+      const rsrc_t rb = live ? ((SPLIT && i >= S::BI / 2) ? br1 : br0) : none;
+      eng::load_lds(rb, sb + (wave + 4 * i) * 512, in ? boff[i] : kOffNone, k0);
+    }
+  }
+};
+
+template <int BN, bool SWIGLU, bool OUT_F32>
+__global__ __launch_bounds__(eng::kThreads) void gemm_mn_kernel(MnArgs a) {
+  using S = eng::Shape<BN>;
+  constexpr int BN_OUT = SWIGLU ? BN / 2 : BN;
+  __shared__ __attribute__((aligned(1024))) uint16_t sA0[S::A_ELEMS];
+  __shared__ __attribute__((aligned(1024))) uint16_t sB0[S::B_ELEMS];
+  __shared__ __attribute__((aligned(1024))) uint16_t sA1[S::A_ELEMS];
+  __shared__ __attribute__((aligned(1024))) uint16_t sB1[S::B_ELEMS];
+  __shared__ __attribute__((aligned(1024))) uint16_t sA2[S::A_ELEMS];
+  __shared__ __attribute__((aligned(1024))) uint16_t sB2[S::B_ELEMS];
+  __shared__ int sRows[eng::kBM];
+
+  const int MT = (a.M + eng::kBM - 1) / eng::kBM, NT = a.N / BN_OUT;
+  int mt, tn;
+  eng::tile_of(blockIdx.x, MT, NT, mt, tn);
+  const int n0 = tn * BN_OUT, g = n0 / a.G;
   const int cnt = a.counts[g];
-  if (m0 >= cnt) return;  // level 0: this tile and every later one of group g are inactive
-  const int rows = min(kMnBM, cnt - m0);
-
-  const int tid = threadIdx.x;
-  const int lane = tid % kWave;
-  const int wave = tid / kWave;
+  const int s0 = mt * eng::kBM;
+  if (s0 >= cnt) return;  // level 0
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int wm = wave / 2, wn = wave % 2;
-
-  if (tid < kMnBM) sRows[tid] = tid < rows ? a.perm[(size_t)g * a.M + m0 + tid] : 0;
+  sRows[tid] = s0 + tid < cnt ? a.perm[(size_t)g * a.M + s0 + tid] : -1;
   __syncthreads();
 
-  const int chunk = tid % 8;
-  const int rbase = tid / 8;
-  // Gathered A rows and the B tile as buffer resources: rows past the count
-  // and the K tail get out-of-range offsets (zeros, no memory traffic), so
-  // every load is issued unconditionally.
-  const rsrc_t ra_rsrc = make_rsrc(a.A, (uint64_t)a.M * a.lda * 2);
-  uint32_t a_off[A_PASSES];
+  MnLoader<BN, SWIGLU> ld;
+  ld.ar = make_rsrc(a.A, (uint64_t)a.M * a.lda * 2);
+  const int brows = SWIGLU ? BN / 2 : BN;
+  ld.br0 = make_rsrc(a.B0 + (size_t)n0 * a.ldb, (uint64_t)brows * a.ldb * 2);
+  ld.br1 = make_rsrc((SWIGLU ? a.B1 : a.B0) + (size_t)n0 * a.ldb, (uint64_t)brows * a.ldb * 2);
+  ld.none = make_rsrc(a.A, 0);
 #pragma unroll
-  for (int p = 0; p < A_PASSES; ++p) {
-    const int r = rbase + 32 * p;
-    // level 1: rows past the count are never fetched
-    a_off[p] = r < rows ? (uint32_t)(sRows[r] * a.lda + chunk * 8) * 2u : kOffNone;
+  for (int i = 0; i < S::AI; ++i) {
+    const int r = eng::load_row(wave, i, lane);
+    const int phys = sRows[r];
+    ld.aoff[i] = phys >= 0 ? (uint32_t)phys * (uint32_t)a.lda * 2u + eng::load_chunk_bytes(r, lane) : kOffNone;
   }
-  rsrc_t rb_rsrc[2];
-  rb_rsrc[0] = make_rsrc(a.B0 + (size_t)n0 * a.ldb, (uint64_t)(SWIGLU ? BNT / 2 : BNT) * a.ldb * 2);
-  rb_rsrc[1] = SWIGLU ? make_rsrc(a.B1 + (size_t)n0 * a.ldb, (uint64_t)(BNT / 2) * a.ldb * 2) : rb_rsrc[0];
-  uint32_t b_off[B_PASSES];
 #pragma unroll
-  for (int p = 0; p < B_PASSES; ++p) {
-    const int br = rbase + 32 * p;
-    const int lr = (SWIGLU && br >= BNT / 2) ? br - BNT / 2 : br;
-    b_off[p] = (uint32_t)(lr * a.ldb + chunk * 8) * 2u;
+  for (int i = 0; i < S::BI; ++i) {
+    const int r = eng::load_row(wave, i, lane);
+    const int rb = SWIGLU ? r % (BN / 2) : r;
+    ld.boff[i] = (uint32_t)rb * (uint32_t)a.ldb * 2u + eng::load_chunk_bytes(r, lane);
   }
+  ld.nk = (a.K + eng::kBK - 1) / eng::kBK;
+  ld.K = a.K;
+  ld.wave = wave;
+  ld.kchunk = (int)(eng::load_chunk_bytes(eng::load_row(wave, 0, lane), lane) / 2);
 
-  const int nk = (a.K + kMnBK - 1) / kMnBK;
-  u32x4 ra[A_PASSES], rb[B_PASSES];
-  auto gload = [&](int kt) {
-    const bool kin = kt * kMnBK + chunk * 8 < a.K;
-    const uint32_t kb = (uint32_t)(kt * kMnBK) * 2u;
+  f32x4 acc[S::FN][S::FM];
 #pragma unroll
-    for (int p = 0; p < A_PASSES; ++p) ra[p] = buf_ld16(ra_rsrc, kin ? a_off[p] + kb : kOffNone);
+  for (int i = 0; i < S::FN; ++i)
 #pragma unroll
-    for (int p = 0; p < B_PASSES; ++p) {
-      const int which = (SWIGLU && rbase + 32 * p >= BNT / 2) ? 1 : 0;
-      rb[p] = buf_ld16(which ? rb_rsrc[1] : rb_rsrc[0], kin ? b_off[p] + kb : kOffNone);
-    }
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int p = 0; p < A_PASSES; ++p) st16(&sA[buf][(rbase + 32 * p) * kMnLds + chunk * 8], ra[p]);
-#pragma unroll
-    for (int p = 0; p < B_PASSES; ++p) st16(&sB[buf][(rbase + 32 * p) * kMnLds + chunk * 8], rb[p]);
-  };
-  auto brow = [&](int j) -> int {
-    if (SWIGLU) return (j < NF / 2) ? wn * 32 + 16 * j : 64 + wn * 32 + 16 * (j - NF / 2);
-    return wn * WN + 16 * j;
-  };
+    for (int j = 0; j < S::FM; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  eng::mainloop<BN, SWIGLU>(ld.nk, ld, (eng::lds_u16 *)sA0, (eng::lds_u16 *)sB0, (eng::lds_u16 *)sA1,
+                            (eng::lds_u16 *)sB1, (eng::lds_u16 *)sA2, (eng::lds_u16 *)sB2, acc, wm, wn, lane);
 
-  f32x4 acc[MF][NF];
+  // Scatter: a lane holds sorted row (lane % 16) of A fragment j and
+  // features 4 (lane / 16) .. +3 of B fragment i.
+  const bool vec = a.ldc % 4 == 0 && reinterpret_cast<uintptr_t>(a.C) % 16 == 0;
 #pragma unroll
-  for (int i = 0; i < MF; ++i)
+  for (int j = 0; j < S::FM; ++j) {
+    const int phys = sRows[wm * S::TM + j * 16 + lane % 16];
+    if (phys < 0) continue;
+    const size_t rowoff = (size_t)phys * a.ldc;
+    if (SWIGLU) {
 #pragma unroll
-    for (int j = 0; j < NF; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // number of live 16-row fragments of this wave (uniform)
-  const int live = uniform(min(MF, max(0, (rows - wm * 64 + 15) / 16)));
-
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) gload(kt + 1);
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const int koff = kk * 32 + (lane / 16) * 8;
-      u32x4 bf[NF];
-#pragma unroll
-      for (int j = 0; j < NF; ++j) bf[j] = ld16(&sB[cur][(brow(j) + lane % 16) * kMnLds + koff]);
-      if (live == MF) {
-        // Fully active rows (every tile of a group but the last): no
-        // predicate, all fragment reads issued together.
-        u32x4 af[MF];
-#pragma unroll
-        for (int i = 0; i < MF; ++i) af[i] = ld16(&sA[cur][(wm * 64 + 16 * i + lane % 16) * kMnLds + koff]);
-#pragma unroll
-        for (int i = 0; i < MF; ++i)
-#pragma unroll
-          for (int j = 0; j < NF; ++j) acc[i][j] = mfma16x16x32(af[i], bf[j], acc[i][j]);
-      } else {
-#pragma unroll
-        for (int i = 0; i < MF; ++i) {
-          if (i < live) {  // level 2: skip fragments past the count
-            const u32x4 af = ld16(&sA[cur][(wm * 64 + 16 * i + lane % 16) * kMnLds + koff]);
-#pragma unroll
-            for (int j = 0; j < NF; ++j) acc[i][j] = mfma16x16x32(af, bf[j], acc[i][j]);
-          }
-        }
+      for (int i = 0; i < S::FN / 2; ++i) {
+        const f32x4 gt = acc[i][j], up = acc[i + S::FN / 2][j];
+        const f32x4 h = {silu(gt[0]) * up[0], silu(gt[1]) * up[1], silu(gt[2]) * up[2], silu(gt[3]) * up[3]};
+        store_out4<OUT_F32>(a.C, rowoff + n0 + wn * (S::TN / 2) + i * 16 + 4 * (lane / 16), h, vec);
       }
-    }
-    if (kt + 1 < nk) lstore(cur ^ 1);
-    __syncthreads();
-  }
-
-  // Epilogue: scatter active rows back to their physical positions.
+    } else {
 #pragma unroll
-  for (int i = 0; i < MF; ++i) {
-    if (i >= live) continue;
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int rl = wm * 64 + 16 * i + 4 * (lane / 16) + v;
-      if (rl >= rows) continue;
-      const size_t rowoff = (size_t)sRows[rl] * a.ldc;
-      if (SWIGLU) {
-#pragma unroll
-        for (int j = 0; j < NF / 2; ++j) {
-          const float gt = acc[i][j][v], up = acc[i][j + NF / 2][v];
-          store_out<OUT_F32>(a.C, rowoff + n0 + wn * 32 + 16 * j + lane % 16, silu(gt) * up);
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < NF; ++j)
-          store_out<OUT_F32>(a.C, rowoff + n0 + wn * WN + 16 * j + lane % 16, acc[i][j][v]);
-      }
+      for (int i = 0; i < S::FN; ++i)
+        store_out4<OUT_F32>(a.C, rowoff + n0 + wn * S::TN + i * 16 + 4 * (lane / 16), acc[i][j], vec);
     }
   }
 }
@@ -261,11 +224,11 @@ __global__ __launch_bounds__(256) void gemv_mn_kernel(MnArgs a) {
   }
 }
 
-template <int BNT, bool SWIGLU, bool F32>
+template <int BN, bool SWIGLU, bool F32>
 static void launch_tiled(const MnArgs &a, hipStream_t s) {
-  constexpr int BN_OUT = SWIGLU ? BNT / 2 : BNT;
-  const int tiles = (a.N / BN_OUT) * ((a.M + kMnBM - 1) / kMnBM);
-  hipLaunchKernelGGL((gemm_mn_kernel<BNT, SWIGLU, F32>), dim3(tiles), dim3(kMnThreads), 0, s, a);
+  constexpr int BN_OUT = SWIGLU ? BN / 2 : BN;
+  const int tiles = (a.N / BN_OUT) * ((a.M + eng::kBM - 1) / eng::kBM);
+  hipLaunchKernelGGL((gemm_mn_kernel<BN, SWIGLU, F32>), dim3(tiles), dim3(eng::kThreads), 0, s, a);
 }
 
 template <bool SWIGLU, bool F32>

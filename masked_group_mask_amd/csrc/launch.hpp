@@ -53,7 +53,6 @@ struct KArgs {
   int beta;
   int M, N, K, G;
   const uint8_t *mask;
-  int raster;          // tile order of the tiled kernel (0, 1 or 2)
 };
 int launch_gemm_k(const KArgs &a, hipStream_t stream);
 
