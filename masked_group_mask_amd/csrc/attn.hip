@@ -28,14 +28,14 @@
 
 #include "common.hpp"
 #include "launch.hpp"
+#include "mma_engine.hpp"
 
 namespace wide {
 
-constexpr int kAq = 128;            // sorted query rows per workgroup
-constexpr int kAk = 64;             // keys per K/V tile
-constexpr int kAd = 128;            // head size
-constexpr int kAKLds = kAd + 8;     // sK row stride (bf16)
-constexpr int kAVLds = kAk + 8;     // sVt row stride (bf16)
+constexpr int kAq = 256;   // sorted query rows per workgroup (64 per wave)
+constexpr int kAk = 64;    // keys per K/V stage
+constexpr int kAd = 128;   // head size
+constexpr int kAStage = kAk * kAd;  // bf16 elements of one K (or V) stage
 constexpr float kLog2e = 1.4426950408889634f;
 
 template <bool OUT_F32>
@@ -48,200 +48,234 @@ __device__ __forceinline__ void store4(void *O, size_t idx, float a, float b, fl
   }
 }
 
+// Stage layouts (row = key, 256 bytes = 16 chunks of 16 bytes):
+//   K: chunk c of row r at position c ^ (r % 16): the 16 rows one K fragment
+//      read touches (same chunk) hit 16 distinct positions;
+//   V: chunk c of row r at position c ^ 2 (r % 8): a transposing read takes
+//      a 32-byte chunk pair from 8 rows per half wave, on distinct positions.
+__device__ __forceinline__ int k_swz(int r) { return r & 15; }
+__device__ __forceinline__ int v_swz(int r) { return (r & 7) << 1; }
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+// gfx950 transposing LDS read: within each 16-lane group, lane i receives
+// element i % 4 of the 8 bytes addressed by lane 4j + i / 4, for j = 0..3.
+__device__ __forceinline__ u32x2 lds_read_tr16(const WIDE_LDS uint16_t *p) {
+  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((WIDE_LDS i16x4 *)p);
+  return __builtin_bit_cast(u32x2, v);
+}
+
+// Prefill: workgroup = (query head h, sorted query tile, batch b); the tile is
+// 256 consecutive entries of perm[b][g], wave w owning entries 64w .. 64w+63.
 template <bool OUT_F32>
-__global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t sK[2][kAk * kAKLds];
-  __shared__ __attribute__((aligned(16))) uint16_t sVt[2][kAd * kAVLds];
+__global__ __launch_bounds__(256) void attn_prefill_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint16_t sK0[kAStage];
+  __shared__ __attribute__((aligned(1024))) uint16_t sV0[kAStage];
+  __shared__ __attribute__((aligned(1024))) uint16_t sK1[kAStage];
+  __shared__ __attribute__((aligned(1024))) uint16_t sV1[kAStage];
+  __shared__ __attribute__((aligned(1024))) uint16_t sK2[kAStage];
+  __shared__ __attribute__((aligned(1024))) uint16_t sV2[kAStage];
   __shared__ int sPos[kAq];
 
+  // Heads of one KV group run on one XCD (they stream the same K/V); the
+  // heaviest causal tiles (latest positions) start first.
+  const int x = blockIdx.x;
+  const int h = a.Hq % 8 == 0 ? (x % 8) * (a.Hq / 8) + x / 8 : x;
   const int ntile = (a.Tq + kAq - 1) / kAq;
-  const int tile = ntile - 1 - (int)blockIdx.x;  // later tiles see more keys: start them first
-  const int h = blockIdx.y;
+  const int tile = ntile - 1 - (int)blockIdx.y;
   const int b = blockIdx.z;
   const int rep = a.Hq / a.Hk;
   const int g = h / rep;
   const int cnt = a.counts[(size_t)b * a.Hk + g];
-  const int m0 = tile * kAq;
-  if (m0 >= cnt) return;  // level 0
-  const int rows = min(kAq, cnt - m0);
-  const int tid = threadIdx.x;
-  const int lane = tid % kWave;
-  const int wave = tid / kWave;
-
-  const int32_t *pg = a.perm + ((size_t)b * a.Hk + g) * a.Tq;
-  if (tid < kAq) sPos[tid] = tid < rows ? pg[m0 + tid] : -1;
+  const int s0 = tile * kAq;
+  if (s0 >= cnt) return;  // level 0
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int c = lane % 16, q = lane / 16;
+  sPos[tid] = s0 + tid < cnt ? a.perm[((size_t)b * a.Hk + g) * a.Tq + s0 + tid] : -1;
   __syncthreads();
 
   const int delta = a.Tk - a.Tq;
   const int jmin = a.leftpad ? a.leftpad[b] : 0;
-  const int jmax = a.causal ? min(a.Tk, sPos[rows - 1] + delta + 1) : a.Tk;
-  const int t_begin = jmin / kAk;
-  const int t_end = jmax > jmin ? (jmax + kAk - 1) / kAk : t_begin;
+  const int nvalid = min(kAq, cnt - s0);
+  const int wg_maxpos = sPos[nvalid - 1];
+  const int wlo = wave * 64, wvalid = max(0, min(64, nvalid - wlo));
+  const int w_maxpos = wvalid > 0 ? sPos[wlo + wvalid - 1] : -1;
+  // first row of the wave (or -1 when the wave has an empty row: forces masks)
+  const int w_minpos = wvalid == 64 ? sPos[wlo] : -1;
 
-  // This wave's 32 query rows.
-  const int wrows = uniform(max(0, min(32, rows - wave * 32)));
-  const int wjmax = wrows > 0 ? (a.causal ? min(a.Tk, sPos[wave * 32 + wrows - 1] + delta + 1) : a.Tk) : 0;
-  int qpos[2];
-#pragma unroll
-  for (int qf = 0; qf < 2; ++qf) qpos[qf] = sPos[wave * 32 + qf * 16 + lane % 16];
+  // Key tiles [t0, t1).
+  const int t0 = jmin / kAk;
+  const int kend = a.causal ? min(a.Tk, wg_maxpos + delta + 1) : a.Tk;
+  const int t1 = (kend + kAk - 1) / kAk;
+  const int nk = max(0, t1 - t0);
 
-  const size_t q_row = (size_t)a.Hq * kAd;       // elements between tokens of Q/O
-  const size_t kv_row = (size_t)a.Hk * kAd;      // elements between tokens of K/V
-  // Q, K and V of this batch as buffer resources: inactive query rows and keys
-  // past Tk get out-of-range offsets (zeros, no traffic), so every load is
-  // issued unconditionally.
-  const rsrc_t q_rsrc = make_rsrc(a.Q + (size_t)b * a.Tq * q_row, (uint64_t)a.Tq * q_row * 2);
-  const rsrc_t k_rsrc = make_rsrc(a.K + (size_t)b * a.Tk * kv_row, (uint64_t)a.Tk * kv_row * 2);
-  const rsrc_t v_rsrc = make_rsrc(a.V + (size_t)b * a.Tk * kv_row, (uint64_t)a.Tk * kv_row * 2);
-  u32x4 qreg[2][4];
+  // Q fragments (B operand of S^T = K Q^T): query 16 qb + c of the wave,
+  // head dims 32 ds + 8 q .. +7.
+  const size_t q_row = (size_t)a.Hq * kAd, kv_row = (size_t)a.Hk * kAd;
+  const rsrc_t qr = make_rsrc(a.Q + (size_t)b * a.Tq * q_row, (uint64_t)a.Tq * q_row * 2);
+  u32x4 qf[4][4];
+  int qpos[4];
 #pragma unroll
-  for (int qf = 0; qf < 2; ++qf)
+  for (int qb = 0; qb < 4; ++qb) {
+    qpos[qb] = sPos[wlo + qb * 16 + c];
+#pragma unroll
+    for (int ds = 0; ds < 4; ++ds) {
+      const uint32_t off = qpos[qb] >= 0 ? (uint32_t)(((size_t)qpos[qb] * q_row + (size_t)h * kAd + ds * 32 + 8 * q) * 2)
+                                         : kOffNone;
+      qf[qb][ds] = buf_ld16(qr, off);
+    }
+  }
+  int jend[4];
+#pragma unroll
+  for (int qb = 0; qb < 4; ++qb) jend[qb] = a.causal ? qpos[qb] + delta + 1 : a.Tk;
+
+  // K/V stage loads: 16 instructions of 1 KB (4 rows) per operand per stage,
+  // wave w issuing j = w + 4i; lane l takes row 4j + l/16, position l % 16.
+  const rsrc_t kr = make_rsrc(a.K + (size_t)b * a.Tk * kv_row, (uint64_t)a.Tk * kv_row * 2);
+  const rsrc_t vr = make_rsrc(a.V + (size_t)b * a.Tk * kv_row, (uint64_t)a.Tk * kv_row * 2);
+  auto issue = [&](int t, WIDE_LDS uint16_t *sk, WIDE_LDS uint16_t *sv) {
+    const int k0 = (t0 + t) * kAk;
+    const bool live = t < nk;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int j = wave + 4 * i;
+      const int r = 4 * j + lane / 16, p = lane % 16;
+      const bool ok = live && k0 + r < a.Tk;
+      const uint32_t base = (uint32_t)(((size_t)(k0 + r) * kv_row + (size_t)g * kAd) * 2);
+      eng::load_lds(kr, (eng::lds_u16 *)(sk + j * 512), ok ? base + (uint32_t)((p ^ k_swz(r)) * 16) : kOffNone, 0u);
+      eng::load_lds(vr, (eng::lds_u16 *)(sv + j * 512), ok ? base + (uint32_t)((p ^ v_swz(r)) * 16) : kOffNone, 0u);
+    }
+  };
+
+  f32x4 o[8][4];
+#pragma unroll
+  for (int db = 0; db < 8; ++db)
+#pragma unroll
+    for (int qb = 0; qb < 4; ++qb) o[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+  float l[4] = {0.f, 0.f, 0.f, 0.f};
+  const float sl2 = a.scale * kLog2e;
+
+  auto compute = [&](int t, const WIDE_LDS uint16_t *sk, const WIDE_LDS uint16_t *sv) {
+    const int k0 = (t0 + t) * kAk;
+    if (k0 > w_maxpos + delta && a.causal) return;  // level 2: every row of the wave precedes the tile
+    if (w_maxpos < 0) return;                        // the wave has no active row
+    f32x4 sc[4][4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int qb = 0; qb < 4; ++qb) sc[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ds = 0; ds < 4; ++ds)
-      qreg[qf][ds] = buf_ld16(q_rsrc, qpos[qf] >= 0
-          ? (uint32_t)(qpos[qf] * q_row + h * kAd + ds * 32 + (lane / 16) * 8) * 2u : kOffNone);
-
-  // K/V tile loaders: K rows (tid/16 + 16p), V key pairs (2*(tid/16) + 32p, +1).
-  const int kc = tid % 16;
-  const int kr = tid / 16;
-  const uint32_t kv_col = (uint32_t)(g * kAd + kc * 8) * 2u;
-  u32x4 rk[4], rv[4];
-  auto gload = [&](int t) {
-    const int j0 = t * kAk;
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const int j = j0 + kr + 16 * p;
-      rk[p] = buf_ld16(k_rsrc, j < a.Tk ? (uint32_t)j * (uint32_t)kv_row * 2u + kv_col : kOffNone);
-    }
+      for (int kb = 0; kb < 4; ++kb) {
+        const int r = kb * 16 + c;
+        const u32x4 kf = *(const WIDE_LDS u32x4 *)(sk + r * kAd + (((ds * 4 + q) ^ k_swz(r)) * 8));
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const int j = j0 + 32 * (p / 2) + 2 * kr + (p % 2);
-      rv[p] = buf_ld16(v_rsrc, j < a.Tk ? (uint32_t)j * (uint32_t)kv_row * 2u + kv_col : kOffNone);
-    }
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int p = 0; p < 4; ++p) st16(&sK[buf][(kr + 16 * p) * kAKLds + kc * 8], rk[p]);
-#pragma unroll
-    for (int pp = 0; pp < 2; ++pp) {
-      const u32x4 e0 = rv[2 * pp], e1 = rv[2 * pp + 1];
-      uint32_t *dst = reinterpret_cast<uint32_t *>(&sVt[buf][(kc * 8) * kAVLds + 32 * pp + 2 * kr]);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t lo = (e % 2) ? (e0[e / 2] >> 16) : (e0[e / 2] & 0xffffu);
-        const uint32_t hi = (e % 2) ? (e1[e / 2] & 0xffff0000u) : (e1[e / 2] << 16);
-        dst[e * (kAVLds / 2)] = lo | hi;
+        for (int qb = 0; qb < 4; ++qb) sc[kb][qb] = mfma16x16x32(kf, qf[qb][ds], sc[kb][qb]);
       }
-    }
-  };
-
-  const float sl2 = a.scale * kLog2e;
-  float mrun[2] = {-INFINITY, -INFINITY};
-  float zpart[2] = {0.f, 0.f};
-  f32x4 oacc[8][2];
+    // Element-wise masks only where some row of the wave may see a key
+    // outside [jmin, jend): tiles that cross a causal diagonal, the left
+    // padding or the end of the keys.
+    const bool need_mask = k0 < jmin || k0 + kAk > a.Tk || (a.causal && k0 + kAk - 1 > w_minpos + delta);
+    u32x4 pf[2][4];
 #pragma unroll
-  for (int df = 0; df < 8; ++df)
+    for (int qb = 0; qb < 4; ++qb) {
+      float mx = -INFINITY;
 #pragma unroll
-    for (int qf = 0; qf < 2; ++qf) oacc[df][qf] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  if (t_begin < t_end) {
-    gload(t_begin);
-    lstore(0);
-  }
-  __syncthreads();
-  for (int t = t_begin; t < t_end; ++t) {
-    const int cur = (t - t_begin) & 1;
-    if (t + 1 < t_end) gload(t + 1);
-    const int j0 = t * kAk;
-    if (j0 < wjmax) {  // level 2: the wave's rows see some key of this tile
-      f32x4 s[4][2];
+      for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-      for (int kf = 0; kf < 4; ++kf)
-#pragma unroll
-        for (int qf = 0; qf < 2; ++qf) s[kf][qf] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ds = 0; ds < 4; ++ds) {
-#pragma unroll
-        for (int kf = 0; kf < 4; ++kf) {
-          const u32x4 kfrag = ld16(&sK[cur][(kf * 16 + lane % 16) * kAKLds + ds * 32 + (lane / 16) * 8]);
-#pragma unroll
-          for (int qf = 0; qf < 2; ++qf) s[kf][qf] = mfma16x16x32(kfrag, qreg[qf][ds], s[kf][qf]);
+        for (int v = 0; v < 4; ++v) {
+          float s = sc[kb][qb][v] * sl2;
+          if (need_mask) {
+            const int key = k0 + kb * 16 + 4 * q + v;
+            if (key < jmin || key >= jend[qb]) s = -INFINITY;
+          }
+          sc[kb][qb][v] = s;
+          mx = fmaxf(mx, s);
         }
-      }
-      // Mask, scale, online softmax (log2 domain).
+      mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+      const float mnew = fmaxf(m[qb], mx);
+      const float muse = mnew == -INFINITY ? 0.f : mnew;
+      const float alpha = exp2f(m[qb] - muse);
+      m[qb] = mnew;
+      float ls = 0.f;
 #pragma unroll
-      for (int qf = 0; qf < 2; ++qf) {
-        const int lim = a.causal ? qpos[qf] + delta : a.Tk - 1;
-        float rmax = -INFINITY;
+      for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int kf = 0; kf < 4; ++kf)
+        for (int v = 0; v < 4; ++v) {
+          const float p = exp2f(sc[kb][qb][v] - muse);
+          sc[kb][qb][v] = p;
+          ls += p;
+        }
+      l[qb] = l[qb] * alpha + ls;
 #pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const int j = j0 + kf * 16 + 4 * (lane / 16) + v;
-            const bool ok = qpos[qf] >= 0 && j >= jmin && j <= lim && j < a.Tk;
-            const float x = ok ? s[kf][qf][v] * sl2 : -INFINITY;
-            s[kf][qf][v] = x;
-            rmax = fmaxf(rmax, x);
-          }
-        rmax = fmaxf(rmax, __shfl_xor(rmax, 16, kWave));
-        rmax = fmaxf(rmax, __shfl_xor(rmax, 32, kWave));
-        const float mnew = fmaxf(mrun[qf], rmax);
-        const float muse = mnew == -INFINITY ? 0.f : mnew;
-        const float alpha = exp2f(mrun[qf] - muse);
-        mrun[qf] = mnew;
-        float psum = 0.f;
+      for (int db = 0; db < 8; ++db) o[db][qb] *= alpha;
 #pragma unroll
-        for (int kf = 0; kf < 4; ++kf)
+      for (int ks = 0; ks < 2; ++ks)
+        pf[ks][qb] = u32x4{pack_bf16x2(sc[2 * ks][qb][0], sc[2 * ks][qb][1]),
+                           pack_bf16x2(sc[2 * ks][qb][2], sc[2 * ks][qb][3]),
+                           pack_bf16x2(sc[2 * ks + 1][qb][0], sc[2 * ks + 1][qb][1]),
+                           pack_bf16x2(sc[2 * ks + 1][qb][2], sc[2 * ks + 1][qb][3])};
+    }
+    // O^T += V^T P^T. V^T fragment (16 head dims x 32 keys) from two
+    // transposing reads: keys 32 ks + 4 q + j, then 32 ks + 16 + 4 q + j,
+    // matching the key order of the P^T registers.
+    const int sidx = lane % 16;
 #pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const float p = exp2f(s[kf][qf][v] - muse);
-            s[kf][qf][v] = p;
-            psum += p;
-          }
-        zpart[qf] = zpart[qf] * alpha + psum;
-#pragma unroll
-        for (int df = 0; df < 8; ++df) oacc[df][qf] *= alpha;
-      }
-      // O^T += V^T P^T over two 32-key steps.
+    for (int db = 0; db < 8; ++db)
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        u32x4 pb[2];
+        const int chunk = 2 * db + (sidx % 4) / 2;
+        const int r0 = ks * 32 + 4 * q + sidx / 4, r1 = r0 + 16;
+        const u32x2 lo = lds_read_tr16(sv + r0 * kAd + ((chunk ^ v_swz(r0)) * 8) + 4 * (sidx % 2));
+        const u32x2 hi = lds_read_tr16(sv + r1 * kAd + ((chunk ^ v_swz(r1)) * 8) + 4 * (sidx % 2));
+        const u32x4 vf = {lo[0], lo[1], hi[0], hi[1]};
 #pragma unroll
-        for (int qf = 0; qf < 2; ++qf) {
-          const f32x4 lo = s[2 * ks][qf], hi = s[2 * ks + 1][qf];
-          pb[qf] = u32x4{pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3]),
-                         pack_bf16x2(hi[0], hi[1]), pack_bf16x2(hi[2], hi[3])};
-        }
-#pragma unroll
-        for (int df = 0; df < 8; ++df) {
-          const uint16_t *vrow = &sVt[cur][(df * 16 + lane % 16) * kAVLds + ks * 32 + 4 * (lane / 16)];
-          const u32x2 lo = *reinterpret_cast<const u32x2 *>(vrow);
-          const u32x2 hi = *reinterpret_cast<const u32x2 *>(vrow + 16);
-          const u32x4 vfrag = {lo[0], lo[1], hi[0], hi[1]};
-#pragma unroll
-          for (int qf = 0; qf < 2; ++qf) oacc[df][qf] = mfma16x16x32(vfrag, pb[qf], oacc[df][qf]);
-        }
+        for (int qb = 0; qb < 4; ++qb) o[db][qb] = mfma16x16x32(vf, pf[ks][qb], o[db][qb]);
       }
-    }
-    if (t + 1 < t_end) lstore(cur ^ 1);
-    __syncthreads();
-  }
+  };
 
-  // Normalise and scatter the active rows to O[b][t][h][:].
-  uint16_t *Ob16 = nullptr;
-  (void)Ob16;
+  WIDE_LDS uint16_t *k0s = (WIDE_LDS uint16_t *)sK0, *v0s = (WIDE_LDS uint16_t *)sV0;
+  WIDE_LDS uint16_t *k1s = (WIDE_LDS uint16_t *)sK1, *v1s = (WIDE_LDS uint16_t *)sV1;
+  WIDE_LDS uint16_t *k2s = (WIDE_LDS uint16_t *)sK2, *v2s = (WIDE_LDS uint16_t *)sV2;
+  constexpr int NL = 8;  // stage loads per wave
+  issue(0, k0s, v0s);
+  issue(1, k1s, v1s);
+  int t = 0;
+#define WIDE_ATTN_STEP(CK, CV, NK, NV) \
+  {                                    \
+    WIDE_WAIT_VM_LGKM0(NL);            \
+    WIDE_BARRIER();                    \
+    issue(t + 2, NK, NV);              \
+    compute(t, CK, CV);                \
+    ++t;                               \
+  }
+  for (; t + 3 <= nk;) {
+    WIDE_ATTN_STEP(k0s, v0s, k2s, v2s)
+    WIDE_ATTN_STEP(k1s, v1s, k0s, v0s)
+    WIDE_ATTN_STEP(k2s, v2s, k1s, v1s)
+  }
+  if (t < nk) WIDE_ATTN_STEP(k0s, v0s, k2s, v2s)
+  if (t < nk) WIDE_ATTN_STEP(k1s, v1s, k0s, v0s)
+#undef WIDE_ATTN_STEP
+  WIDE_WAIT_VM_LGKM0(0);
+
+  // Normalise and scatter: lane holds head dims 16 db + 4 q .. +3 of query
+  // 16 qb + c of the wave.
 #pragma unroll
-  for (int qf = 0; qf < 2; ++qf) {
-    float z = zpart[qf];
+  for (int qb = 0; qb < 4; ++qb) {
+    float z = l[qb];
     z += __shfl_xor(z, 16, kWave);
     z += __shfl_xor(z, 32, kWave);
-    if (qpos[qf] < 0) continue;
+    if (qpos[qb] < 0) continue;
     const float inv = z > 0.f ? 1.f / z : 0.f;
-    const size_t obase = ((size_t)b * a.Tq + qpos[qf]) * q_row + (size_t)h * kAd;
+    const size_t obase = ((size_t)b * a.Tq + qpos[qb]) * q_row + (size_t)h * kAd + 4 * q;
 #pragma unroll
-    for (int df = 0; df < 8; ++df) {
-      const f32x4 o = oacc[df][qf] * inv;
-      store4<OUT_F32>(a.O, obase + df * 16 + 4 * (lane / 16), o[0], o[1], o[2], o[3]);
+    for (int db = 0; db < 8; ++db) {
+      const f32x4 v = o[db][qb] * inv;
+      store4<OUT_F32>(a.O, obase + db * 16, v[0], v[1], v[2], v[3]);
     }
   }
 }
@@ -498,7 +532,7 @@ int launch_attn(const AttnArgs &a, hipStream_t s) {
       hipLaunchKernelGGL(attn_decode_merge_kernel<false>, dim3(a.Hq, a.B), dim3(kAd), 0, s, a, nsplit);
     return check_launch();
   }
-  dim3 grid((a.Tq + kAq - 1) / kAq, a.Hq, a.B);
+  dim3 grid(a.Hq, (a.Tq + kAq - 1) / kAq, a.B);
   if (a.o_f32)
     hipLaunchKernelGGL(attn_prefill_kernel<true>, grid, dim3(256), 0, s, a);
   else
