@@ -176,48 +176,59 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(AttnArgs a) {
       }
     // Element-wise masks only where some row of the wave may see a key
     // outside [jmin, jend): tiles that cross a causal diagonal, the left
-    // padding or the end of the keys.
+    // padding or the end of the keys (a uniform branch; the masked path uses
+    // selects only).
     const bool need_mask = k0 < jmin || k0 + kAk > a.Tk || (a.causal && k0 + kAk - 1 > w_minpos + delta);
+    if (need_mask) {
+#pragma unroll
+      for (int qb = 0; qb < 4; ++qb)
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int key = k0 + kb * 16 + 4 * q + v;
+            const bool ok = key >= jmin && key < jend[qb];
+            sc[kb][qb][v] = ok ? sc[kb][qb][v] : -INFINITY;
+          }
+    }
+    // Online softmax in the log2 domain: m is the running max of scale*log2e*s.
+    float alpha[4];
     u32x4 pf[2][4];
 #pragma unroll
     for (int qb = 0; qb < 4; ++qb) {
       float mx = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          float s = sc[kb][qb][v] * sl2;
-          if (need_mask) {
-            const int key = k0 + kb * 16 + 4 * q + v;
-            if (key < jmin || key >= jend[qb]) s = -INFINITY;
-          }
-          sc[kb][qb][v] = s;
-          mx = fmaxf(mx, s);
-        }
+        mx = fmaxf(mx, fmaxf(fmaxf(sc[kb][qb][0], sc[kb][qb][1]), fmaxf(sc[kb][qb][2], sc[kb][qb][3])));
       mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
       mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-      const float mnew = fmaxf(m[qb], mx);
+      const float mnew = fmaxf(m[qb], mx * sl2);
       const float muse = mnew == -INFINITY ? 0.f : mnew;
-      const float alpha = exp2f(m[qb] - muse);
+      alpha[qb] = exp2_fast(m[qb] - muse);
       m[qb] = mnew;
       float ls = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const float p = exp2f(sc[kb][qb][v] - muse);
+          const float p = exp2_fast(fmaf(sc[kb][qb][v], sl2, -muse));
           sc[kb][qb][v] = p;
           ls += p;
         }
-      l[qb] = l[qb] * alpha + ls;
-#pragma unroll
-      for (int db = 0; db < 8; ++db) o[db][qb] *= alpha;
+      l[qb] = l[qb] * alpha[qb] + ls;
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
         pf[ks][qb] = u32x4{pack_bf16x2(sc[2 * ks][qb][0], sc[2 * ks][qb][1]),
                            pack_bf16x2(sc[2 * ks][qb][2], sc[2 * ks][qb][3]),
                            pack_bf16x2(sc[2 * ks + 1][qb][0], sc[2 * ks + 1][qb][1]),
                            pack_bf16x2(sc[2 * ks + 1][qb][2], sc[2 * ks + 1][qb][3])};
+    }
+    // Rescale the output only when some row's max moved (a wave-wide vote).
+    if (__ballot(alpha[0] != 1.f || alpha[1] != 1.f || alpha[2] != 1.f || alpha[3] != 1.f)) {
+#pragma unroll
+      for (int qb = 0; qb < 4; ++qb)
+#pragma unroll
+        for (int db = 0; db < 8; ++db) o[db][qb] *= alpha[qb];
     }
     // O^T += V^T P^T. V^T fragment (16 head dims x 32 keys) from two
     // transposing reads: keys 32 ks + 4 q + j, then 32 ks + 16 + 4 q + j,
