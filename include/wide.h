@@ -99,8 +99,8 @@ int wide_reorder(const uint8_t *mask, int64_t batch, int64_t rows, int64_t group
  * zero-initialised C).
  * Requirements: K % 8 == 0; lda, ldb >= K and multiples of 8; ldc >= N;
  * A, B, C 16-byte aligned; C must not overlap A or B. WIDE_ERR_UNSUPPORTED
- * unless G % 64 == 0 and M * lda * 2 < 2^31 (rows are gathered with 32-bit
- * byte offsets).
+ * unless G % 64 == 0, M * lda * 2 < 2^31 (rows are gathered with 32-bit byte
+ * offsets) and ldb < 2^22.
  */
 int wide_gemm_mn(const wide_bf16 *A, int64_t lda, const wide_bf16 *B, int64_t ldb,
                  void *C, int64_t ldc, int c_dtype, int64_t M, int64_t N, int64_t K,
@@ -141,7 +141,7 @@ int wide_gemm_mn_swiglu(const wide_bf16 *A, int64_t lda, const wide_bf16 *Wg,
  * Requirements: K % G == 0; lda, ldb >= K and multiples of 8; ldc >= N and a
  * multiple of 4; 16-byte aligned A, B, C; C must not overlap A, B or mask.
  * WIDE_ERR_UNSUPPORTED unless G % 64 == 0, K / G <= 512, N % 128 == 0,
- * lda < 2^22 and ldb < 2^23.
+ * lda < 2^22 and ldb < 2^22.
  */
 int wide_gemm_k(const wide_bf16 *A, int64_t lda, const wide_bf16 *B, int64_t ldb,
                 float *C, int64_t ldc, int beta, int64_t M, int64_t N, int64_t K,

@@ -9,8 +9,9 @@
 // or L2 atomics) costs more than the multiply-adds it saves while the group
 // is short (G = 128 needs 2G = 256 MFMA flops per scattered value; the LDS
 // moves a value in and out more slowly than that). Here C stays in registers:
-//   - a workgroup owns C[m0:m0+256, n0:n0+128] in original row order and runs
-//     the shared 3-stage MFMA main loop over the whole K range;
+//   - a workgroup owns C[m0:m0+256, n0:n0+256] (or n0+128 when N is not a
+//     multiple of 256) in original row order and runs the shared MFMA main
+//     loop over the whole K range;
 //   - the A slice of a row whose group is off for that token is never read
 //     (level 1): its load offset is set out of range, the buffer load moves
 //     no data and the stage holds zeros there, so the product adds exactly 0;
@@ -28,17 +29,20 @@
 namespace wide {
 
 constexpr int kKMaxGroups = 512;
-constexpr int kKBN = 128;  // output features per tile
-using KShape = eng::Shape<kKBN>;
 
-// Builds the tile's bit table: thread t reads the mask row of tile row t and
-// each wave turns one group column of its 64 rows into two words by ballot.
-// Returns whether any row of the tile keeps any group. `flag` is one word of
-// LDS that is free during the prologue.
+// Builds the tile's bit table: bit r of word i of group g says whether tile
+// row 32 i + r keeps group g. Thread t reads the mask row of tile row t % 256
+// (for the groups g = t / 256 mod THREADS / 256) and each wave turns one
+// group column of its 64 rows into two words by ballot. Returns whether any
+// row of the tile keeps any group. `flag` is one word of LDS that is free
+// during the prologue.
+template <int THREADS>
 __device__ __forceinline__ bool build_bits(const KArgs &a, int m0, WIDE_LDS uint32_t *bits, WIDE_LDS int *flag) {
+  constexpr int PARTS = THREADS / 256;
   const int NG = a.K / a.G;
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-  const int m = m0 + tid;
+  const int part = tid / 256, wrow = wave % 4;
+  const int m = m0 + tid % 256;
   const uint8_t *row = a.mask + (size_t)m * NG;
   const bool valid = m < a.M;
   if (tid == 0) *flag = 0;
@@ -48,30 +52,40 @@ __device__ __forceinline__ bool build_bits(const KArgs &a, int m0, WIDE_LDS uint
     const uint64_t bal = __ballot(on);
     any |= bal != 0;
     if (lane == 0) {
-      bits[g * 8 + wave * 2] = (uint32_t)bal;
-      bits[g * 8 + wave * 2 + 1] = (uint32_t)(bal >> 32);
+      bits[g * 8 + wrow * 2] = (uint32_t)bal;
+      bits[g * 8 + wrow * 2 + 1] = (uint32_t)(bal >> 32);
     }
   };
   if (NG % 4 == 0 && reinterpret_cast<uintptr_t>(a.mask) % 4 == 0) {
+    // 4 groups per 32-bit load; part p takes the words w with w % PARTS == p
     const uint32_t *row4 = reinterpret_cast<const uint32_t *>(row);
-    for (int g0 = 0; g0 < NG; g0 += 32) {
+    const int nw = NG / 4;
+    for (int w0 = part; w0 < nw; w0 += 8 * PARTS) {
       uint32_t w[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) w[u] = (valid && g0 + 4 * u < NG) ? row4[g0 / 4 + u] : 0u;
+      for (int u = 0; u < 8; ++u) {
+        const int wi = w0 + u * PARTS;
+        w[u] = (valid && wi < nw) ? row4[wi] : 0u;
+      }
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
+      for (int u = 0; u < 8; ++u) {
+        const int wi = w0 + u * PARTS;
+        if (wi < nw)
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (g0 + 4 * u + e < NG) put(g0 + 4 * u + e, ((w[u] >> (8 * e)) & 0xffu) != 0);
+          for (int e = 0; e < 4; ++e) put(4 * wi + e, ((w[u] >> (8 * e)) & 0xffu) != 0);
+      }
     }
   } else {
-    for (int g0 = 0; g0 < NG; g0 += 8) {
+    for (int g0 = part; g0 < NG; g0 += 8 * PARTS) {
       uint8_t v[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = (valid && g0 + u < NG) ? row[g0 + u] : 0;
+      for (int u = 0; u < 8; ++u) {
+        const int g = g0 + u * PARTS;
+        v[u] = (valid && g < NG) ? row[g] : 0;
+      }
 #pragma unroll
       for (int u = 0; u < 8; ++u)
-        if (g0 + u < NG) put(g0 + u, v[u] != 0);
+        if (g0 + u * PARTS < NG) put(g0 + u * PARTS, v[u] != 0);
     }
   }
   if (any && lane == 0) *flag = 1;
@@ -79,82 +93,92 @@ __device__ __forceinline__ bool build_bits(const KArgs &a, int m0, WIDE_LDS uint
   return *flag != 0;
 }
 
-// Stage loader of the tile: A rows predicated by the bit table (the
-// predicates of the next stage are read one stage ahead), B rows dense.
+// Stage loader of the tile: A rows predicated by the bit table, B rows
+// dense. The bit words of a stage's group are read from LDS a step before the
+// stage is issued, among the fragment reads, and unpacked only when it is, so
+// the LDS latency never sits in front of the loads.
+template <class S>
 struct KLoader {
+  static constexpr int kDsReads = 2;
+  static constexpr int AHEAD = S::STAGES - 1;  // stages in flight ahead of the one multiplied
   rsrc_t ar, br, none;
-  uint32_t aoff[KShape::AI], boff[KShape::BI];
+  uint32_t aoff[S::AI], boff[S::BI];
   const WIDE_LDS uint32_t *bits;
   int nk, steps_per_group, NG, wave, lane;
-  uint32_t pred;  // bit i: A row of load instruction i is live at stage `next`
-  int next;
+  u32x4 wlo, whi;  // bit words (rows 0..127, 128..255) of the group of the next stage
 
-  __device__ __forceinline__ uint32_t read_pred(int t) const {
+  __device__ __forceinline__ void fetch(int t) {
     const int g = min(t / steps_per_group, NG - 1);
-    const u32x4 lo = *(const WIDE_LDS u32x4 *)(bits + g * 8);
-    const u32x4 hi = *(const WIDE_LDS u32x4 *)(bits + g * 8 + 4);
-    const int sh = wave * 8 + lane / 8;  // row % 32 of every load instruction of this lane
-    uint32_t p = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) p |= ((lo[i] >> sh) & 1u) << i;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) p |= ((hi[i] >> sh) & 1u) << (i + 4);
-    return p;
+    wlo = *(const WIDE_LDS u32x4 *)(bits + g * 8);
+    whi = *(const WIDE_LDS u32x4 *)(bits + g * 8 + 4);
   }
 
   __device__ __forceinline__ void operator()(int t, eng::lds_u16 *sa, eng::lds_u16 *sb) {
+    // Load instruction i covers tile row 8 (wave + W i) + lane / 8: word
+    // (W / 4) i + wave / 4 of the table, bit (8 wave + lane / 8) % 32.
+    const int sh = (wave * 8 + lane / 8) % 32;
+    const bool hiw = S::WAVES == 8 && wave >= 4;
+    uint32_t p = 0;
+#pragma unroll
+    for (int i = 0; i < S::AI; ++i) {
+      const int w = (S::WAVES / 4) * i;  // word index for waves 0..3
+      const uint32_t x = w < 4 ? (hiw ? wlo[(w + 1) % 4] : wlo[w % 4]) : (hiw ? whi[(w + 1) % 4] : whi[w % 4]);
+      p |= ((x >> sh) & 1u) << i;
+    }
     const bool live = t < nk;
     const rsrc_t ra = live ? ar : none, rb = live ? br : none;
     const uint32_t k0 = (uint32_t)t * eng::kBK * 2u;
-    const uint32_t p = pred;
 #pragma unroll
-    for (int i = 0; i < KShape::AI; ++i)
-      eng::load_lds(ra, sa + (wave + 4 * i) * 512, ((p >> i) & 1u) ? aoff[i] : kOffNone, k0);
+    for (int i = 0; i < S::AI; ++i)
+      eng::load_lds(ra, eng::load_dst<S::WAVES>(sa, wave, i), ((p >> i) & 1u) ? aoff[i] : kOffNone, k0);
 #pragma unroll
-    for (int i = 0; i < KShape::BI; ++i) eng::load_lds(rb, sb + (wave + 4 * i) * 512, boff[i], k0);
-    next = t + 1;
-    pred = read_pred(next);
+    for (int i = 0; i < S::BI; ++i) eng::load_lds(rb, eng::load_dst<S::WAVES>(sb, wave, i), boff[i], k0);
+    if (t < AHEAD) fetch(t + 1);  // prologue: these stages are issued before any is multiplied
   }
+  // while stage t is multiplied, stage t + AHEAD has just been issued
+  __device__ __forceinline__ void prefetch(int t) { fetch(t + AHEAD + 1); }
 };
 
-__global__ __launch_bounds__(eng::kThreads) void gemm_k_kernel(KArgs a) {
-  __shared__ __attribute__((aligned(1024))) uint16_t sA0[eng::kBM * eng::kBK];
-  __shared__ __attribute__((aligned(1024))) uint16_t sB0[kKBN * eng::kBK];
-  __shared__ __attribute__((aligned(1024))) uint16_t sA1[eng::kBM * eng::kBK];
-  __shared__ __attribute__((aligned(1024))) uint16_t sB1[kKBN * eng::kBK];
-  __shared__ __attribute__((aligned(1024))) uint16_t sA2[eng::kBM * eng::kBK];
-  __shared__ __attribute__((aligned(1024))) uint16_t sB2[kKBN * eng::kBK];
+template <int BN, int W>
+__global__ __launch_bounds__(64 * W) void gemm_k_kernel(KArgs a) {
+  using S = eng::Shape<BN, W>;
+  constexpr int A3 = S::STAGES == 3 ? S::A_ELEMS : 8, B3 = S::STAGES == 3 ? S::B_ELEMS : 8;
+  __shared__ __attribute__((aligned(1024))) uint16_t sA0[S::A_ELEMS];
+  __shared__ __attribute__((aligned(1024))) uint16_t sB0[S::B_ELEMS];
+  __shared__ __attribute__((aligned(1024))) uint16_t sA1[S::A_ELEMS];
+  __shared__ __attribute__((aligned(1024))) uint16_t sB1[S::B_ELEMS];
+  __shared__ __attribute__((aligned(1024))) uint16_t sA2[A3];
+  __shared__ __attribute__((aligned(1024))) uint16_t sB2[B3];
   __shared__ __attribute__((aligned(16))) uint32_t sBits[kKMaxGroups][8];
 
-  const int MT = (a.M + eng::kBM - 1) / eng::kBM, NT = a.N / kKBN;
+  const int MT = (a.M + eng::kBM - 1) / eng::kBM, NT = a.N / BN;
   int mt, tn;
   eng::tile_of(blockIdx.x, MT, NT, mt, tn);
-  const int m0 = mt * eng::kBM, n0 = tn * kKBN;
+  const int m0 = mt * eng::kBM, n0 = tn * BN;
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-  const int wm = wave / 2, wn = wave % 2;
-  using S = KShape;
+  const int wm = wave / S::WNW, wn = wave % S::WNW;
 
-  const bool any = build_bits(a, m0, (WIDE_LDS uint32_t *)&sBits[0][0], (WIDE_LDS int *)sA2);
-  f32x4 acc[S::FN][S::FM];
+  const bool any = build_bits<S::THREADS>(a, m0, (WIDE_LDS uint32_t *)&sBits[0][0], (WIDE_LDS int *)sA1);
+  eng::Acc<S> acc;
 #pragma unroll
   for (int i = 0; i < S::FN; ++i)
 #pragma unroll
     for (int j = 0; j < S::FM; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   if (any) {  // level 0: otherwise the tile's product is exactly zero
-    KLoader ld;
+    KLoader<S> ld;
     const int rows = min(eng::kBM, a.M - m0);
     ld.ar = make_rsrc(a.A + (size_t)m0 * a.lda, (uint64_t)rows * a.lda * 2);  // rows past M: out of range
-    ld.br = make_rsrc(a.B + (size_t)n0 * a.ldb, (uint64_t)kKBN * a.ldb * 2);
+    ld.br = make_rsrc(a.B + (size_t)n0 * a.ldb, (uint64_t)BN * a.ldb * 2);
     ld.none = make_rsrc(a.A, 0);
 #pragma unroll
     for (int i = 0; i < S::AI; ++i) {
-      const int r = eng::load_row(wave, i, lane);
+      const int r = eng::load_row<W>(wave, i, lane);
       ld.aoff[i] = (uint32_t)r * (uint32_t)a.lda * 2u + eng::load_chunk_bytes(r, lane);
     }
 #pragma unroll
     for (int i = 0; i < S::BI; ++i) {
-      const int r = eng::load_row(wave, i, lane);
+      const int r = eng::load_row<W>(wave, i, lane);
       ld.boff[i] = (uint32_t)r * (uint32_t)a.ldb * 2u + eng::load_chunk_bytes(r, lane);
     }
     ld.bits = (const WIDE_LDS uint32_t *)&sBits[0][0];
@@ -163,10 +187,9 @@ __global__ __launch_bounds__(eng::kThreads) void gemm_k_kernel(KArgs a) {
     ld.NG = a.K / a.G;
     ld.wave = wave;
     ld.lane = lane;
-    ld.next = 0;
-    ld.pred = ld.read_pred(0);
-    eng::mainloop<kKBN, false>(ld.nk, ld, (eng::lds_u16 *)sA0, (eng::lds_u16 *)sB0, (eng::lds_u16 *)sA1,
-                               (eng::lds_u16 *)sB1, (eng::lds_u16 *)sA2, (eng::lds_u16 *)sB2, acc, wm, wn, lane);
+    ld.fetch(0);
+    eng::mainloop<S, BN, false>(ld.nk, ld, (eng::lds_u16 *)sA0, (eng::lds_u16 *)sB0, (eng::lds_u16 *)sA1,
+                                (eng::lds_u16 *)sB1, (eng::lds_u16 *)sA2, (eng::lds_u16 *)sB2, acc, wm, wn, lane);
   }
 
   // C = beta * C + acc; a lane holds row (lane % 16) of A fragment j and
@@ -273,11 +296,13 @@ __global__ __launch_bounds__(256) void gemv_k_kernel(KArgs a) {
 }
 
 int launch_gemm_k(const KArgs &a, hipStream_t s) {
+  const int mt = (a.M + eng::kBM - 1) / eng::kBM;
   if (a.M <= 4) {
     hipLaunchKernelGGL(gemv_k_kernel, dim3(a.N / 4), dim3(256), 0, s, a);
+  } else if (a.N % 256 == 0) {
+    hipLaunchKernelGGL((gemm_k_kernel<256, 8>), dim3(mt * (a.N / 256)), dim3(512), 0, s, a);
   } else {
-    const int tiles = ((a.M + eng::kBM - 1) / eng::kBM) * (a.N / kKBN);
-    hipLaunchKernelGGL(gemm_k_kernel, dim3(tiles), dim3(eng::kThreads), 0, s, a);
+    hipLaunchKernelGGL((gemm_k_kernel<128, 4>), dim3(mt * (a.N / 128)), dim3(256), 0, s, a);
   }
   return check_launch();
 }

@@ -15,9 +15,10 @@
 // activation is ever copied. Level 2 (skipping MFMA fragments) only matters
 // in the one partial tile per group and is not taken.
 //
-// The tile runs on the shared 3-stage MFMA main loop: 256 sorted rows x BN
-// weight rows (BN = 128, or 64 when G is not a multiple of 128; for the fused
-// SwiGLU variant 64 gate + the matching 64 up rows, giving 64 outputs).
+// The tile runs on the shared MFMA main loop: 256 sorted rows x BN weight
+// rows, BN = 256 (8 waves) when a group spans 256 of them, else 128 or 64 (4
+// waves). The fused SwiGLU variant stages BN/2 gate rows and the matching
+// BN/2 up rows and writes BN/2 outputs.
 //
 // For M <= 4 with no reorder (one decode step), a matrix-vector kernel reads
 // the mask bytes directly and streams only the active groups' weight rows.
@@ -50,13 +51,15 @@ __device__ __forceinline__ void store_out4(void *C, size_t idx, const f32x4 &v, 
   }
 }
 
-template <int BN, bool SPLIT>
+template <class S, bool SPLIT>
 struct MnLoader {
-  using S = eng::Shape<BN>;
+  static constexpr int kDsReads = 0;
   rsrc_t ar, br0, br1, none;
   uint32_t aoff[S::AI], boff[S::BI];
   int nk, K, wave;
   int kchunk;  // first k (elements) of this lane's 16-byte chunk within a stage
+
+  __device__ __forceinline__ void prefetch(int) const {}
 
   __device__ __forceinline__ void operator()(int t, eng::lds_u16 *sa, eng::lds_u16 *sb) const {
     const bool live = t < nk;
@@ -65,25 +68,27 @@ struct MnLoader {
     const bool in = t * eng::kBK + kchunk < K;
     const rsrc_t ra = live ? ar : none;
 #pragma unroll
-    for (int i = 0; i < S::AI; ++i) eng::load_lds(ra, sa + (wave + 4 * i) * 512, in ? aoff[i] : kOffNone, k0);
+    for (int i = 0; i < S::AI; ++i) eng::load_lds(ra, eng::load_dst<S::WAVES>(sa, wave, i), in ? aoff[i] : kOffNone, k0);
 #pragma unroll
     for (int i = 0; i < S::BI; ++i) {
+      // split tiles: the first half of the B rows are gate rows, the rest up rows
       const rsrc_t rb = live ? ((SPLIT && i >= S::BI / 2) ? br1 : br0) : none;
-      eng::load_lds(rb, sb + (wave + 4 * i) * 512, in ? boff[i] : kOffNone, k0);
+      eng::load_lds(rb, eng::load_dst<S::WAVES>(sb, wave, i), in ? boff[i] : kOffNone, k0);
     }
   }
 };
 
-template <int BN, bool SWIGLU, bool OUT_F32>
-__global__ __launch_bounds__(eng::kThreads) void gemm_mn_kernel(MnArgs a) {
-  using S = eng::Shape<BN>;
+template <int BN, int W, bool SWIGLU, bool OUT_F32>
+__global__ __launch_bounds__(64 * W) void gemm_mn_kernel(MnArgs a) {
+  using S = eng::Shape<BN, W>;
   constexpr int BN_OUT = SWIGLU ? BN / 2 : BN;
+  constexpr int A3 = S::STAGES == 3 ? S::A_ELEMS : 8, B3 = S::STAGES == 3 ? S::B_ELEMS : 8;
   __shared__ __attribute__((aligned(1024))) uint16_t sA0[S::A_ELEMS];
   __shared__ __attribute__((aligned(1024))) uint16_t sB0[S::B_ELEMS];
   __shared__ __attribute__((aligned(1024))) uint16_t sA1[S::A_ELEMS];
   __shared__ __attribute__((aligned(1024))) uint16_t sB1[S::B_ELEMS];
-  __shared__ __attribute__((aligned(1024))) uint16_t sA2[S::A_ELEMS];
-  __shared__ __attribute__((aligned(1024))) uint16_t sB2[S::B_ELEMS];
+  __shared__ __attribute__((aligned(1024))) uint16_t sA2[A3];
+  __shared__ __attribute__((aligned(1024))) uint16_t sB2[B3];
   __shared__ int sRows[eng::kBM];
 
   const int MT = (a.M + eng::kBM - 1) / eng::kBM, NT = a.N / BN_OUT;
@@ -94,11 +99,11 @@ __global__ __launch_bounds__(eng::kThreads) void gemm_mn_kernel(MnArgs a) {
   const int s0 = mt * eng::kBM;
   if (s0 >= cnt) return;  // level 0
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-  const int wm = wave / 2, wn = wave % 2;
-  sRows[tid] = s0 + tid < cnt ? a.perm[(size_t)g * a.M + s0 + tid] : -1;
+  const int wm = wave / S::WNW, wn = wave % S::WNW;
+  if (tid < eng::kBM) sRows[tid] = s0 + tid < cnt ? a.perm[(size_t)g * a.M + s0 + tid] : -1;
   __syncthreads();
 
-  MnLoader<BN, SWIGLU> ld;
+  MnLoader<S, SWIGLU> ld;
   ld.ar = make_rsrc(a.A, (uint64_t)a.M * a.lda * 2);
   const int brows = SWIGLU ? BN / 2 : BN;
   ld.br0 = make_rsrc(a.B0 + (size_t)n0 * a.ldb, (uint64_t)brows * a.ldb * 2);
@@ -106,28 +111,28 @@ __global__ __launch_bounds__(eng::kThreads) void gemm_mn_kernel(MnArgs a) {
   ld.none = make_rsrc(a.A, 0);
 #pragma unroll
   for (int i = 0; i < S::AI; ++i) {
-    const int r = eng::load_row(wave, i, lane);
+    const int r = eng::load_row<W>(wave, i, lane);
     const int phys = sRows[r];
     ld.aoff[i] = phys >= 0 ? (uint32_t)phys * (uint32_t)a.lda * 2u + eng::load_chunk_bytes(r, lane) : kOffNone;
   }
 #pragma unroll
   for (int i = 0; i < S::BI; ++i) {
-    const int r = eng::load_row(wave, i, lane);
+    const int r = eng::load_row<W>(wave, i, lane);
     const int rb = SWIGLU ? r % (BN / 2) : r;
     ld.boff[i] = (uint32_t)rb * (uint32_t)a.ldb * 2u + eng::load_chunk_bytes(r, lane);
   }
   ld.nk = (a.K + eng::kBK - 1) / eng::kBK;
   ld.K = a.K;
   ld.wave = wave;
-  ld.kchunk = (int)(eng::load_chunk_bytes(eng::load_row(wave, 0, lane), lane) / 2);
+  ld.kchunk = (int)(eng::load_chunk_bytes(eng::load_row<W>(wave, 0, lane), lane) / 2);
 
-  f32x4 acc[S::FN][S::FM];
+  eng::Acc<S> acc;
 #pragma unroll
   for (int i = 0; i < S::FN; ++i)
 #pragma unroll
     for (int j = 0; j < S::FM; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  eng::mainloop<BN, SWIGLU>(ld.nk, ld, (eng::lds_u16 *)sA0, (eng::lds_u16 *)sB0, (eng::lds_u16 *)sA1,
-                            (eng::lds_u16 *)sB1, (eng::lds_u16 *)sA2, (eng::lds_u16 *)sB2, acc, wm, wn, lane);
+  eng::mainloop<S, BN, SWIGLU>(ld.nk, ld, (eng::lds_u16 *)sA0, (eng::lds_u16 *)sB0, (eng::lds_u16 *)sA1,
+                               (eng::lds_u16 *)sB1, (eng::lds_u16 *)sA2, (eng::lds_u16 *)sB2, acc, wm, wn, lane);
 
   // Scatter: a lane holds sorted row (lane % 16) of A fragment j and
   // features 4 (lane / 16) .. +3 of B fragment i.
@@ -224,11 +229,11 @@ __global__ __launch_bounds__(256) void gemv_mn_kernel(MnArgs a) {
   }
 }
 
-template <int BN, bool SWIGLU, bool F32>
+template <int BN, int W, bool SWIGLU, bool F32>
 static void launch_tiled(const MnArgs &a, hipStream_t s) {
   constexpr int BN_OUT = SWIGLU ? BN / 2 : BN;
   const int tiles = (a.N / BN_OUT) * ((a.M + eng::kBM - 1) / eng::kBM);
-  hipLaunchKernelGGL((gemm_mn_kernel<BN, SWIGLU, F32>), dim3(tiles), dim3(eng::kThreads), 0, s, a);
+  hipLaunchKernelGGL((gemm_mn_kernel<BN, W, SWIGLU, F32>), dim3(tiles), dim3(64 * W), 0, s, a);
 }
 
 template <bool SWIGLU, bool F32>
@@ -244,12 +249,16 @@ int launch_gemm_mn(const MnArgs &a, hipStream_t s) {
     } else {
       if (a.c_f32) launch_gemv<false, true>(a, s); else launch_gemv<false, false>(a, s);
     }
+  } else if (swiglu && a.G % 128 == 0) {  // 128 gate + 128 up rows: one group per tile
+    if (a.c_f32) launch_tiled<256, 8, true, true>(a, s); else launch_tiled<256, 8, true, false>(a, s);
   } else if (swiglu) {
-    if (a.c_f32) launch_tiled<128, true, true>(a, s); else launch_tiled<128, true, false>(a, s);
+    if (a.c_f32) launch_tiled<128, 4, true, true>(a, s); else launch_tiled<128, 4, true, false>(a, s);
+  } else if (a.G % 256 == 0) {
+    if (a.c_f32) launch_tiled<256, 8, false, true>(a, s); else launch_tiled<256, 8, false, false>(a, s);
   } else if (a.G % 128 == 0) {
-    if (a.c_f32) launch_tiled<128, false, true>(a, s); else launch_tiled<128, false, false>(a, s);
+    if (a.c_f32) launch_tiled<128, 4, false, true>(a, s); else launch_tiled<128, 4, false, false>(a, s);
   } else {
-    if (a.c_f32) launch_tiled<64, false, true>(a, s); else launch_tiled<64, false, false>(a, s);
+    if (a.c_f32) launch_tiled<64, 4, false, true>(a, s); else launch_tiled<64, 4, false, false>(a, s);
   }
   return check_launch();
 }

@@ -1,13 +1,23 @@
 // Shared MFMA main loop of the tiled GEMM kernels (gfx950). Internal to
 // libwide.so.
 //
-// A workgroup of 4 waves computes a 256 x BN tile of D = A * B^T (A rows are
-// tokens, B rows are output features). Every k-step moves a 64-deep slice of
-// both operands (128-byte row segments) from global memory straight into LDS
-// with buffer loads that write LDS directly, through a ring of 3 stages, so
-// two slices are in flight while the third is multiplied and one barrier per
-// step suffices. Each wave owns a 128 x BN/2 block of the tile and multiplies
-// it with 16x16x32 bf16 MFMAs, fp32 accumulators held in registers.
+// A workgroup computes a 256 x BN tile of D = A * B^T (A rows are tokens, B
+// rows are output features) with W waves: W = 4 (one per SIMD, 2 x 2 waves,
+// BN = 64 or 128) or W = 8 (two per SIMD, 2 x 4 waves, BN = 256). Every wave
+// owns a 128 x BN/(W/2) block and multiplies it with 16x16x32 bf16 MFMAs into
+// fp32 accumulators held in registers.
+//
+// Every k-step moves a 64-deep slice of both operands (128-byte row segments)
+// from global memory straight into LDS with buffer loads that write LDS
+// directly: through a ring of 3 stages for W = 4 (LDS 48 KB per stage), of 2
+// stages for W = 8 (64 KB per stage), one barrier per step.
+//
+// Measured on MI355X, the limits of this loop are the MFMA rate, the LDS read
+// rate and the address unit that takes the stage loads: a CU accepts about
+// one 1 KB load instruction per 15 cycles and a wave that issues a load the
+// unit cannot take yet stalls, MFMAs included. The stage loads are therefore
+// spread between MFMAs (scheduling groups impose the order), and the 8-wave
+// tile halves both the load instructions and the LDS reads per flop.
 //
 // Loads past a buffer resource's range return zeros and move no data, which
 // is how rows that are not active (or past the end) are skipped: the caller
@@ -22,19 +32,23 @@ namespace eng {
 #define WIDE_LDS __attribute__((address_space(3)))
 typedef WIDE_LDS uint16_t lds_u16;
 
-constexpr int kBM = 256;      // A rows per tile
-constexpr int kBK = 64;       // reduction depth per stage
-constexpr int kThreads = 256;  // 4 waves, one per SIMD
-constexpr int kGroupM = 4;    // m-tiles per raster group
+constexpr int kBM = 256;    // A rows per tile
+constexpr int kBK = 64;     // reduction depth per stage
+constexpr int kGroupM = 4;  // m-tiles per raster group
 
-template <int BN>
+template <int BN, int W>
 struct Shape {
-  static constexpr int TM = 128;       // wave block rows (2 x 2 waves)
-  static constexpr int TN = BN / 2;    // wave block columns
-  static constexpr int FM = TM / 16;   // 16-row fragments of A per wave
-  static constexpr int FN = TN / 16;   // 16-row fragments of B per wave
-  static constexpr int AI = kBM / 32;  // A load instructions per wave per stage
-  static constexpr int BI = BN / 32;   // B load instructions per wave per stage
+  static_assert((W == 4 && (BN == 64 || BN == 128)) || (W == 8 && BN == 256), "unsupported tile");
+  static constexpr int WAVES = W;
+  static constexpr int THREADS = 64 * W;
+  static constexpr int WNW = W / 2;         // waves along n (2 along m)
+  static constexpr int STAGES = W == 4 ? 3 : 2;
+  static constexpr int TM = 128;            // wave block rows
+  static constexpr int TN = BN / WNW;       // wave block columns
+  static constexpr int FM = TM / 16;        // 16-row fragments of A per wave
+  static constexpr int FN = TN / 16;        // 16-row fragments of B per wave
+  static constexpr int AI = kBM / 8 / W;    // A load instructions per wave per stage
+  static constexpr int BI = BN / 8 / W;     // B load instructions per wave per stage
   static constexpr int NLOAD = AI + BI;
   static constexpr int A_ELEMS = kBM * kBK;
   static constexpr int B_ELEMS = BN * kBK;
@@ -45,12 +59,15 @@ struct Shape {
 // 16 distinct 16-byte bank groups.
 __device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
 
-// Load instruction i of a wave moves 1 KB: rows 8j .. 8j+7 (j = wave + 4i),
+// Load instruction i of a wave moves 1 KB: rows 8j .. 8j+7 (j = wave + W i),
 // lane l taking row 8j + l/8 and storing LDS position l % 8.
-__device__ __forceinline__ int load_row(int wave, int i, int lane) { return (wave + 4 * i) * 8 + lane / 8; }
+template <int W>
+__device__ __forceinline__ int load_row(int wave, int i, int lane) { return (wave + W * i) * 8 + lane / 8; }
 __device__ __forceinline__ uint32_t load_chunk_bytes(int row, int lane) {
   return (uint32_t)(((lane % 8) ^ swz(row)) * 16);
 }
+template <int W>
+__device__ __forceinline__ lds_u16 *load_dst(lds_u16 *stage, int wave, int i) { return stage + (wave + W * i) * 512; }
 
 __device__ __forceinline__ void load_lds(rsrc_t r, lds_u16 *dst, uint32_t voff, uint32_t soff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (WIDE_LDS void *)dst, 16, (int)voff, (int)soff, 0, 0);
@@ -65,28 +82,32 @@ __device__ __forceinline__ void load_lds(rsrc_t r, lds_u16 *dst, uint32_t voff, 
     __builtin_amdgcn_sched_barrier(0);  \
   } while (0)
 
-template <int BN>
+template <class S>
 struct Frag {
-  u32x4 a[Shape<BN>::FM], b[Shape<BN>::FN];
+  u32x4 a[S::FM], b[S::FN];
 };
+
+template <class S>
+using Acc = f32x4[S::FN][S::FM];
 
 // B fragment i of wave column wn: rows wn*TN + 16i, or, for a split tile
 // (SwiGLU: stage rows [0, BN/2) gate, [BN/2, BN) up), gate rows for the first
 // half of the fragments and the matching up rows for the second half.
-template <int BN, bool SPLIT>
+template <class S, int BN, bool SPLIT>
 __device__ __forceinline__ int b_frag_row(int wn, int i) {
-  using S = Shape<BN>;
   if (!SPLIT) return wn * S::TN + i * 16;
   return i < S::FN / 2 ? wn * (S::TN / 2) + i * 16 : BN / 2 + wn * (S::TN / 2) + (i - S::FN / 2) * 16;
 }
 
-template <int BN, bool SPLIT>
-__device__ __forceinline__ void compute_stage(const lds_u16 *sa, const lds_u16 *sb, f32x4 (&acc)[Shape<BN>::FN][Shape<BN>::FM],
-                                              int wm, int wn, int lane) {
-  using S = Shape<BN>;
+// One stage: two 32-deep halves, each reading its fragments then issuing the
+// MFMAs. `issue.prefetch(t)` runs after the first half's reads (the loader's
+// own LDS reads, consumed at the next step).
+template <class S, int BN, bool SPLIT, class Issue>
+__device__ __forceinline__ void compute_stage(const lds_u16 *sa, const lds_u16 *sb, Acc<S> &acc, int wm, int wn,
+                                              int lane, Issue &issue, int t) {
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
-    Frag<BN> f;
+    Frag<S> f;
 #pragma unroll
     for (int i = 0; i < S::FM; ++i) {
       const int row = wm * S::TM + i * 16 + lane % 16;
@@ -94,9 +115,10 @@ __device__ __forceinline__ void compute_stage(const lds_u16 *sa, const lds_u16 *
     }
 #pragma unroll
     for (int i = 0; i < S::FN; ++i) {
-      const int row = b_frag_row<BN, SPLIT>(wn, i) + lane % 16;
+      const int row = b_frag_row<S, BN, SPLIT>(wn, i) + lane % 16;
       f.b[i] = *(const WIDE_LDS u32x4 *)(sb + row * kBK + (((s * 4 + lane / 16) ^ swz(row)) * 8));
     }
+    if (s == 0) issue.prefetch(t);
     // D^T blocks: lane holds tile row (A) lane % 16 of fragment j and
     // columns (B) 4 * (lane / 16) + v of fragment i.
 #pragma unroll
@@ -106,35 +128,87 @@ __device__ __forceinline__ void compute_stage(const lds_u16 *sa, const lds_u16 *
   }
 }
 
-// The k-loop. `issue(t, sa, sb)` must issue exactly Shape<BN>::NLOAD buffer
-// loads per wave for stage t into (sa, sb), out of range when t >= nk, and no
-// other vector-memory loads. The three stage buffers are distinct LDS objects
-// so the compiler can tell the stages apart when it places its own waits.
-template <int BN, bool SPLIT, class Issue>
+// Scheduling groups of one half: NR LDS reads, then NV x (Q MFMAs, 1 stage
+// load), then the remaining MFMAs.
+template <int NR, int NM, int NV>
+__device__ __forceinline__ void interleave_half() {
+  __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);  // DS reads
+  if constexpr (NV > 0) {
+    constexpr int Q = NM / NV;
+    static_assert(Q >= 1, "more stage loads than MFMAs in a half");
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, Q, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);  // VMEM
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, NM - Q * NV, 0);
+  } else {
+    __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
+  }
+}
+
+// Order of one step. 3 stages: the stage loads are spread over both halves.
+// 2 stages: the next stage is needed at the next step, so its loads all go in
+// the first half. The loader's own LDS reads come first in program order.
+template <class S, int EXTRA_DS>
+__device__ __forceinline__ void interleave() {
+  constexpr int NR = S::FM + S::FN, NM = S::FM * S::FN;
+  if constexpr (S::STAGES == 3) {
+    static_assert(S::NLOAD % 2 == 0, "stage loads must split over the two halves");
+    interleave_half<NR + EXTRA_DS, NM, S::NLOAD / 2>();
+    interleave_half<NR, NM, S::NLOAD / 2>();
+  } else {
+    interleave_half<NR + EXTRA_DS, NM, S::NLOAD>();
+    interleave_half<NR, NM, 0>();
+  }
+}
+
+// The k-loop. `issue(t, sa, sb)` must issue exactly S::NLOAD buffer loads per
+// wave for stage t into (sa, sb), out of range when t >= nk, and no other
+// vector-memory loads; `issue.prefetch(t)` (called while stage t is
+// multiplied) may issue Issue::kDsReads LDS reads whose results the next issue
+// uses. The stage buffers are distinct LDS objects so the compiler can tell
+// them apart when it places its own waits.
+//
+// 3 stages: stage t sits in buffer t % 3; after the barrier of step t every
+// wave is done with buffer (t + 2) % 3, which then receives stage t + 2.
+// 2 stages: after the barrier of step t every wave is done with the other
+// buffer, which then receives stage t + 1.
+template <class S, int BN, bool SPLIT, class Issue>
 __device__ __forceinline__ void mainloop(int nk, Issue &issue, lds_u16 *a0, lds_u16 *b0, lds_u16 *a1, lds_u16 *b1,
-                                         lds_u16 *a2, lds_u16 *b2, f32x4 (&acc)[Shape<BN>::FN][Shape<BN>::FM], int wm,
-                                         int wn, int lane) {
-  constexpr int NL = Shape<BN>::NLOAD;
-  issue(0, a0, b0);
-  issue(1, a1, b1);
+                                         lds_u16 *a2, lds_u16 *b2, Acc<S> &acc, int wm, int wn, int lane) {
+  constexpr int NL = S::NLOAD;
   int t = 0;
-  // Stage t sits in buffer t % 3; after the barrier every wave is done with
-  // buffer (t + 2) % 3, which then receives stage t + 2.
-#define WIDE_STEP(CA, CB, NA, NB)                                         \
-  {                                                                       \
-    WIDE_WAIT_VM_LGKM0(NL);                                               \
-    WIDE_BARRIER();                                                       \
-    issue(t + 2, NA, NB);                                                 \
-    compute_stage<BN, SPLIT>(CA, CB, acc, wm, wn, lane);                  \
-    ++t;                                                                  \
+#define WIDE_STEP(WAITN, CA, CB, NA, NB, AHEAD)                         \
+  {                                                                     \
+    WIDE_WAIT_VM_LGKM0(WAITN);                                          \
+    WIDE_BARRIER();                                                     \
+    issue(t + AHEAD, NA, NB);                                           \
+    compute_stage<S, BN, SPLIT>(CA, CB, acc, wm, wn, lane, issue, t);   \
+    interleave<S, Issue::kDsReads>();                                   \
+    __builtin_amdgcn_sched_barrier(0);                                  \
+    ++t;                                                                \
   }
-  for (; t + 3 <= nk;) {
-    WIDE_STEP(a0, b0, a2, b2)
-    WIDE_STEP(a1, b1, a0, b0)
-    WIDE_STEP(a2, b2, a1, b1)
+  if constexpr (S::STAGES == 3) {
+    issue(0, a0, b0);
+    issue(1, a1, b1);
+    for (; t + 3 <= nk;) {
+      WIDE_STEP(NL, a0, b0, a2, b2, 2)
+      WIDE_STEP(NL, a1, b1, a0, b0, 2)
+      WIDE_STEP(NL, a2, b2, a1, b1, 2)
+    }
+    if (t < nk) WIDE_STEP(NL, a0, b0, a2, b2, 2)
+    if (t < nk) WIDE_STEP(NL, a1, b1, a0, b0, 2)
+  } else {
+    (void)a2;
+    (void)b2;
+    issue(0, a0, b0);
+    for (; t + 2 <= nk;) {
+      WIDE_STEP(0, a0, b0, a1, b1, 1)
+      WIDE_STEP(0, a1, b1, a0, b0, 1)
+    }
+    if (t < nk) WIDE_STEP(0, a0, b0, a1, b1, 1)
   }
-  if (t < nk) WIDE_STEP(a0, b0, a2, b2)
-  if (t < nk) WIDE_STEP(a1, b1, a0, b0)
 #undef WIDE_STEP
   WIDE_WAIT_VM_LGKM0(0);
 }
