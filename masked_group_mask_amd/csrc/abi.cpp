@@ -143,7 +143,7 @@ int wide_gemm_k(const wide_bf16 *A, int64_t lda, const wide_bf16 *B, int64_t ldb
   if ((uint64_t)lda * 512u > 0x7fffffffull || (uint64_t)ldb * 512u > 0x7fffffffull)
     return WIDE_ERR_UNSUPPORTED;
   if (!device_ok()) return WIDE_ERR_NO_DEVICE;
-  wide::KArgs a{A, lda, B, ldb, C, ldc, beta, (int)M, (int)N, (int)K, (int)G, mask};
+  wide::KArgs a{A, lda, B, ldb, C, ldc, beta, (int)M, (int)N, (int)K, (int)G, mask, 0, 0};
   return wide::launch_gemm_k(a, reinterpret_cast<hipStream_t>(stream));
 }
 

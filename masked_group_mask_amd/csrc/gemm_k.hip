@@ -22,6 +22,8 @@
 //   - the summation order is fixed, so results are reproducible bit for bit.
 // For M <= 4 a matrix-vector kernel streams only the K-groups some token
 // keeps.
+#include <atomic>
+
 #include "common.hpp"
 #include "launch.hpp"
 #include "mma_engine.hpp"
@@ -151,10 +153,16 @@ __global__ __launch_bounds__(64 * W) void gemm_k_kernel(KArgs a) {
   __shared__ __attribute__((aligned(1024))) uint16_t sB2[B3];
   __shared__ __attribute__((aligned(16))) uint32_t sBits[kKMaxGroups][8];
 
-  const int MT = (a.M + eng::kBM - 1) / eng::kBM, NT = a.N / BN;
-  int mt, tn;
-  eng::tile_of(blockIdx.x, MT, NT, mt, tn);
-  const int m0 = mt * eng::kBM, n0 = tn * BN;
+  const int MT = (a.M + eng::kBM - 1) / eng::kBM;
+  int mt, tn, n0;
+  if (a.split_tail) {  // half of a 256 x 256 tile of the raster
+    eng::tile_of(a.tile_base + (int)blockIdx.x / 2, MT, a.N / 256, mt, tn);
+    n0 = tn * 256 + ((int)blockIdx.x % 2) * BN;
+  } else {
+    eng::tile_of(a.tile_base + (int)blockIdx.x, MT, a.N / BN, mt, tn);
+    n0 = tn * BN;
+  }
+  const int m0 = mt * eng::kBM;
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
   const int wm = wave / S::WNW, wn = wave % S::WNW;
 
@@ -295,12 +303,41 @@ __global__ __launch_bounds__(256) void gemv_k_kernel(KArgs a) {
   }
 }
 
-int launch_gemm_k(const KArgs &a, hipStream_t s) {
+int cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cache[dev].load();
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev].store(n);
+  }
+  return n;
+}
+
+// Tiled launches. With N a multiple of 256 the 8-wave 256 x 256 kernel runs;
+// when its tiles leave a last round at most half full (640 tiles on 256 CUs
+// run as 3 rounds, 2.5 of work), the leftover tiles are covered by twice as
+// many 256 x 128 workgroups of the 4-wave kernel in a second launch, which
+// take one round of half the length. Each output element is still computed
+// by one workgroup with a fixed summation order.
+int launch_gemm_k(const KArgs &a0, hipStream_t s) {
+  KArgs a = a0;
+  a.tile_base = 0;
+  a.split_tail = 0;
   const int mt = (a.M + eng::kBM - 1) / eng::kBM;
   if (a.M <= 4) {
     hipLaunchKernelGGL(gemv_k_kernel, dim3(a.N / 4), dim3(256), 0, s, a);
   } else if (a.N % 256 == 0) {
-    hipLaunchKernelGGL((gemm_k_kernel<256, 8>), dim3(mt * (a.N / 256)), dim3(512), 0, s, a);
+    const int tiles = mt * (a.N / 256), cus = cu_count();
+    const int tail = tiles % cus;
+    const int head = tiles > cus && tail > 0 && 2 * tail <= cus ? tiles - tail : tiles;
+    hipLaunchKernelGGL((gemm_k_kernel<256, 8>), dim3(head), dim3(512), 0, s, a);
+    if (head < tiles) {
+      a.tile_base = head;
+      a.split_tail = 1;
+      hipLaunchKernelGGL((gemm_k_kernel<128, 4>), dim3(2 * (tiles - head)), dim3(256), 0, s, a);
+    }
   } else {
     hipLaunchKernelGGL((gemm_k_kernel<128, 4>), dim3(mt * (a.N / 128)), dim3(256), 0, s, a);
   }

@@ -10,6 +10,9 @@
 
 namespace wide {
 
+// Compute units of the current device (cached per device).
+int cu_count();
+
 inline int check_launch() {
   const hipError_t e = hipGetLastError();
   return e == hipSuccess ? WIDE_OK : WIDE_ERR_LAUNCH;
@@ -53,6 +56,11 @@ struct KArgs {
   int beta;
   int M, N, K, G;
   const uint8_t *mask;
+  // Set by the launcher: the tiled kernels cover logical 256 x 256 tiles
+  // tile_base, tile_base + 1, ... of the raster; with split_tail each one is
+  // covered by two 256 x 128 workgroups.
+  int tile_base;
+  int split_tail;
 };
 int launch_gemm_k(const KArgs &a, hipStream_t stream);
 

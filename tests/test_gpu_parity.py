@@ -189,6 +189,8 @@ def test_gemv_mn_mask_direct(M, swiglu):
 K_CASES = [  # M, N, K, G
     (64, 256, 1024, 128), (300, 256, 512, 128), (300, 384, 640, 64), (1000, 128, 2560, 640),
     (129, 128, 512, 256), (5, 256, 256, 128),
+    # 17 x 16 = 272 tiles of 256 x 256: on 256 CUs the 16 left over run as 32 half-width tiles
+    (4352, 4096, 256, 128),
 ]
 
 
