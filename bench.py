@@ -87,6 +87,29 @@ def bench_decode(torch, wl, metrics, steps=50, sets=3):
     }
 
 
+def measured_traffic(op: str):
+    """Bytes per launch of `op` from profiles/traffic.json (two rocprofv3
+    counter passes, scaled by the same counters on a copy of known size), or
+    None when no record covers `op` or its kernel sources changed since."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("op") != op:
+        return None
+    for rel, sha in rec.get("sources_sha256", {}).items():
+        try:
+            with open(os.path.join(ROOT, rel), "rb") as f:
+                if hashlib.sha256(f.read()).hexdigest() != sha:
+                    return None
+        except OSError:
+            return None
+    return float(rec["traffic_bytes_per_launch"])
+
+
 def cpu_baseline(s, host, rows: int):
     """The CPU oracle on `rows` token rows of the same layer (all routed ops)."""
     from oracle import wide_ref as ref
@@ -136,6 +159,11 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--only", metavar="OP", default=None,
+                    help="profiling aid: after one full masked step, run only this op --steps times")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="profiling aid: run a plain device copy of this many bytes --steps times "
+                         "(reference for the HBM byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -152,6 +180,15 @@ def main():
         sys.exit(1)
     mg.load()
     torch.cuda.set_device(0)
+    if args.copy_bytes:
+        n = args.copy_bytes // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            torch.mul(src, 1.0, out=dst)  # reads n*4 bytes, writes n*4 bytes
+        torch.cuda.synchronize()
+        log(f"copied {n * 4} bytes {args.steps} times")
+        return
 
     p = 1.0 - args.sparsity
     s = wl.shape(args.workload, p_attn=p, p_ffn=p, G_ffn=args.g_ffn)
@@ -167,6 +204,14 @@ def main():
     dense_flops = metrics.layer_flops(s, ones_a, ones_f)
     total_flops = sum(flops.values())
 
+    if args.only:
+        layer.step("masked")
+        for _ in range(args.steps):
+            layer.run(args.only, "masked")
+        torch.cuda.synchronize()
+        log(f"ran {args.only} {args.steps} times")
+        return
+
     log("timing masked layer")
     ms, per_op = time_steps(layer, "masked", args.steps, args.warmup, torch)
     log(f"masked: {ms:.3f} ms/step  " + " ".join(f"{k}={v:.3f}" for k, v in per_op.items()))
@@ -180,7 +225,9 @@ def main():
     dom = max((op for op in per_op if op != "reorder"), key=lambda k: per_op[k])
     achieved = flops[dom] / (per_op[dom] * 1e-3) / 1e12
     roof = {"kernel": dom, "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
-            "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+            "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+            # L2-to-memory bytes per launch (rocprofv3 FETCH_SIZE/WRITE_SIZE, copy-scaled)
+            "traffic": measured_traffic(dom),
             "flops_per_launch": flops[dom], "avg_launch_ms": per_op[dom]}
 
     out = {

@@ -48,8 +48,8 @@ class PrefillLayer:
         self.perm_f = torch.empty((1, s.NG_ffn, M), dtype=i32, device=dev)
         self.cnt_f = torch.empty((1, s.NG_ffn), dtype=i32, device=dev)
         # Every consumer reads only the active entries of its input (GEMM-K
-        # compacts active rows per group, attention gathers active rows), so
-        # the intermediate buffers need no zero-initialisation.
+        # loads only the active (row, group) segments, attention gathers active
+        # rows), so the intermediate buffers need no zero-initialisation.
         self.q = torch.empty((M, s.Hq * s.d), dtype=torch.bfloat16, device=dev)
         self.o = torch.empty((B, T, s.Hq, s.d), dtype=torch.bfloat16, device=dev)
         self.h = torch.empty((M, s.Dff), dtype=torch.bfloat16, device=dev)
@@ -58,29 +58,40 @@ class PrefillLayer:
         if B != 1:
             raise ValueError("the prefill layer driver flattens tokens with B = 1")
 
-    def step(self, which: str = "masked", events=None) -> None:
+    def run(self, op: str, which: str = "masked") -> None:
+        """Enqueue one op of the step on the current stream; it reads whatever
+        the buffers hold (run the ops in PREFILL_OPS order for a layer pass)."""
         s = self.s
         ma, mf = self.masks[which]
-        rec = (lambda i: events[i].record()) if events is not None else (lambda i: None)
-        rec(0)
-        mg.reorder(ma, self.perm_a, self.cnt_a)
-        mg.reorder(mf.view(1, s.M, s.NG_ffn), self.perm_f, self.cnt_f)
-        rec(1)
-        # B = 1: the attention reorder is also the flattened reorder of the GEMMs.
-        mg.gemm_mn(self.x, self.wq, s.G_attn, perm=self.perm_a[0], counts=self.cnt_a[0],
-                   out=self.q)
-        rec(2)
-        mg.attn(self.q.view(s.B, s.T, s.Hq, s.d), self.k, self.v, perm=self.perm_a,
-                counts=self.cnt_a, out=self.o)
-        rec(3)
-        mg.gemm_k(self.o.view(s.M, s.Hq * s.d), self.wo, s.G_attn, ma.view(s.M, s.Hk),
-                  out=self.y_attn)
-        rec(4)
-        mg.gemm_mn_swiglu(self.x, self.wg, self.wu, s.G_ffn, perm=self.perm_f[0],
-                          counts=self.cnt_f[0], out=self.h)
-        rec(5)
-        mg.gemm_k(self.h, self.wd, s.G_ffn, mf.view(s.M, s.NG_ffn), out=self.y_ffn)
-        rec(6)
+        if op == "reorder":
+            mg.reorder(ma, self.perm_a, self.cnt_a)
+            mg.reorder(mf.view(1, s.M, s.NG_ffn), self.perm_f, self.cnt_f)
+        elif op == "q_proj":
+            # B = 1: the attention reorder is also the flattened reorder of the GEMMs.
+            mg.gemm_mn(self.x, self.wq, s.G_attn, perm=self.perm_a[0], counts=self.cnt_a[0],
+                       out=self.q)
+        elif op == "attention":
+            mg.attn(self.q.view(s.B, s.T, s.Hq, s.d), self.k, self.v, perm=self.perm_a,
+                    counts=self.cnt_a, out=self.o)
+        elif op == "o_proj":
+            mg.gemm_k(self.o.view(s.M, s.Hq * s.d), self.wo, s.G_attn, ma.view(s.M, s.Hk),
+                      out=self.y_attn)
+        elif op == "gate_up_swiglu":
+            mg.gemm_mn_swiglu(self.x, self.wg, self.wu, s.G_ffn, perm=self.perm_f[0],
+                              counts=self.cnt_f[0], out=self.h)
+        elif op == "down_proj":
+            mg.gemm_k(self.h, self.wd, s.G_ffn, mf.view(s.M, s.NG_ffn), out=self.y_ffn)
+        else:
+            raise ValueError(f"unknown op {op!r}")
+
+    def step(self, which: str = "masked", events=None) -> None:
+        """One pass of the routed path; events[i] / events[i + 1] bracket op i."""
+        if events is not None:
+            events[0].record()
+        for i, op in enumerate(PREFILL_OPS):
+            self.run(op, which)
+            if events is not None:
+                events[i + 1].record()
 
 
 class DecodeLayer:
