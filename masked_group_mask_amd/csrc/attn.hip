@@ -32,7 +32,11 @@
 
 namespace wide {
 
-constexpr int kAq = 256;   // sorted query rows per workgroup (64 per wave)
+constexpr int kAWaves = 8;             // two waves per SIMD
+constexpr int kAQB = 2;                // 16-query blocks per wave
+constexpr int kAqw = 16 * kAQB;        // queries per wave
+constexpr int kAq = kAWaves * kAqw;    // sorted query rows per workgroup
+constexpr int kAThreads = 64 * kAWaves;
 constexpr int kAk = 64;    // keys per K/V stage
 constexpr int kAd = 128;   // head size
 constexpr int kAStage = kAk * kAd;  // bf16 elements of one K (or V) stage
@@ -68,7 +72,7 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const WIDE_LDS uint16_t *p) {
 // Prefill: workgroup = (query head h, sorted query tile, batch b); the tile is
 // 256 consecutive entries of perm[b][g], wave w owning entries 64w .. 64w+63.
 template <bool OUT_F32>
-__global__ __launch_bounds__(256) void attn_prefill_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kAThreads) void attn_prefill_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) uint16_t sK0[kAStage];
   __shared__ __attribute__((aligned(1024))) uint16_t sV0[kAStage];
   __shared__ __attribute__((aligned(1024))) uint16_t sK1[kAStage];
@@ -91,17 +95,17 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(AttnArgs a) {
   if (s0 >= cnt) return;  // level 0
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int c = lane % 16, q = lane / 16;
-  sPos[tid] = s0 + tid < cnt ? a.perm[((size_t)b * a.Hk + g) * a.Tq + s0 + tid] : -1;
+  if (tid < kAq) sPos[tid] = s0 + tid < cnt ? a.perm[((size_t)b * a.Hk + g) * a.Tq + s0 + tid] : -1;
   __syncthreads();
 
   const int delta = a.Tk - a.Tq;
   const int jmin = a.leftpad ? a.leftpad[b] : 0;
   const int nvalid = min(kAq, cnt - s0);
   const int wg_maxpos = sPos[nvalid - 1];
-  const int wlo = wave * 64, wvalid = max(0, min(64, nvalid - wlo));
+  const int wlo = wave * kAqw, wvalid = max(0, min(kAqw, nvalid - wlo));
   const int w_maxpos = wvalid > 0 ? sPos[wlo + wvalid - 1] : -1;
   // first row of the wave (or -1 when the wave has an empty row: forces masks)
-  const int w_minpos = wvalid == 64 ? sPos[wlo] : -1;
+  const int w_minpos = wvalid == kAqw ? sPos[wlo] : -1;
 
   // Key tiles [t0, t1).
   const int t0 = jmin / kAk;
@@ -113,10 +117,10 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(AttnArgs a) {
   // head dims 32 ds + 8 q .. +7.
   const size_t q_row = (size_t)a.Hq * kAd, kv_row = (size_t)a.Hk * kAd;
   const rsrc_t qr = make_rsrc(a.Q + (size_t)b * a.Tq * q_row, (uint64_t)a.Tq * q_row * 2);
-  u32x4 qf[4][4];
-  int qpos[4];
+  u32x4 qf[kAQB][4];
+  int qpos[kAQB];
 #pragma unroll
-  for (int qb = 0; qb < 4; ++qb) {
+  for (int qb = 0; qb < kAQB; ++qb) {
     qpos[qb] = sPos[wlo + qb * 16 + c];
 #pragma unroll
     for (int ds = 0; ds < 4; ++ds) {
@@ -125,20 +129,20 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(AttnArgs a) {
       qf[qb][ds] = buf_ld16(qr, off);
     }
   }
-  int jend[4];
+  int jend[kAQB];
 #pragma unroll
-  for (int qb = 0; qb < 4; ++qb) jend[qb] = a.causal ? qpos[qb] + delta + 1 : a.Tk;
+  for (int qb = 0; qb < kAQB; ++qb) jend[qb] = a.causal ? qpos[qb] + delta + 1 : a.Tk;
 
   // K/V stage loads: 16 instructions of 1 KB (4 rows) per operand per stage,
-  // wave w issuing j = w + 4i; lane l takes row 4j + l/16, position l % 16.
+  // wave w issuing j = w + W i; lane l takes row 4j + l/16, position l % 16.
   const rsrc_t kr = make_rsrc(a.K + (size_t)b * a.Tk * kv_row, (uint64_t)a.Tk * kv_row * 2);
   const rsrc_t vr = make_rsrc(a.V + (size_t)b * a.Tk * kv_row, (uint64_t)a.Tk * kv_row * 2);
   auto issue = [&](int t, WIDE_LDS uint16_t *sk, WIDE_LDS uint16_t *sv) {
     const int k0 = (t0 + t) * kAk;
     const bool live = t < nk;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int j = wave + 4 * i;
+    for (int i = 0; i < 16 / kAWaves; ++i) {
+      const int j = wave + kAWaves * i;
       const int r = 4 * j + lane / 16, p = lane % 16;
       const bool ok = live && k0 + r < a.Tk;
       const uint32_t base = (uint32_t)(((size_t)(k0 + r) * kv_row + (size_t)g * kAd) * 2);
@@ -147,24 +151,28 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(AttnArgs a) {
     }
   };
 
-  f32x4 o[8][4];
+  f32x4 o[8][kAQB];
 #pragma unroll
   for (int db = 0; db < 8; ++db)
 #pragma unroll
-    for (int qb = 0; qb < 4; ++qb) o[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-  float l[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int qb = 0; qb < kAQB; ++qb) o[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m[kAQB], l[kAQB];
+#pragma unroll
+  for (int qb = 0; qb < kAQB; ++qb) {
+    m[qb] = -INFINITY;
+    l[qb] = 0.f;
+  }
   const float sl2 = a.scale * kLog2e;
 
   auto compute = [&](int t, const WIDE_LDS uint16_t *sk, const WIDE_LDS uint16_t *sv) {
     const int k0 = (t0 + t) * kAk;
     if (k0 > w_maxpos + delta && a.causal) return;  // level 2: every row of the wave precedes the tile
     if (w_maxpos < 0) return;                        // the wave has no active row
-    f32x4 sc[4][4];
+    f32x4 sc[4][kAQB];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-      for (int qb = 0; qb < 4; ++qb) sc[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int qb = 0; qb < kAQB; ++qb) sc[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ds = 0; ds < 4; ++ds)
 #pragma unroll
@@ -172,7 +180,7 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(AttnArgs a) {
         const int r = kb * 16 + c;
         const u32x4 kf = *(const WIDE_LDS u32x4 *)(sk + r * kAd + (((ds * 4 + q) ^ k_swz(r)) * 8));
 #pragma unroll
-        for (int qb = 0; qb < 4; ++qb) sc[kb][qb] = mfma16x16x32(kf, qf[qb][ds], sc[kb][qb]);
+        for (int qb = 0; qb < kAQB; ++qb) sc[kb][qb] = mfma16x16x32(kf, qf[qb][ds], sc[kb][qb]);
       }
     // Element-wise masks only where some row of the wave may see a key
     // outside [jmin, jend): tiles that cross a causal diagonal, the left
@@ -181,7 +189,7 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(AttnArgs a) {
     const bool need_mask = k0 < jmin || k0 + kAk > a.Tk || (a.causal && k0 + kAk - 1 > w_minpos + delta);
     if (need_mask) {
 #pragma unroll
-      for (int qb = 0; qb < 4; ++qb)
+      for (int qb = 0; qb < kAQB; ++qb)
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
@@ -192,10 +200,10 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(AttnArgs a) {
           }
     }
     // Online softmax in the log2 domain: m is the running max of scale*log2e*s.
-    float alpha[4];
-    u32x4 pf[2][4];
+    float alpha[kAQB];
+    u32x4 pf[2][kAQB];
 #pragma unroll
-    for (int qb = 0; qb < 4; ++qb) {
+    for (int qb = 0; qb < kAQB; ++qb) {
       float mx = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
@@ -224,9 +232,12 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(AttnArgs a) {
                            pack_bf16x2(sc[2 * ks + 1][qb][2], sc[2 * ks + 1][qb][3])};
     }
     // Rescale the output only when some row's max moved (a wave-wide vote).
-    if (__ballot(alpha[0] != 1.f || alpha[1] != 1.f || alpha[2] != 1.f || alpha[3] != 1.f)) {
+    bool moved = false;
 #pragma unroll
-      for (int qb = 0; qb < 4; ++qb)
+    for (int qb = 0; qb < kAQB; ++qb) moved |= alpha[qb] != 1.f;
+    if (__ballot(moved)) {
+#pragma unroll
+      for (int qb = 0; qb < kAQB; ++qb)
 #pragma unroll
         for (int db = 0; db < 8; ++db) o[db][qb] *= alpha[qb];
     }
@@ -244,14 +255,14 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(AttnArgs a) {
         const u32x2 hi = lds_read_tr16(sv + r1 * kAd + ((chunk ^ v_swz(r1)) * 8) + 4 * (sidx % 2));
         const u32x4 vf = {lo[0], lo[1], hi[0], hi[1]};
 #pragma unroll
-        for (int qb = 0; qb < 4; ++qb) o[db][qb] = mfma16x16x32(vf, pf[ks][qb], o[db][qb]);
+        for (int qb = 0; qb < kAQB; ++qb) o[db][qb] = mfma16x16x32(vf, pf[ks][qb], o[db][qb]);
       }
   };
 
   WIDE_LDS uint16_t *k0s = (WIDE_LDS uint16_t *)sK0, *v0s = (WIDE_LDS uint16_t *)sV0;
   WIDE_LDS uint16_t *k1s = (WIDE_LDS uint16_t *)sK1, *v1s = (WIDE_LDS uint16_t *)sV1;
   WIDE_LDS uint16_t *k2s = (WIDE_LDS uint16_t *)sK2, *v2s = (WIDE_LDS uint16_t *)sV2;
-  constexpr int NL = 8;  // stage loads per wave
+  constexpr int NL = 2 * (16 / kAWaves);  // stage loads per wave (K and V)
   issue(0, k0s, v0s);
   issue(1, k1s, v1s);
   int t = 0;
@@ -276,7 +287,7 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(AttnArgs a) {
   // Normalise and scatter: lane holds head dims 16 db + 4 q .. +3 of query
   // 16 qb + c of the wave.
 #pragma unroll
-  for (int qb = 0; qb < 4; ++qb) {
+  for (int qb = 0; qb < kAQB; ++qb) {
     float z = l[qb];
     z += __shfl_xor(z, 16, kWave);
     z += __shfl_xor(z, 32, kWave);
@@ -545,9 +556,9 @@ int launch_attn(const AttnArgs &a, hipStream_t s) {
   }
   dim3 grid(a.Hq, (a.Tq + kAq - 1) / kAq, a.B);
   if (a.o_f32)
-    hipLaunchKernelGGL(attn_prefill_kernel<true>, grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL(attn_prefill_kernel<true>, grid, dim3(kAThreads), 0, s, a);
   else
-    hipLaunchKernelGGL(attn_prefill_kernel<false>, grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL(attn_prefill_kernel<false>, grid, dim3(kAThreads), 0, s, a);
   return check_launch();
 }
 
