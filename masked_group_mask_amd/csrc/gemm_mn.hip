@@ -255,6 +255,8 @@ int launch_gemm_mn(const MnArgs &a, hipStream_t s) {
     if (a.c_f32) launch_tiled<128, 4, true, true>(a, s); else launch_tiled<128, 4, true, false>(a, s);
   } else if (a.G % 256 == 0) {
     if (a.c_f32) launch_tiled<256, 8, false, true>(a, s); else launch_tiled<256, 8, false, false>(a, s);
+  } else if (a.G % 320 == 0) {
+    if (a.c_f32) launch_tiled<320, 8, false, true>(a, s); else launch_tiled<320, 8, false, false>(a, s);
   } else if (a.G % 128 == 0) {
     if (a.c_f32) launch_tiled<128, 4, false, true>(a, s); else launch_tiled<128, 4, false, false>(a, s);
   } else {

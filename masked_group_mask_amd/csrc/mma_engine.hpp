@@ -3,7 +3,7 @@
 //
 // A workgroup computes a 256 x BN tile of D = A * B^T (A rows are tokens, B
 // rows are output features) with W waves: W = 4 (one per SIMD, 2 x 2 waves,
-// BN = 64 or 128) or W = 8 (two per SIMD, 2 x 4 waves, BN = 256). Every wave
+// BN = 64 or 128) or W = 8 (two per SIMD, 2 x 4 waves, BN = 256 or 320). Every wave
 // owns a 128 x BN/(W/2) block and multiplies it with 16x16x32 bf16 MFMAs into
 // fp32 accumulators held in registers.
 //
@@ -38,7 +38,7 @@ constexpr int kGroupM = 4;  // m-tiles per raster group
 
 template <int BN, int W>
 struct Shape {
-  static_assert((W == 4 && (BN == 64 || BN == 128)) || (W == 8 && BN == 256), "unsupported tile");
+  static_assert((W == 4 && (BN == 64 || BN == 128)) || (W == 8 && (BN == 256 || BN == 320)), "unsupported tile");
   static constexpr int WAVES = W;
   static constexpr int THREADS = 64 * W;
   static constexpr int WNW = W / 2;         // waves along n (2 along m)
@@ -100,36 +100,46 @@ __device__ __forceinline__ int b_frag_row(int wn, int i) {
 }
 
 // One stage: two 32-deep halves, each reading its fragments then issuing the
-// MFMAs. `issue.prefetch(t)` runs after the first half's reads (the loader's
-// own LDS reads, consumed at the next step).
+// MFMAs. With more than 4 B fragments per wave (BN = 320) the A fragments are
+// read and used in AG = 2 groups, so fewer fragment registers are live at
+// once. `issue.prefetch(t)` runs after the first half's first reads (the
+// loader's own LDS reads, consumed at the next step).
+template <class S>
+constexpr int a_groups() { return S::FN > 4 ? 2 : 1; }
+
 template <class S, int BN, bool SPLIT, class Issue>
 __device__ __forceinline__ void compute_stage(const lds_u16 *sa, const lds_u16 *sb, Acc<S> &acc, int wm, int wn,
                                               int lane, Issue &issue, int t) {
+  constexpr int AG = a_groups<S>(), FMG = S::FM / AG;
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
-    Frag<S> f;
-#pragma unroll
-    for (int i = 0; i < S::FM; ++i) {
-      const int row = wm * S::TM + i * 16 + lane % 16;
-      f.a[i] = *(const WIDE_LDS u32x4 *)(sa + row * kBK + (((s * 4 + lane / 16) ^ swz(row)) * 8));
-    }
+    u32x4 fb[S::FN];
 #pragma unroll
     for (int i = 0; i < S::FN; ++i) {
       const int row = b_frag_row<S, BN, SPLIT>(wn, i) + lane % 16;
-      f.b[i] = *(const WIDE_LDS u32x4 *)(sb + row * kBK + (((s * 4 + lane / 16) ^ swz(row)) * 8));
+      fb[i] = *(const WIDE_LDS u32x4 *)(sb + row * kBK + (((s * 4 + lane / 16) ^ swz(row)) * 8));
     }
-    if (s == 0) issue.prefetch(t);
-    // D^T blocks: lane holds tile row (A) lane % 16 of fragment j and
-    // columns (B) 4 * (lane / 16) + v of fragment i.
 #pragma unroll
-    for (int i = 0; i < S::FN; ++i)
+    for (int jg = 0; jg < AG; ++jg) {
+      u32x4 fa[FMG];
 #pragma unroll
-      for (int j = 0; j < S::FM; ++j) acc[i][j] = mfma16x16x32(f.b[i], f.a[j], acc[i][j]);
+      for (int jj = 0; jj < FMG; ++jj) {
+        const int row = wm * S::TM + (jg * FMG + jj) * 16 + lane % 16;
+        fa[jj] = *(const WIDE_LDS u32x4 *)(sa + row * kBK + (((s * 4 + lane / 16) ^ swz(row)) * 8));
+      }
+      if (s == 0 && jg == 0) issue.prefetch(t);
+      // D^T blocks: lane holds tile row (A) lane % 16 of fragment j and
+      // columns (B) 4 * (lane / 16) + v of fragment i.
+#pragma unroll
+      for (int i = 0; i < S::FN; ++i)
+#pragma unroll
+        for (int jj = 0; jj < FMG; ++jj) acc[i][jg * FMG + jj] = mfma16x16x32(fb[i], fa[jj], acc[i][jg * FMG + jj]);
+    }
   }
 }
 
-// Scheduling groups of one half: NR LDS reads, then NV x (Q MFMAs, 1 stage
-// load), then the remaining MFMAs.
+// Scheduling groups of one A-fragment group: NR LDS reads, then NV x (Q
+// MFMAs, 1 stage load), then the remaining MFMAs.
 template <int NR, int NM, int NV>
 __device__ __forceinline__ void interleave_half() {
   __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);  // DS reads
@@ -152,14 +162,27 @@ __device__ __forceinline__ void interleave_half() {
 // the first half. The loader's own LDS reads come first in program order.
 template <class S, int EXTRA_DS>
 __device__ __forceinline__ void interleave() {
-  constexpr int NR = S::FM + S::FN, NM = S::FM * S::FN;
-  if constexpr (S::STAGES == 3) {
-    static_assert(S::NLOAD % 2 == 0, "stage loads must split over the two halves");
-    interleave_half<NR + EXTRA_DS, NM, S::NLOAD / 2>();
-    interleave_half<NR, NM, S::NLOAD / 2>();
+  constexpr int AG = a_groups<S>();
+  constexpr int NRB = S::FN, NRA = S::FM / AG, NMG = S::FN * S::FM / AG;
+  if constexpr (AG == 1) {
+    constexpr int NR = NRA + NRB, NM = NMG;
+    if constexpr (S::STAGES == 3) {
+      static_assert(S::NLOAD % 2 == 0, "stage loads must split over the two halves");
+      interleave_half<NR + EXTRA_DS, NM, S::NLOAD / 2>();
+      interleave_half<NR, NM, S::NLOAD / 2>();
+    } else {
+      interleave_half<NR + EXTRA_DS, NM, S::NLOAD>();
+      interleave_half<NR, NM, 0>();
+    }
   } else {
-    interleave_half<NR + EXTRA_DS, NM, S::NLOAD>();
-    interleave_half<NR, NM, 0>();
+    static_assert(AG == 2 && S::STAGES == 2, "A-fragment groups only with the 2-stage tile");
+    // first half: B + A group 0 (and the loader's reads), A group 1; loads
+    // spread over the first half; second half without loads
+    constexpr int NV0 = S::NLOAD / 2, NV1 = S::NLOAD - NV0;
+    interleave_half<NRB + NRA + EXTRA_DS, NMG, NV0>();
+    interleave_half<NRA, NMG, NV1>();
+    interleave_half<NRB + NRA, NMG, 0>();
+    interleave_half<NRA, NMG, 0>();
   }
 }
 
