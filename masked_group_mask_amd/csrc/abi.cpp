@@ -181,8 +181,8 @@ int wide_attn(const wide_bf16 *Q, const wide_bf16 *K, const wide_bf16 *V, void *
   // Per-sequence Q/K/V are addressed with 32-bit byte offsets.
   if ((uint64_t)Tq * Hq * d * 2u > 0x7fffffffull || (uint64_t)Tk * Hk * d * 2u > 0x7fffffffull)
     return WIDE_ERR_UNSUPPORTED;
-  // Decoding merges at most 1024 splits of 256 keys.
-  if (Tq == 1 && (Hq / Hk > 8 || Tk > 1024 * 256)) return WIDE_ERR_UNSUPPORTED;
+  // Decoding merges at most 4096 splits of 64 keys.
+  if (Tq == 1 && (Hq / Hk > 8 || Tk > 4096 * 64)) return WIDE_ERR_UNSUPPORTED;
   if (!device_ok()) return WIDE_ERR_NO_DEVICE;
   wide::AttnArgs a{};
   a.Q = Q;

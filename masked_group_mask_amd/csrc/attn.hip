@@ -306,7 +306,7 @@ __global__ __launch_bounds__(kAThreads) void attn_prefill_kernel(AttnArgs a) {
 // Decode: split-KV partials + merge.
 // ---------------------------------------------------------------------------
 
-constexpr int kDecKeys = 256;      // keys per split
+constexpr int kDecKeys = 64;       // keys per split (one wave)
 constexpr int kDecPart = kAd + 4;  // floats per partial: o[128], m, z (+pad)
 
 __device__ __forceinline__ bool group_active(const AttnArgs &a, int b, int g) {
@@ -314,28 +314,22 @@ __device__ __forceinline__ bool group_active(const AttnArgs &a, int b, int g) {
   return a.counts[(size_t)b * a.Hk + g] > 0;
 }
 
-// One split = 256 keys of one active (b, g), for all Hq/Hk heads of the
-// group. Lane l of a wave handles key quad slot l / 16 and head-dim chunk
-// l % 16 (8 values), so every 16-byte load of K and V covers whole lines of
-// four key rows; the 16 K loads and 16 V loads of a lane are issued before
-// any is used. Scores are reduced over the 16 lanes of a key, then the
-// split's max and sum per head come from an LDS reduction; the unnormalised
-// output is reduced over the key slots of a wave and then over the waves.
+// One split = 64 keys of one active (b, g), for all Hq/Hk heads of the group,
+// on one wave (many small independent waves keep every CU busy with loads in
+// flight; no LDS, no barrier). Lane l handles key slot l / 16 of each group of
+// four keys and head-dim chunk l % 16 (8 values), so every 16-byte load of K
+// and V covers whole lines of four key rows; the 16 K and 16 V loads of a lane
+// are issued before any is used. Scores are reduced over the 16 lanes of a
+// key; max, sum and the unnormalised output over the four key slots.
 template <int RMAX>
-__global__ __launch_bounds__(256) void attn_decode_split_kernel(AttnArgs a, int nsplit) {
-  constexpr int IT = kDecKeys / 16;  // key quads per wave (16 x 4 = 64 keys)
-  __shared__ float sP[RMAX][kDecKeys];
-  __shared__ float sRed[RMAX][4];
-  __shared__ float sO[4][RMAX][kAd];
-
+__global__ __launch_bounds__(kWave) void attn_decode_split_kernel(AttnArgs a, int nsplit) {
+  constexpr int IT = kDecKeys / 4;  // groups of four keys
   const int split = blockIdx.x;
   const int g = blockIdx.y;
   const int b = blockIdx.z;
   if (!group_active(a, b, g)) return;  // the group is off for this token: nothing is read
   const int rep = a.Hq / a.Hk;
-  const int tid = threadIdx.x;
-  const int lane = tid % kWave;
-  const int wave = tid / kWave;
+  const int lane = threadIdx.x;
   const int kq = lane / 16, dc = lane % 16;
   const int jmin = a.leftpad ? a.leftpad[b] : 0;
   const int j0 = split * kDecKeys;
@@ -345,7 +339,7 @@ __global__ __launch_bounds__(256) void attn_decode_split_kernel(AttnArgs a, int 
   const size_t q_row = (size_t)a.Hq * kAd, kv_row = (size_t)a.Hk * kAd;
 
   if (jlo >= jhi) {  // every key of the split is before the sequence's left padding
-    for (int i = tid; i < rep * kDecPart; i += 256) {
+    for (int i = lane; i < rep * kDecPart; i += kWave) {
       const int r = i / kDecPart, c = i % kDecPart;
       float *part = ws + (((size_t)b * a.Hq + g * rep + r) * nsplit + split) * kDecPart;
       part[c] = c == kAd ? -INFINITY : 0.f;
@@ -359,14 +353,14 @@ __global__ __launch_bounds__(256) void attn_decode_split_kernel(AttnArgs a, int 
   bool kok[IT];
 #pragma unroll
   for (int i = 0; i < IT; ++i) {
-    const int j = j0 + wave * (kDecKeys / 4) + i * 4 + kq;
+    const int j = j0 + i * 4 + kq;
     kok[i] = j >= jlo && j < jhi;
     const uint32_t off = kok[i] ? (uint32_t)((size_t)j * kv_row + g * kAd + dc * 8) * 2u : kOffNone;
     kreg[i] = buf_ld16(kr, off);
   }
 #pragma unroll
   for (int i = 0; i < IT; ++i) {
-    const int j = j0 + wave * (kDecKeys / 4) + i * 4 + kq;
+    const int j = j0 + i * 4 + kq;
     const uint32_t off = kok[i] ? (uint32_t)((size_t)j * kv_row + g * kAd + dc * 8) * 2u : kOffNone;
     vreg[i] = buf_ld16(vr, off);
   }
@@ -382,149 +376,147 @@ __global__ __launch_bounds__(256) void attn_decode_split_kernel(AttnArgs a, int 
 
   // Scores (log2 domain): dot over this lane's chunk, then over the 16 lanes of the key.
   const float sl2 = a.scale * kLog2e;
+  float sc[IT][RMAX];
 #pragma unroll
   for (int i = 0; i < IT; ++i) {
-    float sc[RMAX];
 #pragma unroll
     for (int r = 0; r < RMAX; ++r) {
       float acc = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc = fmaf((e % 2) ? bf_hi(kreg[i][e / 2]) : bf_lo(kreg[i][e / 2]), qv[r][e], acc);
-      sc[r] = acc;
-    }
 #pragma unroll
-    for (int r = 0; r < RMAX; ++r) {
-      if (r >= rep) break;
-#pragma unroll
-      for (int o = 8; o >= 1; o >>= 1) sc[r] += __shfl_xor(sc[r], o, kWave);
-    }
-    if (dc == 0) {
-      const int jl = wave * (kDecKeys / 4) + i * 4 + kq;
-#pragma unroll
-      for (int r = 0; r < RMAX; ++r)
-        if (r < rep) sP[r][jl] = kok[i] ? sc[r] * sl2 : -INFINITY;
+      for (int o = 8; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, kWave);
+      sc[i][r] = kok[i] ? acc * sl2 : -INFINITY;
     }
   }
-  __syncthreads();
-  // Split max and sum per head: thread t owns key t.
+  // Per head: max and sum over the split (16 keys per lane, then the 4 key slots).
   float mx[RMAX], zs[RMAX];
 #pragma unroll
   for (int r = 0; r < RMAX; ++r) {
-    float v = r < rep ? sP[r][tid] : -INFINITY;
+    float m = -INFINITY;
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-    if (lane == 0) sRed[r][wave] = v;
-  }
-  __syncthreads();
+    for (int i = 0; i < IT; ++i) m = fmaxf(m, sc[i][r]);
+    m = fmaxf(m, __shfl_xor(m, 16, kWave));
+    m = fmaxf(m, __shfl_xor(m, 32, kWave));
+    mx[r] = m;  // finite: the split has a valid key
+    float z = 0.f;
 #pragma unroll
-  for (int r = 0; r < RMAX; ++r) {
-    mx[r] = fmaxf(fmaxf(sRed[r][0], sRed[r][1]), fmaxf(sRed[r][2], sRed[r][3]));
-    if (r < rep) {
-      const float p = exp2f(sP[r][tid] - mx[r]);  // -inf -> 0; the split has a valid key
-      sP[r][tid] = p;
-      zs[r] = p;
-    } else {
-      zs[r] = 0.f;
+    for (int i = 0; i < IT; ++i) {
+      const float pv = exp2_fast(sc[i][r] - m);  // -inf -> 0
+      sc[i][r] = pv;
+      z += pv;
     }
+    z += __shfl_xor(z, 16, kWave);
+    z += __shfl_xor(z, 32, kWave);
+    zs[r] = z;
   }
-  __syncthreads();
-#pragma unroll
-  for (int r = 0; r < RMAX; ++r) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) zs[r] += __shfl_xor(zs[r], o, kWave);
-  }
-  if (lane == 0)
-#pragma unroll
-    for (int r = 0; r < RMAX; ++r) sRed[r][wave] = zs[r];
-
-  // Unnormalised output for this lane's chunk, over this wave's keys.
-  float o[RMAX][8];
-#pragma unroll
-  for (int r = 0; r < RMAX; ++r)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) o[r][e] = 0.f;
-#pragma unroll
-  for (int i = 0; i < IT; ++i) {
-    const int jl = wave * (kDecKeys / 4) + i * 4 + kq;
-#pragma unroll
-    for (int r = 0; r < RMAX; ++r) {
-      if (r >= rep) break;
-      const float p = sP[r][jl];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) o[r][e] = fmaf(p, (e % 2) ? bf_hi(vreg[i][e / 2]) : bf_lo(vreg[i][e / 2]), o[r][e]);
-    }
-  }
+  // Unnormalised output for this lane's 8 head dims, summed over the 4 key slots.
 #pragma unroll
   for (int r = 0; r < RMAX; ++r) {
     if (r >= rep) break;
+    float o[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = 0.f;
+#pragma unroll
+    for (int i = 0; i < IT; ++i)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = fmaf(sc[i][r], (e % 2) ? bf_hi(vreg[i][e / 2]) : bf_lo(vreg[i][e / 2]), o[e]);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      o[r][e] += __shfl_xor(o[r][e], 16, kWave);
-      o[r][e] += __shfl_xor(o[r][e], 32, kWave);
+      o[e] += __shfl_xor(o[e], 16, kWave);
+      o[e] += __shfl_xor(o[e], 32, kWave);
     }
-    if (kq == 0)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) sO[wave][r][dc * 8 + e] = o[r][e];
-  }
-  __syncthreads();
-  for (int i = tid; i < rep * kAd; i += 256) {
-    const int r = i / kAd, d = i % kAd;
     float *part = ws + (((size_t)b * a.Hq + g * rep + r) * nsplit + split) * kDecPart;
-    part[d] = sO[0][r][d] + sO[1][r][d] + sO[2][r][d] + sO[3][r][d];
-    if (d == 0) {
+    if (kq == 0) {
+      *reinterpret_cast<f32x4 *>(part + dc * 8) = f32x4{o[0], o[1], o[2], o[3]};
+      *reinterpret_cast<f32x4 *>(part + dc * 8 + 4) = f32x4{o[4], o[5], o[6], o[7]};
+    }
+    if (lane == 0) {
       part[kAd] = mx[r];
-      part[kAd + 1] = sRed[r][0] + sRed[r][1] + sRed[r][2] + sRed[r][3];
+      part[kAd + 1] = zs[r];
     }
   }
 }
 
-// Merge of the splits of one (b, h): weights 2^(m_s - max) from the split
-// maxima (staged in LDS), then the weighted sum of the partial outputs with
-// the reads unrolled.
+// Merge of the splits of one (b, h) and 16 of its head dims (8 workgroups
+// per head): the split maxima are staged in LDS, the weights 2^(m_s - max)
+// and the total sum come from block reductions, and the weighted sum of the
+// partial outputs is split over 16 groups of splits, then reduced in LDS.
+constexpr int kMergeThreads = 256;
+constexpr int kMergeDims = 16;
+
+__device__ __forceinline__ float block_max(float v, float *red) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  if (threadIdx.x % kWave == 0) red[threadIdx.x / kWave] = v;
+  __syncthreads();
+  v = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  __syncthreads();
+  return v;
+}
+
+__device__ __forceinline__ float block_sum(float v, float *red) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  if (threadIdx.x % kWave == 0) red[threadIdx.x / kWave] = v;
+  __syncthreads();
+  v = (red[0] + red[1]) + (red[2] + red[3]);
+  __syncthreads();
+  return v;
+}
+
 template <bool OUT_F32>
-__global__ __launch_bounds__(kAd) void attn_decode_merge_kernel(AttnArgs a, int nsplit) {
-  __shared__ float sW[1024];
-  __shared__ float sZ;
+__global__ __launch_bounds__(kMergeThreads) void attn_decode_merge_kernel(AttnArgs a, int nsplit) {
+  __shared__ float sW[4096];  // split weights (at most 4096 splits)
+  __shared__ float sRed[4];
+  __shared__ float sPart[kMergeThreads / kMergeDims][kMergeDims + 1];
   const int h = blockIdx.x;
   const int b = blockIdx.y;
+  const int d0 = blockIdx.z * kMergeDims;
   const int rep = a.Hq / a.Hk;
   if (!group_active(a, b, h / rep)) return;
-  const int d = threadIdx.x;
+  const int tid = threadIdx.x;
   const float *ws = reinterpret_cast<const float *>(a.workspace) + ((size_t)b * a.Hq + h) * nsplit * kDecPart;
-  // split maxima -> LDS, global max, weights
-  for (int s = d; s < nsplit; s += kAd) sW[s] = ws[s * kDecPart + kAd];
-  __syncthreads();
-  float M = -INFINITY;
-  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, sW[s]);
-  __syncthreads();
-  for (int s = d; s < nsplit; s += kAd) {
+  float mloc = -INFINITY;
+  for (int s = tid; s < nsplit; s += kMergeThreads) {
+    const float m = ws[(size_t)s * kDecPart + kAd];
+    sW[s] = m;
+    mloc = fmaxf(mloc, m);
+  }
+  const float M = block_max(mloc, sRed);
+  float zloc = 0.f;
+  for (int s = tid; s < nsplit; s += kMergeThreads) {
     const float m = sW[s];
-    sW[s] = (M == -INFINITY || m == -INFINITY) ? 0.f : exp2f(m - M);
+    const float w = (M == -INFINITY || m == -INFINITY) ? 0.f : exp2f(m - M);
+    sW[s] = w;
+    zloc = fmaf(w, ws[(size_t)s * kDecPart + kAd + 1], zloc);
   }
-  __syncthreads();
-  if (d == 0) {
-    float Z = 0.f;
-    for (int s = 0; s < nsplit; ++s) Z += sW[s] * ws[s * kDecPart + kAd + 1];
-    sZ = Z;
-  }
+  const float Z = block_sum(zloc, sRed);  // also orders the sW writes before the reads below
+  const int dl = tid % kMergeDims, sg = tid / kMergeDims;
+  constexpr int NG = kMergeThreads / kMergeDims;
   float o = 0.f;
-  int s = 0;
-  for (; s + 8 <= nsplit; s += 8) {
+  int s = sg;
+  for (; s + 7 * NG < nsplit; s += 8 * NG) {
     float v[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = ws[(s + u) * kDecPart + d];
+    for (int u = 0; u < 8; ++u) v[u] = ws[(size_t)(s + u * NG) * kDecPart + d0 + dl];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) o = fmaf(sW[s + u], v[u], o);
+    for (int u = 0; u < 8; ++u) o = fmaf(sW[s + u * NG], v[u], o);
   }
-  for (; s < nsplit; ++s) o = fmaf(sW[s], ws[s * kDecPart + d], o);
+  for (; s < nsplit; s += NG) o = fmaf(sW[s], ws[(size_t)s * kDecPart + d0 + dl], o);
+  sPart[sg][dl] = o;
   __syncthreads();
-  const float Z = sZ;
-  const float out = Z > 0.f ? o / Z : 0.f;
-  const size_t idx = (size_t)b * a.Hq * kAd + (size_t)h * kAd + d;
-  if (OUT_F32)
-    reinterpret_cast<float *>(a.O)[idx] = out;
-  else
-    reinterpret_cast<uint16_t *>(a.O)[idx] = f2bf(out);
+  if (tid < kMergeDims) {
+    float t = 0.f;
+#pragma unroll
+    for (int g = 0; g < NG; ++g) t += sPart[g][tid];
+    const float out = Z > 0.f ? t / Z : 0.f;
+    const size_t idx = (size_t)b * a.Hq * kAd + (size_t)h * kAd + d0 + tid;
+    if (OUT_F32)
+      reinterpret_cast<float *>(a.O)[idx] = out;
+    else
+      reinterpret_cast<uint16_t *>(a.O)[idx] = f2bf(out);
+  }
 }
 
 size_t attn_workspace_bytes(int64_t B, int64_t Tq, int64_t Tk, int64_t Hq, int64_t Hk, int64_t d) {
@@ -541,17 +533,18 @@ int launch_attn(const AttnArgs &a, hipStream_t s) {
     const dim3 grid(nsplit, a.Hk, a.B);
     const int rep = a.Hq / a.Hk;
     if (rep == 1)
-      hipLaunchKernelGGL(attn_decode_split_kernel<1>, grid, dim3(256), 0, s, a, nsplit);
+      hipLaunchKernelGGL(attn_decode_split_kernel<1>, grid, dim3(kWave), 0, s, a, nsplit);
     else if (rep == 2)
-      hipLaunchKernelGGL(attn_decode_split_kernel<2>, grid, dim3(256), 0, s, a, nsplit);
+      hipLaunchKernelGGL(attn_decode_split_kernel<2>, grid, dim3(kWave), 0, s, a, nsplit);
     else if (rep <= 4)
-      hipLaunchKernelGGL(attn_decode_split_kernel<4>, grid, dim3(256), 0, s, a, nsplit);
+      hipLaunchKernelGGL(attn_decode_split_kernel<4>, grid, dim3(kWave), 0, s, a, nsplit);
     else
-      hipLaunchKernelGGL(attn_decode_split_kernel<8>, grid, dim3(256), 0, s, a, nsplit);
+      hipLaunchKernelGGL(attn_decode_split_kernel<8>, grid, dim3(kWave), 0, s, a, nsplit);
+    const dim3 mgrid(a.Hq, a.B, kAd / kMergeDims);
     if (a.o_f32)
-      hipLaunchKernelGGL(attn_decode_merge_kernel<true>, dim3(a.Hq, a.B), dim3(kAd), 0, s, a, nsplit);
+      hipLaunchKernelGGL(attn_decode_merge_kernel<true>, mgrid, dim3(kMergeThreads), 0, s, a, nsplit);
     else
-      hipLaunchKernelGGL(attn_decode_merge_kernel<false>, dim3(a.Hq, a.B), dim3(kAd), 0, s, a, nsplit);
+      hipLaunchKernelGGL(attn_decode_merge_kernel<false>, mgrid, dim3(kMergeThreads), 0, s, a, nsplit);
     return check_launch();
   }
   dim3 grid(a.Hq, (a.Tq + kAq - 1) / kAq, a.B);
