@@ -155,7 +155,7 @@ def main():
     ap.add_argument("--workload", default="qwen14b_prefill")
     ap.add_argument("--sparsity", type=float, default=0.5)
     ap.add_argument("--g-ffn", type=int, default=128)
-    ap.add_argument("--cpu-rows", type=int, default=4096)
+    ap.add_argument("--cpu-rows", type=int, default=8192)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-decode", action="store_true")

@@ -116,6 +116,28 @@ def test_gemm_mn_fp32(M, N, K, G):
     assert (out.cpu().numpy().view(np.uint32)[off] == 0).all(), "inactive entries were written"
 
 
+@pytest.mark.parametrize("G", [128, 640])
+def test_gemm_mn_strided_operands(G):
+    """Leading dimensions larger than the rows: A and B padded, and an odd ldc
+    (ldc = N + 1) that rules out vector stores; the padding stays untouched."""
+    M, N, K = 300, 2 * G, 320
+    A = wl.random_bf16(60, (M, K))
+    B = wl.random_bf16(61, (N, K), 0.05)
+    mask = wl.random_mask(62, (M, N // G), 0.5)
+    say("gemm_mn strided", M, N, K, G)
+    Ap = torch.zeros((M, K + 8), dtype=torch.bfloat16, device="cuda")
+    Bp = torch.zeros((N, K + 16), dtype=torch.bfloat16, device="cuda")
+    Ap[:, :K] = to_dev(A, torch)
+    Bp[:, :K] = to_dev(B, torch)
+    Cp = torch.zeros((M, N + 1), dtype=torch.float32, device="cuda")
+    perm, counts = W().reorder(to_dev(mask[None], torch))
+    W().gemm_mn(Ap[:, :K], Bp[:, :K], G, perm=perm[0], counts=counts[0], out=Cp[:, :N])
+    torch.cuda.synchronize()
+    got = Cp.cpu().numpy()
+    check_gemm(got[:, :N], ref.gemm_mn(A, B, mask, G), "gemm_mn strided")
+    assert (got[:, N] == 0).all(), "the padding column was written"
+
+
 @pytest.mark.parametrize("p", [0.0, 1.0])
 def test_gemm_mn_all_or_nothing(p):
     M, N, K, G = 200, 256, 128, 128
@@ -225,6 +247,21 @@ def test_gemm_k_beta_and_determinism():
     want = ref.gemm_k(A, B, mask, G)
     check_gemm(f32_of(out), want + C0, "gemm_k beta=1")
     assert torch.equal(r1, r2), "GEMM-K is not bitwise reproducible"
+
+
+def test_gemm_k_leftover_tiles_beta():
+    """272 tiles of 256 x 256 on 256 CUs: the 16 left over run as 32 half-width
+    workgroups in a second launch; beta = 1 must hold in both launches."""
+    M, N, K, G = 4352, 4096, 256, 128
+    A = wl.random_bf16(70, (M, K))
+    B = wl.random_bf16(71, (N, K), 0.05)
+    mask = wl.random_mask(72, (M, K // G), 0.5)
+    C0 = ref.from_bf16(wl.random_bf16(73, (M, N)).view(np.uint16)).astype(np.float32)
+    say("gemm_k leftover tiles beta=1")
+    out = to_dev(C0, torch)
+    W().gemm_k(to_dev(A, torch), to_dev(B, torch), G, to_dev(mask, torch), out=out, beta=1)
+    torch.cuda.synchronize()
+    check_gemm(f32_of(out), ref.gemm_k(A, B, mask, G) + C0, "gemm_k leftover tiles beta=1")
 
 
 @pytest.mark.parametrize("p", [0.0, 1.0])
