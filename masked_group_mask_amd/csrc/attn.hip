@@ -79,6 +79,8 @@ __global__ __launch_bounds__(kAThreads) void attn_prefill_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) uint16_t sV1[kAStage];
   __shared__ __attribute__((aligned(1024))) uint16_t sK2[kAStage];
   __shared__ __attribute__((aligned(1024))) uint16_t sV2[kAStage];
+  __shared__ __attribute__((aligned(1024))) uint16_t sK3[kAStage];
+  __shared__ __attribute__((aligned(1024))) uint16_t sV3[kAStage];
   __shared__ int sPos[kAq];
 
   // Heads of one KV group run on one XCD (they stream the same K/V); the
@@ -262,26 +264,32 @@ __global__ __launch_bounds__(kAThreads) void attn_prefill_kernel(AttnArgs a) {
   WIDE_LDS uint16_t *k0s = (WIDE_LDS uint16_t *)sK0, *v0s = (WIDE_LDS uint16_t *)sV0;
   WIDE_LDS uint16_t *k1s = (WIDE_LDS uint16_t *)sK1, *v1s = (WIDE_LDS uint16_t *)sV1;
   WIDE_LDS uint16_t *k2s = (WIDE_LDS uint16_t *)sK2, *v2s = (WIDE_LDS uint16_t *)sV2;
-  constexpr int NL = 2 * (16 / kAWaves);  // stage loads per wave (K and V)
+  WIDE_LDS uint16_t *k3s = (WIDE_LDS uint16_t *)sK3, *v3s = (WIDE_LDS uint16_t *)sV3;
+  // A ring of 4 stages with one barrier per pair of key tiles: at the barrier
+  // of pair (t, t+1) both stages have landed for every wave and every wave is
+  // done with the previous pair, whose two buffers then receive stages t+2 and
+  // t+3. Half as many barriers as one per tile, with the same two tiles of
+  // latency cover, and the waves drift apart within a pair (fewer coinciding
+  // stalls on the two waves that share a SIMD).
   issue(0, k0s, v0s);
   issue(1, k1s, v1s);
   int t = 0;
-#define WIDE_ATTN_STEP(CK, CV, NK, NV) \
-  {                                    \
-    WIDE_WAIT_VM_LGKM0(NL);            \
-    WIDE_BARRIER();                    \
-    issue(t + 2, NK, NV);              \
-    compute(t, CK, CV);                \
-    ++t;                               \
+#define WIDE_ATTN_PAIR(CK0, CV0, CK1, CV1, NK0, NV0, NK1, NV1) \
+  {                                                            \
+    WIDE_WAIT_VM_LGKM0(0);                                     \
+    WIDE_BARRIER();                                            \
+    issue(t + 2, NK0, NV0);                                    \
+    issue(t + 3, NK1, NV1);                                    \
+    compute(t, CK0, CV0);                                      \
+    if (t + 1 < nk) compute(t + 1, CK1, CV1);                  \
+    t += 2;                                                    \
   }
-  for (; t + 3 <= nk;) {
-    WIDE_ATTN_STEP(k0s, v0s, k2s, v2s)
-    WIDE_ATTN_STEP(k1s, v1s, k0s, v0s)
-    WIDE_ATTN_STEP(k2s, v2s, k1s, v1s)
+  while (t < nk) {
+    WIDE_ATTN_PAIR(k0s, v0s, k1s, v1s, k2s, v2s, k3s, v3s)
+    if (t >= nk) break;
+    WIDE_ATTN_PAIR(k2s, v2s, k3s, v3s, k0s, v0s, k1s, v1s)
   }
-  if (t < nk) WIDE_ATTN_STEP(k0s, v0s, k2s, v2s)
-  if (t < nk) WIDE_ATTN_STEP(k1s, v1s, k0s, v0s)
-#undef WIDE_ATTN_STEP
+#undef WIDE_ATTN_PAIR
   WIDE_WAIT_VM_LGKM0(0);
 
   // Normalise and scatter: lane holds head dims 16 db + 4 q .. +3 of query
