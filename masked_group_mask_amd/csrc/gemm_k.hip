@@ -102,6 +102,7 @@ __device__ __forceinline__ bool build_bits(const KArgs &a, int m0, WIDE_LDS uint
 template <class S>
 struct KLoader {
   static constexpr int kDsReads = 2;
+  static constexpr int kLoadGap = 0;
   static constexpr int AHEAD = S::STAGES - 1;  // stages in flight ahead of the one multiplied
   rsrc_t ar, br, none;
   uint32_t aoff[S::AI], boff[S::BI];

@@ -54,6 +54,9 @@ __device__ __forceinline__ void store_out4(void *C, size_t idx, const f32x4 &v, 
 template <class S, bool SPLIT>
 struct MnLoader {
   static constexpr int kDsReads = 0;
+  // SwiGLU tiles run faster with the next stage's loads packed at the start
+  // of the step; plain tiles with them spread (both measured)
+  static constexpr int kLoadGap = SPLIT ? 1 : 0;
   rsrc_t ar, br0, br1, none;
   uint32_t aoff[S::AI], boff[S::BI];
   int nk, K, wave;

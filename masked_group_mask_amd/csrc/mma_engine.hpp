@@ -139,12 +139,13 @@ __device__ __forceinline__ void compute_stage(const lds_u16 *sa, const lds_u16 *
 }
 
 // Scheduling groups of one A-fragment group: NR LDS reads, then NV x (Q
-// MFMAs, 1 stage load), then the remaining MFMAs.
-template <int NR, int NM, int NV>
+// MFMAs, 1 stage load), then the remaining MFMAs. Q is NM / NV (loads spread
+// evenly), capped at QMAX when QMAX > 0 (loads packed towards the start).
+template <int NR, int NM, int NV, int QMAX = 0>
 __device__ __forceinline__ void interleave_half() {
   __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);  // DS reads
   if constexpr (NV > 0) {
-    constexpr int Q = NM / NV;
+    constexpr int Q = (QMAX > 0 && QMAX < NM / NV) ? QMAX : NM / NV;
     static_assert(Q >= 1, "more stage loads than MFMAs in a half");
 #pragma unroll
     for (int k = 0; k < NV; ++k) {
@@ -159,8 +160,9 @@ __device__ __forceinline__ void interleave_half() {
 
 // Order of one step. 3 stages: the stage loads are spread over both halves.
 // 2 stages: the next stage is needed at the next step, so its loads all go in
-// the first half. The loader's own LDS reads come first in program order.
-template <class S, int EXTRA_DS>
+// the first half, at most QMAX MFMAs apart when QMAX > 0. The loader's own LDS
+// reads come first in program order.
+template <class S, int EXTRA_DS, int QMAX>
 __device__ __forceinline__ void interleave() {
   constexpr int AG = a_groups<S>();
   constexpr int NRB = S::FN, NRA = S::FM / AG, NMG = S::FN * S::FM / AG;
@@ -171,7 +173,7 @@ __device__ __forceinline__ void interleave() {
       interleave_half<NR + EXTRA_DS, NM, S::NLOAD / 2>();
       interleave_half<NR, NM, S::NLOAD / 2>();
     } else {
-      interleave_half<NR + EXTRA_DS, NM, S::NLOAD>();
+      interleave_half<NR + EXTRA_DS, NM, S::NLOAD, QMAX>();
       interleave_half<NR, NM, 0>();
     }
   } else {
@@ -179,8 +181,8 @@ __device__ __forceinline__ void interleave() {
     // first half: B + A group 0 (and the loader's reads), A group 1; loads
     // spread over the first half; second half without loads
     constexpr int NV0 = S::NLOAD / 2, NV1 = S::NLOAD - NV0;
-    interleave_half<NRB + NRA + EXTRA_DS, NMG, NV0>();
-    interleave_half<NRA, NMG, NV1>();
+    interleave_half<NRB + NRA + EXTRA_DS, NMG, NV0, QMAX>();
+    interleave_half<NRA, NMG, NV1, QMAX>();
     interleave_half<NRB + NRA, NMG, 0>();
     interleave_half<NRA, NMG, 0>();
   }
@@ -190,8 +192,9 @@ __device__ __forceinline__ void interleave() {
 // wave for stage t into (sa, sb), out of range when t >= nk, and no other
 // vector-memory loads; `issue.prefetch(t)` (called while stage t is
 // multiplied) may issue Issue::kDsReads LDS reads whose results the next issue
-// uses. The stage buffers are distinct LDS objects so the compiler can tell
-// them apart when it places its own waits.
+// uses; Issue::kLoadGap caps the MFMAs between two stage loads of the 2-stage
+// tile (0: spread evenly). The stage buffers are distinct LDS objects so the
+// compiler can tell them apart when it places its own waits.
 //
 // 3 stages: stage t sits in buffer t % 3; after the barrier of step t every
 // wave is done with buffer (t + 2) % 3, which then receives stage t + 2.
@@ -208,7 +211,7 @@ __device__ __forceinline__ void mainloop(int nk, Issue &issue, lds_u16 *a0, lds_
     WIDE_BARRIER();                                                     \
     issue(t + AHEAD, NA, NB);                                           \
     compute_stage<S, BN, SPLIT>(CA, CB, acc, wm, wn, lane, issue, t);   \
-    interleave<S, Issue::kDsReads>();                                   \
+    interleave<S, Issue::kDsReads, Issue::kLoadGap>();                  \
     __builtin_amdgcn_sched_barrier(0);                                  \
     ++t;                                                                \
   }
