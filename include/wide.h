@@ -169,7 +169,7 @@ int wide_gemm_k(const wide_bf16 *A, int64_t lda, const wide_bf16 *B, int64_t ldb
  *     bytes (0 bytes for Tq > 1); may be NULL when that is 0.
  * Requirements: Hq % Hk == 0; Tk >= Tq >= 1; 16-byte aligned Q, K, V, O;
  * O must not overlap Q, K or V. WIDE_ERR_UNSUPPORTED unless d == 128, one
- * sequence's Q and K each span less than 2^31 bytes, and (decoding) Hq/Hk <= 8
+ * sequence's Q and K each span less than 2^31 bytes, and (decoding) Hq/Hk <= 16
  * and Tk <= 262144.
  */
 int wide_attn(const wide_bf16 *Q, const wide_bf16 *K, const wide_bf16 *V, void *O,

@@ -182,7 +182,7 @@ int wide_attn(const wide_bf16 *Q, const wide_bf16 *K, const wide_bf16 *V, void *
   if ((uint64_t)Tq * Hq * d * 2u > 0x7fffffffull || (uint64_t)Tk * Hk * d * 2u > 0x7fffffffull)
     return WIDE_ERR_UNSUPPORTED;
   // Decoding merges at most 4096 splits of 64 keys.
-  if (Tq == 1 && (Hq / Hk > 8 || Tk > 4096 * 64)) return WIDE_ERR_UNSUPPORTED;
+  if (Tq == 1 && (Hq / Hk > 16 || Tk > 4096 * 64)) return WIDE_ERR_UNSUPPORTED;
   if (!device_ok()) return WIDE_ERR_NO_DEVICE;
   wide::AttnArgs a{};
   a.Q = Q;

@@ -322,23 +322,27 @@ __device__ __forceinline__ bool group_active(const AttnArgs &a, int b, int g) {
   return a.counts[(size_t)b * a.Hk + g] > 0;
 }
 
-// One split = 64 keys of one active (b, g), for all Hq/Hk heads of the group,
-// on one wave (many small independent waves keep every CU busy with loads in
-// flight; no LDS, no barrier). Lane l handles key slot l / 16 of each group of
-// four keys and head-dim chunk l % 16 (8 values), so every 16-byte load of K
-// and V covers whole lines of four key rows; the 16 K and 16 V loads of a lane
-// are issued before any is used. Scores are reduced over the 16 lanes of a
-// key; max, sum and the unnormalised output over the four key slots.
-template <int RMAX>
+// One split = 64 keys of one active (b, g) on one wave, for all Hq/Hk heads of
+// the group at once (they share the keys), on the matrix cores with the heads
+// as the 16 columns (unused columns hold zero queries and are never written):
+//   S^T = K Q^T: the K fragments (16 keys x 32 head dims) are loaded straight
+//     into registers, lane l taking key 16 t + l % 16 and the 16-byte chunk
+//     4 ds + l / 16 of its row, so every load covers 64 contiguous bytes of 16
+//     keys; Q^T uses the same chunk order;
+//   O^T = V^T P^T: V goes to LDS with direct loads (prefill stage layout) and
+//     its transposed fragments come from transposing reads; P^T is the score
+//     registers themselves, packed to bf16.
+// A lane holds the scores of one head for 16 keys, so the split's max and sum
+// take two cross-lane steps. All loads are issued before any is used.
 __global__ __launch_bounds__(kWave) void attn_decode_split_kernel(AttnArgs a, int nsplit) {
-  constexpr int IT = kDecKeys / 4;  // groups of four keys
+  __shared__ __attribute__((aligned(1024))) uint16_t sV[kDecKeys * kAd];
   const int split = blockIdx.x;
   const int g = blockIdx.y;
   const int b = blockIdx.z;
   if (!group_active(a, b, g)) return;  // the group is off for this token: nothing is read
   const int rep = a.Hq / a.Hk;
   const int lane = threadIdx.x;
-  const int kq = lane / 16, dc = lane % 16;
+  const int q = lane / 16, c16 = lane % 16;
   const int jmin = a.leftpad ? a.leftpad[b] : 0;
   const int j0 = split * kDecKeys;
   const int jlo = max(j0, jmin);
@@ -357,91 +361,96 @@ __global__ __launch_bounds__(kWave) void attn_decode_split_kernel(AttnArgs a, in
 
   const rsrc_t kr = make_rsrc(a.K + (size_t)b * a.Tk * kv_row, (uint64_t)a.Tk * kv_row * 2);
   const rsrc_t vr = make_rsrc(a.V + (size_t)b * a.Tk * kv_row, (uint64_t)a.Tk * kv_row * 2);
-  u32x4 kreg[IT], vreg[IT];
-  bool kok[IT];
+  WIDE_LDS uint16_t *sv = (WIDE_LDS uint16_t *)sV;
+  // V: 16 instructions of 1 KB, instruction j covering keys 4 j .. 4 j + 3.
 #pragma unroll
-  for (int i = 0; i < IT; ++i) {
-    const int j = j0 + i * 4 + kq;
-    kok[i] = j >= jlo && j < jhi;
-    const uint32_t off = kok[i] ? (uint32_t)((size_t)j * kv_row + g * kAd + dc * 8) * 2u : kOffNone;
-    kreg[i] = buf_ld16(kr, off);
+  for (int j = 0; j < 16; ++j) {
+    const int r = 4 * j + lane / 16, p = lane % 16;
+    const bool ok = j0 + r >= jlo && j0 + r < jhi;
+    const uint32_t base = (uint32_t)(((size_t)(j0 + r) * kv_row + (size_t)g * kAd) * 2);
+    eng::load_lds(vr, (eng::lds_u16 *)(sv + j * 512), ok ? base + (uint32_t)((p ^ v_swz(r)) * 16) : kOffNone, 0u);
   }
+  // K fragments of the four 16-key tiles.
+  u32x4 kf[4][4];
 #pragma unroll
-  for (int i = 0; i < IT; ++i) {
-    const int j = j0 + i * 4 + kq;
-    const uint32_t off = kok[i] ? (uint32_t)((size_t)j * kv_row + g * kAd + dc * 8) * 2u : kOffNone;
-    vreg[i] = buf_ld16(vr, off);
-  }
-  // This lane's 8 query values for every head of the group.
-  const uint16_t *Qb = a.Q + (size_t)b * q_row + (size_t)g * rep * kAd + dc * 8;
-  float qv[RMAX][8];
+  for (int t = 0; t < 4; ++t) {
+    const int j = j0 + 16 * t + c16;
+    const bool ok = j >= jlo && j < jhi;
 #pragma unroll
-  for (int r = 0; r < RMAX; ++r) {
-    const u32x4 w = r < rep ? ld16(Qb + r * kAd) : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int e = 0; e < 8; ++e) qv[r][e] = (e % 2) ? bf_hi(w[e / 2]) : bf_lo(w[e / 2]);
-  }
-
-  // Scores (log2 domain): dot over this lane's chunk, then over the 16 lanes of the key.
-  const float sl2 = a.scale * kLog2e;
-  float sc[IT][RMAX];
-#pragma unroll
-  for (int i = 0; i < IT; ++i) {
-#pragma unroll
-    for (int r = 0; r < RMAX; ++r) {
-      float acc = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc = fmaf((e % 2) ? bf_hi(kreg[i][e / 2]) : bf_lo(kreg[i][e / 2]), qv[r][e], acc);
-#pragma unroll
-      for (int o = 8; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, kWave);
-      sc[i][r] = kok[i] ? acc * sl2 : -INFINITY;
+    for (int ds = 0; ds < 4; ++ds) {
+      const uint32_t off = (uint32_t)(((size_t)j * kv_row + (size_t)g * kAd + 8 * (4 * ds + q)) * 2);
+      kf[t][ds] = buf_ld16(kr, ok ? off : kOffNone);
     }
   }
-  // Per head: max and sum over the split (16 keys per lane, then the 4 key slots).
-  float mx[RMAX], zs[RMAX];
+  // Q^T fragments: column c16 is head g * rep + c16.
+  u32x4 qf[4];
+  const uint16_t *Qh = a.Q + (size_t)b * q_row + ((size_t)g * rep + c16) * kAd;
 #pragma unroll
-  for (int r = 0; r < RMAX; ++r) {
-    float m = -INFINITY;
+  for (int ds = 0; ds < 4; ++ds)
+    qf[ds] = c16 < rep ? ld16(Qh + 8 * (4 * ds + q)) : u32x4{0u, 0u, 0u, 0u};
+
+  // Scores (log2 domain) of keys 16 t + 4 q + i for head c16.
+  const float sl2 = a.scale * kLog2e;
+  f32x4 sc[4];
+  float m = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < IT; ++i) m = fmaxf(m, sc[i][r]);
-    m = fmaxf(m, __shfl_xor(m, 16, kWave));
-    m = fmaxf(m, __shfl_xor(m, 32, kWave));
-    mx[r] = m;  // finite: the split has a valid key
-    float z = 0.f;
+  for (int t = 0; t < 4; ++t) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < IT; ++i) {
-      const float pv = exp2_fast(sc[i][r] - m);  // -inf -> 0
-      sc[i][r] = pv;
+    for (int ds = 0; ds < 4; ++ds) acc = mfma16x16x32(kf[t][ds], qf[ds], acc);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int j = j0 + 16 * t + 4 * q + i;
+      acc[i] = (j >= jlo && j < jhi) ? acc[i] * sl2 : -INFINITY;
+      m = fmaxf(m, acc[i]);
+    }
+    sc[t] = acc;
+  }
+  m = fmaxf(m, __shfl_xor(m, 16, kWave));
+  m = fmaxf(m, __shfl_xor(m, 32, kWave));  // finite: the split has a valid key
+  float z = 0.f;
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float pv = exp2_fast(sc[t][i] - m);  // -inf -> 0
+      sc[t][i] = pv;
       z += pv;
     }
-    z += __shfl_xor(z, 16, kWave);
-    z += __shfl_xor(z, 32, kWave);
-    zs[r] = z;
+  z += __shfl_xor(z, 16, kWave);
+  z += __shfl_xor(z, 32, kWave);
+  // P^T fragments: keys 32 ks + 4 q + i, then 32 ks + 16 + 4 q + i.
+  u32x4 pf[2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+    pf[ks] = u32x4{pack_bf16x2(sc[2 * ks][0], sc[2 * ks][1]), pack_bf16x2(sc[2 * ks][2], sc[2 * ks][3]),
+                   pack_bf16x2(sc[2 * ks + 1][0], sc[2 * ks + 1][1]),
+                   pack_bf16x2(sc[2 * ks + 1][2], sc[2 * ks + 1][3])};
+
+  WIDE_WAIT_VM_LGKM0(0);  // V has landed in LDS
+  WIDE_BARRIER();
+  // O^T: rows = head dims 16 db + 4 q + i, column = head c16.
+  f32x4 o[8];
+#pragma unroll
+  for (int db = 0; db < 8; ++db) {
+    o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int chunk = 2 * db + (c16 % 4) / 2;
+      const int r0 = ks * 32 + 4 * q + c16 / 4, r1 = r0 + 16;
+      const u32x2 lo = lds_read_tr16(sv + r0 * kAd + ((chunk ^ v_swz(r0)) * 8) + 4 * (c16 % 2));
+      const u32x2 hi = lds_read_tr16(sv + r1 * kAd + ((chunk ^ v_swz(r1)) * 8) + 4 * (c16 % 2));
+      const u32x4 vf = {lo[0], lo[1], hi[0], hi[1]};
+      o[db] = mfma16x16x32(vf, pf[ks], o[db]);
+    }
   }
-  // Unnormalised output for this lane's 8 head dims, summed over the 4 key slots.
+  if (c16 < rep) {
+    float *part = ws + (((size_t)b * a.Hq + g * rep + c16) * nsplit + split) * kDecPart;
 #pragma unroll
-  for (int r = 0; r < RMAX; ++r) {
-    if (r >= rep) break;
-    float o[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) o[e] = 0.f;
-#pragma unroll
-    for (int i = 0; i < IT; ++i)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) o[e] = fmaf(sc[i][r], (e % 2) ? bf_hi(vreg[i][e / 2]) : bf_lo(vreg[i][e / 2]), o[e]);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      o[e] += __shfl_xor(o[e], 16, kWave);
-      o[e] += __shfl_xor(o[e], 32, kWave);
-    }
-    float *part = ws + (((size_t)b * a.Hq + g * rep + r) * nsplit + split) * kDecPart;
-    if (kq == 0) {
-      *reinterpret_cast<f32x4 *>(part + dc * 8) = f32x4{o[0], o[1], o[2], o[3]};
-      *reinterpret_cast<f32x4 *>(part + dc * 8 + 4) = f32x4{o[4], o[5], o[6], o[7]};
-    }
-    if (lane == 0) {
-      part[kAd] = mx[r];
-      part[kAd + 1] = zs[r];
+    for (int db = 0; db < 8; ++db) *reinterpret_cast<f32x4 *>(part + 16 * db + 4 * q) = o[db];
+    if (q == 0) {
+      part[kAd] = m;
+      part[kAd + 1] = z;
     }
   }
 }
@@ -539,15 +548,7 @@ int launch_attn(const AttnArgs &a, hipStream_t s) {
   if (a.Tq == 1) {
     const int nsplit = (a.Tk + kDecKeys - 1) / kDecKeys;
     const dim3 grid(nsplit, a.Hk, a.B);
-    const int rep = a.Hq / a.Hk;
-    if (rep == 1)
-      hipLaunchKernelGGL(attn_decode_split_kernel<1>, grid, dim3(kWave), 0, s, a, nsplit);
-    else if (rep == 2)
-      hipLaunchKernelGGL(attn_decode_split_kernel<2>, grid, dim3(kWave), 0, s, a, nsplit);
-    else if (rep <= 4)
-      hipLaunchKernelGGL(attn_decode_split_kernel<4>, grid, dim3(kWave), 0, s, a, nsplit);
-    else
-      hipLaunchKernelGGL(attn_decode_split_kernel<8>, grid, dim3(kWave), 0, s, a, nsplit);
+    hipLaunchKernelGGL(attn_decode_split_kernel, grid, dim3(kWave), 0, s, a, nsplit);
     const dim3 mgrid(a.Hq, a.B, kAd / kMergeDims);
     if (a.o_f32)
       hipLaunchKernelGGL(attn_decode_merge_kernel<true>, mgrid, dim3(kMergeThreads), 0, s, a, nsplit);
