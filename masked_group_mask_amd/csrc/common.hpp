@@ -80,4 +80,36 @@ __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirs
 
 __device__ __forceinline__ float silu(float x) { return x / (1.0f + __expf(-x)); }
 
+// acc + sum over 8 bf16 pairs of w * x: four v_dot2c_f32_bf16 (exact bf16
+// products, fp32 sums). Each element is copied to a scalar before the bit
+// cast: hipcc drops the index of a bit cast applied to a vector subscript.
+__device__ __forceinline__ float dot8(const u32x4 &w, const u32x4 &x, float acc) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const uint32_t we = w[e], xe = x[e];
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, we), __builtin_bit_cast(bf16x2, xe), acc, false);
+  }
+  return acc;
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the 64 lanes, the same value in every lane: four DPP steps give
+// each 16-lane row its sum (swap neighbours, swap pairs, mirror within 8,
+// mirror within 16), then the four row sums are read out. No LDS traffic.
+__device__ __forceinline__ float wave_sum(float v) {
+  v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp<0x141>(v);  // row_half_mirror
+  v += dpp<0x140>(v);  // row_mirror
+  const int b = __builtin_bit_cast(int, v);
+  return (__builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0)) +
+          __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16))) +
+         (__builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32)) +
+          __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48)));
+}
+
 }  // namespace wide

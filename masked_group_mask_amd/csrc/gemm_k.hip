@@ -217,26 +217,12 @@ __global__ __launch_bounds__(64 * W) void gemm_k_kernel(KArgs a) {
   }
 }
 
-__device__ __forceinline__ float wave_sum_k(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
-}
-
-__device__ __forceinline__ float dot8k(const u32x4 &w, const u32x4 &x, float acc) {
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    acc = fmaf(bf_lo(w[e]), bf_lo(x[e]), acc);
-    acc = fmaf(bf_hi(w[e]), bf_hi(x[e]), acc);
-  }
-  return acc;
-}
-
-// Matrix-vector GEMM-K for M <= 4. The four waves first list the K-groups
-// some token keeps (one ballot per 64 groups); then each wave owns one output
-// feature and streams only the listed groups' segments of its weight row,
-// 16 bytes per lane with consecutive lanes on consecutive chunks, a block of
-// 8 chunks per lane issued before any is used.
+// Matrix-vector GEMM-K for M = MT <= 4 tokens. The four waves first list the
+// K-groups some token keeps (one ballot per 64 groups); then each wave owns
+// one output feature and streams only the listed groups' segments of its
+// weight row, 16 bytes per lane with consecutive lanes on consecutive chunks,
+// a block of 8 chunks per lane issued before any is used.
+template <int MT>
 __global__ __launch_bounds__(256) void gemv_k_kernel(KArgs a) {
   constexpr int U = 8;
   __shared__ uint16_t sGrp[kKMaxGroups];
@@ -244,13 +230,13 @@ __global__ __launch_bounds__(256) void gemv_k_kernel(KArgs a) {
   __shared__ int sCnt[4];
   const int NG = a.K / a.G;
   const int lane = threadIdx.x % kWave;
-  const int wave = threadIdx.x / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
   int base = 0;
   for (int g0 = 0; g0 < NG; g0 += 4 * kWave) {
     const int g = g0 + wave * kWave + lane;
     int on = 0;
     if (g < NG)
-      for (int m = 0; m < a.M; ++m) on |= (a.mask[(size_t)m * NG + g] != 0) << m;
+      for (int m = 0; m < MT; ++m) on |= (a.mask[(size_t)m * NG + g] != 0) << m;
     const uint64_t bal = __ballot(on != 0);
     if (lane == 0) sCnt[wave] = __popcll(bal);
     __syncthreads();
@@ -268,7 +254,9 @@ __global__ __launch_bounds__(256) void gemv_k_kernel(KArgs a) {
   const int nchunks = base * cpg;
   const int n = blockIdx.x * 4 + wave;
   const rsrc_t wr = make_rsrc(a.B + (size_t)n * a.ldb, (uint64_t)a.K * 2);
-  float s[4] = {0.f, 0.f, 0.f, 0.f};
+  float s[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) s[m] = 0.f;
   for (int c0 = 0; c0 < nchunks; c0 += kWave * U) {
     u32x4 w[U];
     int kk[U], on[U];
@@ -279,24 +267,26 @@ __global__ __launch_bounds__(256) void gemv_k_kernel(KArgs a) {
       const int gi = ok ? c / cpg : 0;
       kk[u] = sGrp[gi] * a.G + (c % cpg) * 8;
       on[u] = ok ? sOn[gi] : 0;
-      w[u] = buf_ld16(wr, ok ? (uint32_t)kk[u] * 2u : kOffNone);
     }
+    // x chunks first (cache hits), then the weight chunks, then the products.
+    u32x4 x[MT][U];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      if (m >= a.M) break;
+    for (int m = 0; m < MT; ++m) {
       const rsrc_t xr = make_rsrc(a.A + (size_t)m * a.lda, (uint64_t)a.K * 2);
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const bool use = (on[u] >> m) & 1;
-        const u32x4 x = buf_ld16(xr, use ? (uint32_t)kk[u] * 2u : kOffNone);
-        s[m] = dot8k(w[u], x, s[m]);
-      }
+      for (int u = 0; u < U; ++u) x[m][u] = buf_ld16(xr, (on[u] >> m) & 1 ? (uint32_t)kk[u] * 2u : kOffNone);
     }
+#pragma unroll
+    for (int u = 0; u < U; ++u) w[u] = buf_ld16(wr, on[u] ? (uint32_t)kk[u] * 2u : kOffNone);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int m = 0; m < MT; ++m) s[m] = dot8(w[u], x[m][u], s[m]);
   }
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    if (m >= a.M) break;
-    const float v = wave_sum_k(s[m]);
+  for (int m = 0; m < MT; ++m) {
+    const float v = wave_sum(s[m]);
     if (lane == 0) {
       float *dst = a.C + (size_t)m * a.ldc + n;
       *dst = a.beta ? *dst + v : v;
@@ -328,7 +318,13 @@ int launch_gemm_k(const KArgs &a0, hipStream_t s) {
   a.split_tail = 0;
   const int mt = (a.M + eng::kBM - 1) / eng::kBM;
   if (a.M <= 4) {
-    hipLaunchKernelGGL(gemv_k_kernel, dim3(a.N / 4), dim3(256), 0, s, a);
+    const dim3 grid(a.N / 4), block(256);
+    switch (a.M) {
+      case 1: hipLaunchKernelGGL(gemv_k_kernel<1>, grid, block, 0, s, a); break;
+      case 2: hipLaunchKernelGGL(gemv_k_kernel<2>, grid, block, 0, s, a); break;
+      case 3: hipLaunchKernelGGL(gemv_k_kernel<3>, grid, block, 0, s, a); break;
+      default: hipLaunchKernelGGL(gemv_k_kernel<4>, grid, block, 0, s, a); break;
+    }
   } else if (a.N % 256 == 0) {
     const int tiles = mt * (a.N / 256), cus = cu_count();
     const int tail = tiles % cus;

@@ -160,48 +160,48 @@ __global__ __launch_bounds__(64 * W) void gemm_mn_kernel(MnArgs a) {
   }
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
-}
-
-__device__ __forceinline__ float dot8(const u32x4 &w, const u32x4 &x, float acc) {
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    acc = fmaf(bf_lo(w[e]), bf_lo(x[e]), acc);
-    acc = fmaf(bf_hi(w[e]), bf_hi(x[e]), acc);
-  }
-  return acc;
-}
-
-// Matrix-vector GEMM-MN for M <= 4 reading the mask directly (no reorder).
-// One wave per output feature n (four per workgroup, all in one group). A
-// workgroup whose group is off for every token exits without reading its
-// weights. The weight row is streamed in 16-byte chunks (consecutive lanes,
-// consecutive chunks: whole cache lines), with a whole block of chunks per
-// lane issued before any is used, so each wave keeps 8 KB per row in flight.
-template <bool SWIGLU, bool OUT_F32>
+// Matrix-vector GEMM-MN for M = MT <= 4 tokens, reading the mask directly
+// (no reorder). One wave per output feature n (four per workgroup, all in one
+// group). A workgroup whose group is off for every token exits without
+// reading its weights. The weight row is streamed in 16-byte chunks
+// (consecutive lanes, consecutive chunks: whole cache lines), a whole block of
+// chunks per lane issued before any is used, so each wave keeps 8 KB per row
+// in flight; the token count is a template argument so that only MT rows of
+// x are held in registers (occupancy).
+template <bool SWIGLU, bool OUT_F32, int MT>
 __global__ __launch_bounds__(256) void gemv_mn_kernel(MnArgs a) {
   constexpr int U = 8;                // 16-byte chunks per lane per block
   constexpr int BLK = kWave * 8 * U;  // bf16 elements per block
-  const int n = blockIdx.x * 4 + threadIdx.x / kWave;
+  const int n = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
   const int g = (blockIdx.x * 4) / a.G;
   const int NG = a.N / a.G;
-  bool act[4];
+  bool act[MT];
   bool any = false;
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    act[m] = m < a.M && a.mask[(size_t)m * NG + g] != 0;
+  for (int m = 0; m < MT; ++m) {
+    act[m] = a.mask[(size_t)m * NG + g] != 0;
     any |= act[m];
   }
   if (!any) return;  // the whole group is off for every token: its weights are never read
   const int lane = threadIdx.x % kWave;
   const rsrc_t w0r = make_rsrc(a.B0 + (size_t)n * a.ldb, (uint64_t)a.K * 2);
   const rsrc_t w1r = make_rsrc((SWIGLU ? a.B1 : a.B0) + (size_t)n * a.ldb, (uint64_t)a.K * 2);
-  float s0[4] = {0.f, 0.f, 0.f, 0.f}, s1[4] = {0.f, 0.f, 0.f, 0.f};
+  float s0[MT], s1[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) s0[m] = s1[m] = 0.f;
   for (int k0 = 0; k0 < a.K; k0 += BLK) {
-    u32x4 w0[U], w1[U];
+    // The block's x chunks first (cache hits, shared by every wave), then the
+    // weight chunks, then the products: no load waits behind another's use.
+    u32x4 x[MT][U], w0[U], w1[U];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      const rsrc_t xr = make_rsrc(a.A + (size_t)m * a.lda, (uint64_t)a.K * 2);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int k = k0 + (u * kWave + lane) * 8;
+        x[m][u] = buf_ld16(xr, act[m] && k < a.K ? (uint32_t)k * 2u : kOffNone);
+      }
+    }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int k = k0 + (u * kWave + lane) * 8;
@@ -209,21 +209,17 @@ __global__ __launch_bounds__(256) void gemv_mn_kernel(MnArgs a) {
       w0[u] = buf_ld16(w0r, off);
       if (SWIGLU) w1[u] = buf_ld16(w1r, off);
     }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      if (!act[m]) continue;
-      const rsrc_t xr = make_rsrc(a.A + (size_t)m * a.lda, (uint64_t)a.K * 2);
+    for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int k = k0 + (u * kWave + lane) * 8;
-        const u32x4 x = buf_ld16(xr, k < a.K ? (uint32_t)k * 2u : kOffNone);
-        s0[m] = dot8(w0[u], x, s0[m]);
-        if (SWIGLU) s1[m] = dot8(w1[u], x, s1[m]);
+      for (int m = 0; m < MT; ++m) {
+        s0[m] = dot8(w0[u], x[m][u], s0[m]);
+        if (SWIGLU) s1[m] = dot8(w1[u], x[m][u], s1[m]);
       }
-    }
   }
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
+  for (int m = 0; m < MT; ++m) {
     if (!act[m]) continue;
     const float g0 = wave_sum(s0[m]);
     float out = g0;
@@ -241,7 +237,13 @@ static void launch_tiled(const MnArgs &a, hipStream_t s) {
 
 template <bool SWIGLU, bool F32>
 static void launch_gemv(const MnArgs &a, hipStream_t s) {
-  hipLaunchKernelGGL((gemv_mn_kernel<SWIGLU, F32>), dim3(a.N / 4), dim3(256), 0, s, a);
+  const dim3 grid(a.N / 4), block(256);
+  switch (a.M) {
+    case 1: hipLaunchKernelGGL((gemv_mn_kernel<SWIGLU, F32, 1>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((gemv_mn_kernel<SWIGLU, F32, 2>), grid, block, 0, s, a); break;
+    case 3: hipLaunchKernelGGL((gemv_mn_kernel<SWIGLU, F32, 3>), grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL((gemv_mn_kernel<SWIGLU, F32, 4>), grid, block, 0, s, a); break;
+  }
 }
 
 int launch_gemm_mn(const MnArgs &a, hipStream_t s) {

@@ -185,8 +185,9 @@ def test_gemm_mn_swiglu(M, N, K, G, dt):
 
 @pytest.mark.parametrize("M", [1, 2, 3, 4])
 @pytest.mark.parametrize("swiglu", [False, True])
-def test_gemv_mn_mask_direct(M, swiglu):
-    N, K, G = 1024, 512, 128
+@pytest.mark.parametrize("K", [512, 9000])  # one partial block; three blocks of 4096 with a ragged last one
+def test_gemv_mn_mask_direct(M, swiglu, K):
+    N, G = 1024, 128
     A = wl.random_bf16(10 + M, (M, K))
     B = wl.random_bf16(11, (N, K), 0.05)
     U = wl.random_bf16(12, (N, K), 0.05)
@@ -280,15 +281,29 @@ def test_gemm_k_all_or_nothing(p):
 
 
 @pytest.mark.parametrize("M", [1, 2, 3, 4])
-def test_gemv_k(M):
-    N, K, G = 512, 2048, 128
+@pytest.mark.parametrize("K,G", [(2048, 128), (14336, 128), (4096, 512)])
+def test_gemv_k(M, K, G):
+    N = 512
     A = wl.random_bf16(30 + M, (M, K))
     B = wl.random_bf16(31, (N, K), 0.05)
     mask = wl.random_mask(32 + M, (M, K // G), 0.5)
-    say("gemv_k", M)
+    say("gemv_k", M, K, G)
     out = W().gemm_k(to_dev(A, torch), to_dev(B, torch), G, to_dev(mask, torch))
     torch.cuda.synchronize()
     check_gemm(f32_of(out), ref.gemm_k(A, B, mask, G), "gemv_k")
+
+
+def test_gemv_k_beta():
+    M, N, K, G = 2, 256, 4096, 128
+    A = wl.random_bf16(40, (M, K))
+    B = wl.random_bf16(41, (N, K), 0.05)
+    mask = wl.random_mask(42, (M, K // G), 0.5)
+    C0 = np.random.default_rng(43).standard_normal((M, N)).astype(np.float32)
+    say("gemv_k beta")
+    out = torch.from_numpy(C0.copy()).to("cuda")
+    W().gemm_k(to_dev(A, torch), to_dev(B, torch), G, to_dev(mask, torch), out=out, beta=1)
+    torch.cuda.synchronize()
+    check_gemm(f32_of(out), C0.astype(np.float64) + ref.gemm_k(A, B, mask, G), "gemv_k beta")
 
 
 # ---------------------------------------------------------------------------
