@@ -382,6 +382,41 @@ def test_attention_decode(Hq, Hk, Tk, mode):
     assert (out.cpu().numpy().view(np.uint32)[~keep] == 0).all()
 
 
+def test_attention_decode_workspace_reuse():
+    """One workspace (uninitialised) through consecutive decoding calls of
+    different sizes: nothing a call leaves there may leak into the next."""
+    Hq, Hk, d = 32, 8, 128
+    ws = torch.empty(W().attn_workspace_bytes(2, 1, 3000, Hq, Hk, d), dtype=torch.uint8, device="cuda")
+    for i, (B, Tk) in enumerate([(2, 3000), (1, 700), (2, 257), (2, 3000)]):
+        Q = wl.random_bf16(80 + i, (B, 1, Hq, d), 1.0)
+        K = wl.random_bf16(90 + i, (B, Tk, Hk, d), 1.0)
+        V = wl.random_bf16(100 + i, (B, Tk, Hk, d), 1.0)
+        mask = wl.random_mask(110 + i, (B, 1, Hk), 0.5)
+        say("decode workspace reuse", i, B, Tk)
+        out = W().attn(to_dev(Q, torch), to_dev(K, torch), to_dev(V, torch), mask=to_dev(mask, torch),
+                       out_dtype=torch.float32, workspace=ws)
+        torch.cuda.synchronize()
+        check_attn(f32_of(out), ref.attention(Q, K, V, mask), f"decode call {i}")
+
+
+def test_attention_decode_no_valid_key():
+    """Left padding that covers every key: active heads get O = 0."""
+    B, Tk, Hq, Hk, d = 2, 600, 16, 4, 128
+    Q = wl.random_bf16(120, (B, 1, Hq, d), 1.0)
+    K = wl.random_bf16(121, (B, Tk, Hk, d), 1.0)
+    V = wl.random_bf16(122, (B, Tk, Hk, d), 1.0)
+    mask = np.ones((B, 1, Hk), np.uint8)
+    lp = [Tk, 5]
+    say("decode no valid key")
+    out = W().attn(to_dev(Q, torch), to_dev(K, torch), to_dev(V, torch), mask=to_dev(mask, torch),
+                   leftpad=to_dev(np.array(lp, np.int32), torch), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    want = ref.attention(Q, K, V, mask, leftpad=lp)
+    assert (want[0] == 0).all()
+    check_attn(f32_of(out), want, "decode no valid key")
+    assert (f32_of(out)[0] == 0).all()
+
+
 def test_attention_decode_leftpad():
     B, Tk, Hq, Hk, d = 2, 700, 16, 4, 128
     Q = wl.random_bf16(70, (B, 1, Hq, d), 1.0)
