@@ -10,9 +10,9 @@ the attention groups and 50% of the FFN groups inactive, FFN group size 128.
 
 Prints one JSON line: active-FLOP TFLOP/s of the masked layer, the speedup
 over the same kernels run with all-ones masks, the roofline of the dominant
-kernel (timed with HIP events on the launch stream), a one-token decode step
-of the Llama3.1-8B shape (HBM bytes/s), and the CPU oracle timed on a sample
-of the same workload.
+kernel (timed with HIP events on the launch stream), decode steps of the
+Llama3.1-8B shape for one and for four sequences (HBM bytes/s), and the CPU
+oracle timed on a sample of the same workload.
 """
 from __future__ import annotations
 
@@ -72,9 +72,10 @@ def hold_gpu(torch, ms: float) -> None:
     sleep(int(ms * hold_gpu.cycles_per_ms))
 
 
-def bench_decode(torch, wl, metrics, steps=50, sets=3):
-    """One-token decode step of the Llama3.1-8B shape, KV cache of 16384, half
-    of the attention and FFN groups off. Weight/KV sets rotate so the 256 MB
+def bench_decode(torch, wl, metrics, B=1, steps=50, sets=3):
+    """Decode step of the Llama3.1-8B shape: B sequences with one new token
+    each, KV cache of 16384 per sequence, half of the attention and FFN groups
+    off for every token. Weight/KV sets rotate so the 256 MB
     Infinity Cache cannot hold the active set across steps.
 
     Timed two ways: as individual launches (HIP events around each op, the
@@ -82,7 +83,7 @@ def bench_decode(torch, wl, metrics, steps=50, sets=3):
     captured HIP graph of the step replayed back to back (whole step, gaps
     between kernels included). The headline rate is the graph replay's."""
     from masked_group_mask_amd.layer import DECODE_OPS, DecodeLayer
-    s = wl.shape("llama8b_decode")
+    s = wl.shape("llama8b_decode", B=B)
     host = wl.make_layer(s, seed=1)
     nbytes = metrics.decode_bytes(s, host["mask_attn"], host["mask_ffn"])
     total = sum(nbytes.values())
@@ -117,7 +118,8 @@ def bench_decode(torch, wl, metrics, steps=50, sets=3):
     torch.cuda.synchronize()
     graph_ms = e0.elapsed_time(e1) / steps
     return {
-        "workload": "llama8b_decode (B=1, KV 16384, 4/8 attention and 56/112 FFN groups on)",
+        "workload": ("llama8b_decode (B=%d, KV 16384 per sequence, 4/8 attention and 56/112 FFN groups "
+                     "on per token)" % B),
         "active_bytes": total,
         "graph_ms_per_step": graph_ms,
         "launch_ms_per_step": launch_ms,
@@ -292,9 +294,12 @@ def main():
     }
     if not args.no_decode:
         log("timing decode step")
-        out["decode"] = bench_decode(torch, wl, metrics)
+        out["decode"] = bench_decode(torch, wl, metrics, B=1)
         log(f"decode: {out['decode']['graph_ms_per_step'] * 1e3:.1f} us, "
             f"{out['decode']['GB_per_s']:.0f} GB/s")
+        out["decode_b4"] = bench_decode(torch, wl, metrics, B=4)
+        log(f"decode B=4: {out['decode_b4']['graph_ms_per_step'] * 1e3:.1f} us, "
+            f"{out['decode_b4']['GB_per_s']:.0f} GB/s")
     if not args.no_cpu_baseline:
         log(f"timing CPU oracle on {args.cpu_rows} rows")
         out["cpu_baseline"] = cpu_baseline(s, host, args.cpu_rows)

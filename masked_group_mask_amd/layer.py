@@ -95,36 +95,40 @@ class PrefillLayer:
 
 
 class DecodeLayer:
-    """One-token decode step of shape `s` with `sets` rotated weight/KV copies."""
+    """Decode step of shape `s`: B sequences with one new token each (B <= 4:
+    the matrix-vector kernels read the mask bytes directly), with `sets`
+    rotated weight/KV copies."""
 
     def __init__(self, s, host: dict, sets: int = 1):
         self.s = s
+        B = s.B
         d = lambda k: to_device(host[k])  # noqa: E731
         base = {k: d(k) for k in ("w_q", "w_o", "w_gate", "w_up", "w_down", "k", "v")}
         self.wsets = [base] + [{k: t.clone() for k, t in base.items()} for _ in range(sets - 1)]
-        self.x = d("x")
-        self.ma = d("mask_attn")                                   # [B=1][1][Hk]
-        self.mf = d("mask_ffn").view(1, s.NG_ffn)
+        self.x = d("x")                                            # [B][D]
+        self.ma = d("mask_attn")                                   # [B][1][Hk]
+        self.mf = d("mask_ffn").view(B, s.NG_ffn)
         dev = self.x.device
-        self.q = torch.empty((1, s.Hq * s.d), dtype=torch.bfloat16, device=dev)
-        self.o = torch.empty((1, 1, s.Hq, s.d), dtype=torch.bfloat16, device=dev)
-        self.h = torch.empty((1, s.Dff), dtype=torch.bfloat16, device=dev)
-        self.y_attn = torch.empty((1, s.D), dtype=torch.float32, device=dev)
-        self.y_ffn = torch.empty((1, s.D), dtype=torch.float32, device=dev)
-        self.ws = torch.empty(mg.attn_workspace_bytes(1, 1, s.Tkv, s.Hq, s.Hk, s.d),
+        self.q = torch.empty((B, s.Hq * s.d), dtype=torch.bfloat16, device=dev)
+        self.o = torch.empty((B, 1, s.Hq, s.d), dtype=torch.bfloat16, device=dev)
+        self.h = torch.empty((B, s.Dff), dtype=torch.bfloat16, device=dev)
+        self.y_attn = torch.empty((B, s.D), dtype=torch.float32, device=dev)
+        self.y_ffn = torch.empty((B, s.D), dtype=torch.float32, device=dev)
+        self.ws = torch.empty(mg.attn_workspace_bytes(B, 1, s.Tkv, s.Hq, s.Hk, s.d),
                               dtype=torch.uint8, device=dev)
 
     def step(self, i: int = 0, events=None) -> None:
         s = self.s
+        B = s.B
         w = self.wsets[i % len(self.wsets)]
         rec = (lambda j: events[j].record()) if events is not None else (lambda j: None)
         rec(0)
-        mg.gemm_mn(self.x, w["w_q"], s.G_attn, mask=self.ma.view(1, s.Hk), out=self.q)
+        mg.gemm_mn(self.x, w["w_q"], s.G_attn, mask=self.ma.view(B, s.Hk), out=self.q)
         rec(1)
-        mg.attn(self.q.view(1, 1, s.Hq, s.d), w["k"], w["v"], mask=self.ma, out=self.o,
+        mg.attn(self.q.view(B, 1, s.Hq, s.d), w["k"], w["v"], mask=self.ma, out=self.o,
                 workspace=self.ws)
         rec(2)
-        mg.gemm_k(self.o.view(1, s.Hq * s.d), w["w_o"], s.G_attn, self.ma.view(1, s.Hk),
+        mg.gemm_k(self.o.view(B, s.Hq * s.d), w["w_o"], s.G_attn, self.ma.view(B, s.Hk),
                   out=self.y_attn)
         rec(3)
         mg.gemm_mn_swiglu(self.x, w["w_gate"], w["w_up"], s.G_ffn, mask=self.mf, out=self.h)

@@ -49,13 +49,19 @@ def layer_flops(s, mask_attn, mask_ffn) -> dict:
     return out
 
 
-def decode_bytes(s, mask_attn_row, mask_ffn_row) -> dict:
-    """HBM bytes one decode step must read for the active groups (bf16)."""
-    ga = active_pairs(mask_attn_row)
-    gf = active_pairs(mask_ffn_row)
+def decode_bytes(s, mask_attn, mask_ffn) -> dict:
+    """HBM bytes one decode step must read (bf16), for B sequences with one new
+    token each (masks [B][1][Hk] and [B][1][NG_ffn], or one row for B = 1):
+    a weight row or column is read once if any token keeps its group; each
+    sequence reads the K and V cache of every group its token keeps."""
+    ma = np.asarray(mask_attn).reshape(-1, s.Hk) != 0
+    mf = np.asarray(mask_ffn).reshape(-1, s.NG_ffn) != 0
+    ga = int(ma.any(axis=0).sum())    # attention groups some token keeps
+    gf = int(mf.any(axis=0).sum())
+    kv_pairs = int(ma.sum())          # (sequence, group) pairs
     return {
         "q_proj": ga * s.G_attn * s.D * 2,
-        "attention": ga * 2 * s.Tkv * s.d * 2 * s.B,
+        "attention": kv_pairs * 2 * s.Tkv * s.d * 2,
         "o_proj": ga * s.D * s.G_attn * 2,
         "gate_up_swiglu": gf * 2 * s.G_ffn * s.D * 2,
         "down_proj": gf * s.D * s.G_ffn * 2,

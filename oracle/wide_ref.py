@@ -318,17 +318,31 @@ def flops_attention(mask, Tk: int, Hq: int, d: int, causal: bool = True,
     return total
 
 
-def decode_bytes(mask_attn_row, mask_ffn_row, D: int, Hq: int, Hk: int, d: int,
+def decode_bytes(mask_attn, mask_ffn, D: int, Hq: int, Hk: int, d: int,
                  G_ffn: int, Tk: int) -> int:
-    """HBM bytes a one-token decode step must read (bf16 weights and KV).
+    """HBM bytes a decode step must read (bf16 weights and KV), for B sequences
+    with one new token each: masks [B][Hk] and [B][NG_ffn] (a single row is one
+    sequence).
 
-    Per active attention group: its W_q rows and W_o columns (G_attn x D each)
-    and its K and V cache (Tk x d each). Per active FFN group: G_ffn rows of
-    W_gate and W_up and G_ffn columns of W_down (G_ffn x D each).
+    The W_q rows and W_o columns of an attention group (G_attn x D each), and
+    the G_ffn rows of W_gate and W_up and G_ffn columns of W_down of an FFN
+    group, are read once if any of the B tokens keeps the group. Every
+    sequence reads its own K and V cache (Tk x d each) for every group its
+    token keeps.
     """
-    ga = int(np.count_nonzero(np.asarray(mask_attn_row)))
-    gf = int(np.count_nonzero(np.asarray(mask_ffn_row)))
+    ma = np.atleast_2d(np.asarray(mask_attn)) != 0
+    mf = np.atleast_2d(np.asarray(mask_ffn)) != 0
     G_attn = (Hq // Hk) * d
-    per_attn = 2 * (2 * G_attn * D) + 2 * (2 * Tk * d)
-    per_ffn = 2 * (3 * G_ffn * D)
-    return ga * per_attn + gf * per_ffn
+    weights = 0
+    for g in range(ma.shape[1]):
+        if ma[:, g].any():
+            weights += 2 * (2 * G_attn * D)
+    for g in range(mf.shape[1]):
+        if mf[:, g].any():
+            weights += 2 * (3 * G_ffn * D)
+    kv = 0
+    for b in range(ma.shape[0]):
+        for g in range(ma.shape[1]):
+            if ma[b, g]:
+                kv += 2 * (2 * Tk * d)
+    return weights + kv

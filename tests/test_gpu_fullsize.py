@@ -135,25 +135,27 @@ def test_tiny_ffn_every_entry():
     assert (bits_of(h)[~ref.expand(m2, s.G_ffn)] == 0).all()
 
 
-def test_decode_step_full_size():
-    """Llama3.1-8B decode: one token, KV cache 16384, half the groups off."""
+@pytest.mark.parametrize("B", [1, 4])
+def test_decode_step_full_size(B):
+    """Llama3.1-8B decode: B sequences with one new token each, KV cache 16384,
+    half the groups off for every token (each token its own half)."""
     from masked_group_mask_amd.layer import DecodeLayer
-    s = wl.shape("llama8b_decode")
-    say("full-size decode")
+    s = wl.shape("llama8b_decode", B=B)
+    say("full-size decode", B)
     host = wl.make_layer(s, seed=1)
     layer = DecodeLayer(s, host, sets=1)
     layer.step(0)
     torch.cuda.synchronize()
-    ma2 = host["mask_attn"].reshape(1, s.Hk)
-    mf2 = host["mask_ffn"].reshape(1, s.NG_ffn)
+    ma2 = host["mask_attn"].reshape(B, s.Hk)
+    mf2 = host["mask_ffn"].reshape(B, s.NG_ffn)
     q_bits = bits_of(layer.q)
     want_q = ref.gemm_mn(host["x"], host["w_q"], ma2, s.G_attn)
     keep = ref.expand(ma2, s.G_attn)
     check_bf16_store(q_bits[keep], want_q[keep], "decode q_proj")
-    want_o = ref.attention(q_bits.reshape(1, 1, s.Hq, s.d), host["k"], host["v"], host["mask_attn"])
-    o_bits = bits_of(layer.o).reshape(1, s.Hq, s.d)
+    want_o = ref.attention(q_bits.reshape(B, 1, s.Hq, s.d), host["k"], host["v"], host["mask_attn"])
+    o_bits = bits_of(layer.o).reshape(B, s.Hq, s.d)
     keep_h = np.repeat(ma2 != 0, s.Hq // s.Hk, axis=1)
-    check_attn_bf16(o_bits[keep_h], want_o.reshape(1, s.Hq, s.d)[keep_h], "decode attention")
-    want_y = ref.gemm_k(o_bits.reshape(1, -1), host["w_o"], ma2, s.G_attn)
+    check_attn_bf16(o_bits[keep_h], want_o.reshape(B, s.Hq, s.d)[keep_h], "decode attention")
+    want_y = ref.gemm_k(o_bits.reshape(B, -1), host["w_o"], ma2, s.G_attn)
     check_gemm(layer.y_attn.cpu().numpy().astype(np.float64), want_y, "decode o_proj")
-    check_ffn(s, host, np.array([0]), bits_of(layer.h), layer.y_ffn.cpu().numpy().astype(np.float64))
+    check_ffn(s, host, np.arange(B), bits_of(layer.h), layer.y_ffn.cpu().numpy().astype(np.float64))

@@ -33,3 +33,13 @@ def test_decode_bytes_match_oracle():
     got = sum(metrics.decode_bytes(s, ma, mf).values())
     assert got == ref.decode_bytes(ma, mf, s.D, s.Hq, s.Hk, s.d, s.G_ffn, s.Tk)
     assert x["x"].shape == (1, 4096)
+
+
+def test_decode_bytes_batched_match_oracle():
+    s = wl.shape("llama8b_decode", B=4)
+    h = wl.make_layer(s, seed=2, parts=("attn", "ffn"))
+    ma, mf = h["mask_attn"], h["mask_ffn"]
+    got = sum(metrics.decode_bytes(s, ma, mf).values())
+    assert got == ref.decode_bytes(ma.reshape(4, s.Hk), mf.reshape(4, s.NG_ffn), s.D, s.Hq, s.Hk, s.d,
+                                   s.G_ffn, s.Tk)
+    assert int(ma.sum()) == 4 * s.Hk // 2     # "half" rule: every token keeps exactly half

@@ -424,3 +424,9 @@ def test_work_counts():
     nb = ref.decode_bytes([1] * 4 + [0] * 4, [1] * 56 + [0] * 56, s.D, s.Hq, s.Hk, s.d, s.G_ffn, s.Tk)
     assert nb == 4 * (2 * 2 * 512 * 4096 + 2 * 2 * 16384 * 128) + 56 * 2 * 3 * 128 * 4096
     assert abs(nb / 1e6 - 243.27) < 0.01
+    # two sequences: group weights are read once for the union of the tokens'
+    # groups, K/V once per (sequence, kept group)
+    nb2 = ref.decode_bytes([[1, 1, 0, 0], [0, 1, 1, 0]], [[1, 0, 0], [1, 1, 0]], D=64, Hq=8, Hk=4, d=16,
+                           G_ffn=32, Tk=10)
+    G_attn = 2 * 16
+    assert nb2 == 3 * 2 * 2 * G_attn * 64 + 4 * 2 * 2 * 10 * 16 + 2 * 2 * 3 * 32 * 64
