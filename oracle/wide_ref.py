@@ -31,6 +31,9 @@ Readings of the page where it is silent (each restated where used):
 * The activation phi of Eq. 3 is SiLU (SwiGLU FFN).
 * A query row with no valid key outputs 0 (the online softmax leaves its state
   at zero, Appendix B, implementation of attention).
+* The router's reshape of 2 N_G logits into N_G pairs takes consecutive
+  entries (2g, 2g + 1), and an argmax tie keeps class 0, so the group runs
+  (section 3.1 Eq. 4 and 5).
 
 Every function is pinned by ``tests/test_oracle.py`` against closed forms,
 library routines, the page's naive gather-scatter formulations (Appendix A),
@@ -290,6 +293,31 @@ def attn_layer(X_bits, Wq_bits, K_bits, V_bits, Wo_bits, mask_attn,
 # ---------------------------------------------------------------------------
 # Work counts (algorithmic FLOPs and bytes of the routed operators)
 # ---------------------------------------------------------------------------
+
+
+def router_logits(X_bits, W1_bits, W2_bits) -> np.ndarray:
+    """The bottleneck router's logits, section 3.1 "Routing Components", Eq. 4:
+    R = reshape(X W1 W2) to [M][N_G][2].
+
+    X [M][D]; the page's W1 (D x r) and W2 (r x 2 N_G) arrive in this
+    library's weight convention, [out][in]: W1_bits [r][D] and W2_bits
+    [2 N_G][r]. The reshape of each row's 2 N_G logits to N_G pairs takes
+    consecutive entries: pair g is (column 2g, column 2g + 1), classes 0 and 1.
+    """
+    x = from_bf16(X_bits)
+    w1 = from_bf16(W1_bits)
+    w2 = from_bf16(W2_bits)
+    R = (x @ w1.T) @ w2.T                     # [M][2 N_G]
+    return R.reshape(R.shape[0], -1, 2)
+
+
+def router_mask(X_bits, W1_bits, W2_bits) -> np.ndarray:
+    """Inference routing decision, section 3.1 Eq. 5: group g of token m is
+    executed (mask 1) when the argmax over the two classes of R[m, g] is class
+    0. A tie keeps class 0, the first maximum (numpy's argmax convention).
+    Returns uint8 [M][N_G]."""
+    R = router_logits(X_bits, W1_bits, W2_bits)
+    return (np.argmax(R, axis=-1) == 0).astype(np.uint8)
 
 
 def flops_gemm_mn(mask2d, K: int, G: int) -> int:

@@ -430,3 +430,70 @@ def test_work_counts():
                            G_ffn=32, Tk=10)
     G_attn = 2 * 16
     assert nb2 == 3 * 2 * 2 * G_attn * 64 + 4 * 2 * 2 * 10 * 16 + 2 * 2 * 3 * 32 * 64
+
+
+# ---------------------------------------------------------------------------
+# Router (section 3.1, Eq. 4 and 5)
+# ---------------------------------------------------------------------------
+
+def _router_inputs(seed, M=7, D=40, r=4, NG=5):
+    X = wl.random_bf16(seed, (M, D))
+    W1 = wl.random_bf16(seed + 1, (r, D), D ** -0.5)
+    W2 = wl.random_bf16(seed + 2, (2 * NG, r), r ** -0.5)
+    return X, W1, W2
+
+
+def test_router_logits_brute_force():
+    """Element-by-element loops over the page's formula: R[m, g, c] is the
+    product X W1 W2 at output column 2g + c (W1 [D][r] and W2 [r][2 N_G] in the
+    page's orientation, i.e. the transposes of the stored arrays)."""
+    X, W1, W2 = _router_inputs(200)
+    x, w1, w2 = ref.from_bf16(X), ref.from_bf16(W1), ref.from_bf16(W2)
+    M, D = x.shape
+    r, NG = w1.shape[0], w2.shape[0] // 2
+    R = ref.router_logits(X, W1, W2)
+    assert R.shape == (M, NG, 2)
+    for m in range(M):
+        h = [sum(x[m, k] * w1[j, k] for k in range(D)) for j in range(r)]
+        for g in range(NG):
+            for c in range(2):
+                want = sum(h[j] * w2[2 * g + c, j] for j in range(r))
+                assert abs(R[m, g, c] - want) <= 1e-12 * (1 + abs(want))
+
+
+def test_router_mask_decision_rule():
+    X, W1, W2 = _router_inputs(210, M=50, NG=9)
+    R = ref.router_logits(X, W1, W2)
+    mask = ref.router_mask(X, W1, W2)
+    assert mask.dtype == np.uint8 and mask.shape == (50, 9)
+    assert np.array_equal(mask, (R[..., 0] >= R[..., 1]).astype(np.uint8))
+    assert 0 < mask.mean() < 1
+
+
+def test_router_ties_execute_and_swaps_flip():
+    X, W1, W2 = _router_inputs(220, M=30, NG=6)
+    tied = W2.copy()
+    tied[1::2] = tied[0::2]                       # class 1 logits equal class 0: every pair ties
+    assert ref.router_mask(X, W1, tied).all()      # a tie keeps class 0: executed
+    swapped = W2.copy()
+    swapped[0::2], swapped[1::2] = W2[1::2], W2[0::2]
+    R = ref.router_logits(X, W1, W2)
+    strict = R[..., 0] != R[..., 1]
+    assert np.array_equal(ref.router_mask(X, W1, swapped)[strict], 1 - ref.router_mask(X, W1, W2)[strict])
+
+
+def test_router_antisymmetric_pairs_are_a_sign_test():
+    """With W2 row 2g+1 = -(row 2g), the decision is R[m, g, 0] >= 0, i.e. the
+    sign of (X W1) w_g."""
+    X, W1, W2 = _router_inputs(230, M=40, NG=7)
+    anti = W2.copy()
+    anti[1::2] = anti[0::2] ^ np.uint16(0x8000)   # negate the bf16 values exactly
+    h = ref.from_bf16(X) @ ref.from_bf16(W1).T
+    want = (h @ ref.from_bf16(W2[0::2]).T >= 0).astype(np.uint8)
+    assert np.array_equal(ref.router_mask(X, W1, anti), want)
+
+
+def test_router_mask_invariant_to_positive_scaling():
+    X, W1, W2 = _router_inputs(240, M=40, NG=7)
+    X2 = wl.f32_to_bf16_bits(ref.from_bf16(X).astype(np.float32) * np.float32(4.0))  # exact power of two
+    assert np.array_equal(ref.router_mask(X2, W1, W2), ref.router_mask(X, W1, W2))
