@@ -178,6 +178,32 @@ int wide_attn(const wide_bf16 *Q, const wide_bf16 *K, const wide_bf16 *V, void *
               const int32_t *perm, const int32_t *counts, const uint8_t *mask,
               void *workspace, size_t workspace_bytes, wide_stream_t stream);
 
+/*
+ * wide_router -- the bottleneck router of one layer and its routing decision
+ * (section 3.1 "Routing Components", Eq. 4 and 5), optionally followed by the
+ * mask reordering of wide_reorder, all on the device.
+ *
+ *   H = X W1^T (fp32), R[m][2g + c] = sum_j H[m][j] * W2[2g + c][j] (fp32,
+ *   j in order), mask[m][g] = 1 (the group runs) iff R[m][2g] >= R[m][2g+1]:
+ *   class 0 is the argmax, a tie included.
+ *
+ *   X  [batch * rows][D] bf16, leading dim ldx (ldx >= D, a multiple of 8).
+ *   W1 [r][D] bf16, contiguous: the page's W1 (D x r) transposed into this
+ *      library's [out][in] convention. r is 16, 32, 48 or 64.
+ *   W2 [2 * groups][r] bf16, contiguous: the page's W2 (r x 2 N_G) transposed;
+ *      rows 2g and 2g + 1 are the two classes of group g.
+ *   mask   out [batch][rows][groups] uint8 (0 or 1), always written.
+ *   logits out [batch * rows][2 * groups] fp32, or NULL.
+ *   perm, counts: out, or both NULL; when given, the reorder of the mask just
+ *      written, as wide_reorder(mask, batch, rows, groups, perm, counts).
+ * Requirements: D % 8 == 0; 16-byte aligned X, W1, W2, logits; groups * r <=
+ * 16384; (batch * rows) * ldx * 2 < 2^31; outputs overlap no input.
+ */
+int wide_router(const wide_bf16 *X, int64_t ldx, const wide_bf16 *W1, const wide_bf16 *W2,
+                int64_t batch, int64_t rows, int64_t D, int64_t r, int64_t groups,
+                uint8_t *mask, float *logits, int32_t *perm, int32_t *counts,
+                wide_stream_t stream);
+
 /* Bytes of device workspace wide_attn needs for these sizes (0 if none). */
 size_t wide_attn_workspace_bytes(int64_t B, int64_t Tq, int64_t Tk, int64_t Hq,
                                  int64_t Hk, int64_t d);

@@ -34,6 +34,8 @@ _SIGS = {
     "wide_gemm_k": [_ptr, _i64, _ptr, _i64, _ptr, _i64, _int, _i64, _i64, _i64, _i64, _ptr, _ptr],
     "wide_attn": [_ptr, _ptr, _ptr, _ptr, _int, _i64, _i64, _i64, _i64, _i64, _i64, _int, _f32,
                   _ptr, _ptr, _ptr, _ptr, _ptr, _size, _ptr],
+    "wide_router": [_ptr, _i64, _ptr, _ptr, _i64, _i64, _i64, _i64, _i64, _ptr, _ptr, _ptr, _ptr,
+                    _ptr],
     "wide_attn_workspace_bytes": [_i64] * 6,
     "wide_status_string": [_int],
     "wide_abi_version": [],
@@ -132,6 +134,35 @@ def reorder(mask: torch.Tensor, perm: Optional[torch.Tensor] = None,
         raise ValueError("perm/counts must be contiguous")
     _call("wide_reorder", _p(mask), B, T, NG, _p(perm), _p(counts), _stream())
     return perm, counts
+
+
+def router(X: torch.Tensor, W1: torch.Tensor, W2: torch.Tensor, B: int = 1,
+           with_logits: bool = False, with_reorder: bool = True):
+    """Bottleneck router and routing decision, then (optionally) the reorder.
+
+    X [B*T][D] bf16; W1 [r][D] and W2 [2*NG][r] bf16, contiguous. Returns
+    (mask [B][T][NG] uint8, perm, counts, logits) with perm/counts None unless
+    with_reorder and logits ([B*T][2*NG] fp32) None unless with_logits."""
+    _need(X, "X", torch.bfloat16, 2)
+    _need(W1, "W1", torch.bfloat16, 2)
+    _need(W2, "W2", torch.bfloat16, 2)
+    if not (W1.is_contiguous() and W2.is_contiguous()):
+        raise ValueError("W1 and W2 must be contiguous")
+    M, D = X.shape
+    r = W1.shape[0]
+    if W1.shape[1] != D or W2.shape[1] != r or W2.shape[0] % 2:
+        raise ValueError("router shapes disagree")
+    if M % B:
+        raise ValueError("rows of X must be a multiple of B")
+    T, NG = M // B, W2.shape[0] // 2
+    dev = X.device
+    mask = torch.empty((B, T, NG), dtype=torch.uint8, device=dev)
+    logits = torch.empty((M, 2 * NG), dtype=torch.float32, device=dev) if with_logits else None
+    perm = torch.empty((B, NG, T), dtype=torch.int32, device=dev) if with_reorder else None
+    counts = torch.empty((B, NG), dtype=torch.int32, device=dev) if with_reorder else None
+    _call("wide_router", _p(X), _rowmajor(X, "X"), _p(W1), _p(W2), B, T, D, r, NG, _p(mask),
+          _p(logits), _p(perm), _p(counts), _stream())
+    return mask, perm, counts, logits
 
 
 def _mn_common(A, G, perm, counts, mask):

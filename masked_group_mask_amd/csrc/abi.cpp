@@ -147,6 +147,40 @@ int wide_gemm_k(const wide_bf16 *A, int64_t lda, const wide_bf16 *B, int64_t ldb
   return wide::launch_gemm_k(a, reinterpret_cast<hipStream_t>(stream));
 }
 
+int wide_router(const wide_bf16 *X, int64_t ldx, const wide_bf16 *W1, const wide_bf16 *W2,
+                int64_t batch, int64_t rows, int64_t D, int64_t r, int64_t groups, uint8_t *mask,
+                float *logits, int32_t *perm, int32_t *counts, wide_stream_t stream) {
+  if (!X || !W1 || !W2 || !mask || (perm == nullptr) != (counts == nullptr)) return WIDE_ERR_INVALID_ARG;
+  if (batch < 1 || rows < 1 || D < 1 || groups < 1 || batch > 65535) return WIDE_ERR_INVALID_ARG;
+  if (rows > kI32Max || D > kI32Max || groups > kI32Max) return WIDE_ERR_INVALID_ARG;
+  const int64_t M = batch * rows;
+  if (M > kI32Max || D % 8 != 0 || ldx < D || ldx % 8 != 0) return WIDE_ERR_INVALID_ARG;
+  if (r != 16 && r != 32 && r != 48 && r != 64) return WIDE_ERR_UNSUPPORTED;
+  if (!aligned16(X) || !aligned16(W1) || !aligned16(W2) || (logits && !aligned16(logits)))
+    return WIDE_ERR_INVALID_ARG;
+  if (groups * r > 16384) return WIDE_ERR_UNSUPPORTED;  // W2 staged in 64 KB of LDS
+  if ((uint64_t)M * (uint64_t)ldx * 2u > 0x7fffffffull || (uint64_t)r * (uint64_t)D * 2u > 0x7fffffffull)
+    return WIDE_ERR_UNSUPPORTED;  // 32-bit byte offsets
+  const size_t xb = span_bytes(M, D, ldx, 2), w1b = (size_t)r * D * 2, w2b = (size_t)2 * groups * r * 2;
+  const size_t mb = (size_t)M * groups, lb = (size_t)M * groups * 2 * 4;
+  const size_t pb = (size_t)M * groups * 4, cb = (size_t)batch * groups * 4;
+  const void *ins[3] = {X, W1, W2};
+  const size_t insz[3] = {xb, w1b, w2b};
+  for (int i = 0; i < 3; ++i) {
+    if (overlap(mask, mb, ins[i], insz[i]) || (logits && overlap(logits, lb, ins[i], insz[i])) ||
+        (perm && (overlap(perm, pb, ins[i], insz[i]) || overlap(counts, cb, ins[i], insz[i]))))
+      return WIDE_ERR_INVALID_ARG;
+  }
+  if ((logits && overlap(logits, lb, mask, mb)) ||
+      (perm && (overlap(perm, pb, mask, mb) || overlap(counts, cb, mask, mb) || overlap(counts, cb, perm, pb) ||
+                (logits && (overlap(perm, pb, logits, lb) || overlap(counts, cb, logits, lb))))))
+    return WIDE_ERR_INVALID_ARG;
+  if (!device_ok()) return WIDE_ERR_NO_DEVICE;
+  wide::RouterArgs a{X, ldx, W1, W2, (int)M, (int)D, (int)r, (int)groups, (int)batch, (int)rows,
+                     mask, logits, perm, counts};
+  return wide::launch_router(a, reinterpret_cast<hipStream_t>(stream));
+}
+
 size_t wide_attn_workspace_bytes(int64_t B, int64_t Tq, int64_t Tk, int64_t Hq, int64_t Hk,
                                  int64_t d) {
   if (B < 1 || Tq < 1 || Tk < 1 || Hq < 1 || Hk < 1 || d < 1) return 0;

@@ -77,6 +77,20 @@ struct AttnArgs {
   void *workspace;
 };
 int launch_attn(const AttnArgs &a, hipStream_t stream);
+
+struct RouterArgs {
+  const uint16_t *X;   // [M][ldx] bf16
+  int64_t ldx;
+  const uint16_t *W1;  // [r][D] bf16
+  const uint16_t *W2;  // [2 groups][r] bf16
+  int M, D, r, groups;
+  int batch, rows;     // M = batch * rows (for the reorder)
+  uint8_t *mask;       // [M][groups]
+  float *logits;       // [M][2 groups] or NULL
+  int32_t *perm;       // [batch][groups][rows] or NULL
+  int32_t *counts;     // [batch][groups] (with perm)
+};
+int launch_router(const RouterArgs &a, hipStream_t stream);
 size_t attn_workspace_bytes(int64_t B, int64_t Tq, int64_t Tk, int64_t Hq, int64_t Hk,
                             int64_t d);
 

@@ -177,6 +177,16 @@ def make_layer(s: LayerShape, seed: int = 0, parts=("attn", "ffn"),
     return out
 
 
+def router_weights(seed: int, D: int, r: int, NG: int):
+    """Seeded bottleneck-router weights in the library's [out][in] layout:
+    W1 [r][D] ~ N(0, 1/sqrt(D)) and W2 [2 NG][r] ~ N(0, 1/sqrt(r)), so that for
+    X ~ N(0, 1) the logits are O(1) and about half the groups run."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 0x5EED])))
+    w1 = normal_bf16(rng, (r, D), float(D) ** -0.5)
+    w2 = normal_bf16(rng, (2 * NG, r), float(r) ** -0.5)
+    return w1, w2
+
+
 def random_bf16(seed: int, shp, std: float = 1.0) -> np.ndarray:
     """A single seeded bf16 tensor (for unit-level tests)."""
     return normal_bf16(np.random.Generator(np.random.PCG64(seed)), shp, std)

@@ -132,6 +132,24 @@ def test_attn_validation(lib):
     assert at(lib, Tq=1, Tk=4096, perm=None, counts=None, mask=P(6), ws=P(7), wsb=need - 4) == INVALID
 
 
+def test_router_validation(lib):
+    def call(X=P(0), ldx=64, W1=P(1), W2=P(2), B=1, T=32, D=64, r=32, NG=8, mask=P(3), logits=None,
+             perm=None, counts=None):
+        return lib.wide_router(X, ldx, W1, W2, B, T, D, r, NG, mask, logits, perm, counts, None)
+    assert call(X=None) == INVALID
+    assert call(mask=None) == INVALID
+    assert call(perm=P(4)) == INVALID                 # perm without counts
+    assert call(counts=P(5)) == INVALID               # counts without perm
+    assert call(D=60, ldx=64) == INVALID              # D % 8
+    assert call(ldx=32) == INVALID                    # ldx < D
+    assert call(r=8) == UNSUPPORTED
+    assert call(r=24) == UNSUPPORTED
+    assert call(NG=1024, r=32) == UNSUPPORTED         # W2 does not fit the staging LDS
+    assert call(X=ctypes.c_void_p(FAKE + 8)) == INVALID   # misaligned
+    assert call(mask=ctypes.c_void_p(FAKE * 1 + 16)) == INVALID   # mask overlaps X
+    assert call(T=1 << 26, ldx=64) == UNSUPPORTED     # 32-bit offsets into X
+
+
 def test_valid_call_without_device_reports_no_device(lib):
     torch = pytest.importorskip("torch")
     if torch.cuda.is_available():
