@@ -132,6 +132,36 @@ def bench_decode(torch, wl, metrics, B=1, steps=50, sets=3):
     }
 
 
+def bench_router(torch, wl, s, steps=50, rank=32):
+    """The two routers of the bench layer (attention: Hk groups, FFN: NG_ffn
+    groups; rank 32, seeded weights) on the same X, each followed by its
+    reorder, as one call each. Reported beside the masked step, which starts
+    from given masks."""
+    import masked_group_mask_amd as mg
+    X = torch.randn(s.M, s.D, device="cuda").to(torch.bfloat16)
+    out = {"workload": "%s routers, rank %d, %d tokens" % (s.name, rank, s.M)}
+    per = {}
+    routers = ([("attention", s.Hk)] if s.Hk else []) + [("ffn", s.NG_ffn)]
+    for name, NG in routers:
+        w1, w2 = wl.router_weights(7, s.D, rank, NG)
+        w1 = torch.from_numpy(w1.view(np.int16)).view(torch.bfloat16).cuda()
+        w2 = torch.from_numpy(w2.view(np.int16)).view(torch.bfloat16).cuda()
+        for _ in range(3):
+            mg.router(X, w1, w2)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        hold_gpu(torch, 5.0)
+        e0.record()
+        for _ in range(steps):
+            mg.router(X, w1, w2)
+        e1.record()
+        torch.cuda.synchronize()
+        per[name] = e0.elapsed_time(e1) / steps
+    out["ms_with_reorder"] = per
+    out["x_read_GB_per_s"] = {k: s.M * s.D * 2 / (v * 1e-3) / 1e9 for k, v in per.items()}
+    return out
+
+
 def measured_traffic(op: str):
     """Bytes per launch of `op` from profiles/traffic.json (two rocprofv3
     counter passes, scaled by the same counters on a copy of known size), or
@@ -204,6 +234,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-router", action="store_true")
     ap.add_argument("--only", metavar="OP", default=None,
                     help="profiling aid: after one full masked step, run only this op --steps times")
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -292,6 +323,10 @@ def main():
         "dense_per_op_ms": dense_per_op,
         "roofline": roof,
     }
+    if not args.no_router:
+        out["router"] = bench_router(torch, wl, s)
+        log("routers (+reorder): " + ", ".join(f"{k} {v * 1e3:.1f} us"
+                                                for k, v in out["router"]["ms_with_reorder"].items()))
     if not args.no_decode:
         log("timing decode step")
         out["decode"] = bench_decode(torch, wl, metrics, B=1)
