@@ -40,6 +40,10 @@ def W():
 REORDER_CASES = [
     (1, 64, 8, 0.5), (1, 1, 3, 0.5), (1, 513, 112, 0.28), (2, 1031, 5, 0.7), (3, 700, 68, 0.5),
     (1, 4096, 64, 0.5), (1, 2000, 136, 0.0), (1, 2000, 17, 1.0), (4, 257, 8, 0.34),
+    # rows held in registers: 16 and 32 chunks of 512 rows, a ragged last
+    # chunk; then past the register budget (mask re-read per chunk)
+    (1, 8192, 136, 0.5), (2, 6000, 20, 0.5), (2, 16000, 8, 0.4), (1, 9000, 40, 0.5),
+    (1, 17000, 24, 0.5), (1, 16385, 3, 0.5),
 ]
 
 
