@@ -120,6 +120,26 @@ def test_gemm_mn_fp32(M, N, K, G):
     assert (out.cpu().numpy().view(np.uint32)[off] == 0).all(), "inactive entries were written"
 
 
+@pytest.mark.parametrize("M,N,K", [(700, 512, 1024), (257, 1280, 640), (64, 256, 256)])
+def test_depth_routing_single_group(M, N, K):
+    """M-axis (depth) routing as the one-group case of both GEMMs: each token
+    runs the whole projection or none of it (G = N for GEMM-MN, G = K for
+    GEMM-K)."""
+    A = wl.random_bf16(M + 11, (M, K))
+    B = wl.random_bf16(N + 12, (N, K), 0.05)
+    mask = wl.random_mask(M + 13, (M, 1), 0.5)
+    mask[0, 0] = 0
+    say("depth routing", M, N, K)
+    out = run_mn(A, B, mask, N, torch.float32)
+    check_gemm(f32_of(out), ref.gemm_mn(A, B, mask, N), f"depth gemm_mn {M}x{N}x{K}")
+    assert (out.cpu().numpy().view(np.uint32)[mask[:, 0] == 0] == 0).all()
+    Bk = wl.random_bf16(N + 14, (N, K), 0.05)
+    yk = W().gemm_k(to_dev(A, torch), to_dev(Bk, torch), K, to_dev(mask, torch))
+    torch.cuda.synchronize()
+    check_gemm(f32_of(yk), ref.gemm_k(A, Bk, mask, K), f"depth gemm_k {M}x{N}x{K}")
+    assert (yk.cpu().numpy()[mask[:, 0] == 0] == 0).all()
+
+
 @pytest.mark.parametrize("G", [128, 640])
 def test_gemm_mn_strided_operands(G):
     """Leading dimensions larger than the rows: A and B padded, and an odd ldc
