@@ -221,10 +221,14 @@ __global__ __launch_bounds__(64 * W) void gemm_k_kernel(KArgs a) {
 // K-groups some token keeps (one ballot per 64 groups); then each wave owns
 // one output feature and streams only the listed groups' segments of its
 // weight row, 16 bytes per lane with consecutive lanes on consecutive chunks,
-// a block of 8 chunks per lane issued before any is used.
+// a block of 8 chunks per lane issued before any is used. Every wave walks
+// the same chunk list, so a block's x chunks of every token go to LDS once
+// per workgroup (direct loads, zeros where the token does not keep the
+// group) and the products read them there.
 template <int MT>
 __global__ __launch_bounds__(256) void gemv_k_kernel(KArgs a) {
   constexpr int U = 8;
+  __shared__ __attribute__((aligned(16))) uint16_t sx[MT][U * kWave * 8];  // a block of x per token
   __shared__ uint16_t sGrp[kKMaxGroups];
   __shared__ uint8_t sOn[kKMaxGroups];
   __shared__ int sCnt[4];
@@ -268,21 +272,34 @@ __global__ __launch_bounds__(256) void gemv_k_kernel(KArgs a) {
       kk[u] = sGrp[gi] * a.G + (c % cpg) * 8;
       on[u] = ok ? sOn[gi] : 0;
     }
-    // x chunks first (cache hits), then the weight chunks, then the products.
-    u32x4 x[MT][U];
+    if (c0 > 0) __syncthreads();  // every wave is done with the previous block of x
+    // x -> LDS: instruction (m, u), u = wave, wave + 4, moves list chunks c0 + 64 u + lane
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
       const rsrc_t xr = make_rsrc(a.A + (size_t)m * a.lda, (uint64_t)a.K * 2);
 #pragma unroll
-      for (int u = 0; u < U; ++u) x[m][u] = buf_ld16(xr, (on[u] >> m) & 1 ? (uint32_t)kk[u] * 2u : kOffNone);
+      for (int i = 0; i < U / 4; ++i) {
+        const int u = wave + 4 * i;
+        int kku = kk[0], onu = on[0];
+#pragma unroll
+        for (int v = 1; v < U; ++v)
+          if (v == u) kku = kk[v], onu = on[v];
+        eng::load_lds(xr, (eng::lds_u16 *)&sx[m][u * kWave * 8], (onu >> m) & 1 ? (uint32_t)kku * 2u : kOffNone, 0u);
+      }
     }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int u = 0; u < U; ++u) w[u] = buf_ld16(wr, on[u] ? (uint32_t)kk[u] * 2u : kOffNone);
     __builtin_amdgcn_sched_barrier(0);
+    WIDE_WAIT_VM_LGKM0(U);  // this wave's x loads have landed; its weights may still be in flight
+    __syncthreads();        // and every other wave's
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int m = 0; m < MT; ++m) s[m] = dot8(w[u], x[m][u], s[m]);
+      for (int m = 0; m < MT; ++m) {
+        const u32x4 x = *(const WIDE_LDS u32x4 *)((const WIDE_LDS uint16_t *)&sx[m][0] + (u * kWave + lane) * 8);
+        s[m] = dot8(w[u], x, s[m]);
+      }
   }
 #pragma unroll
   for (int m = 0; m < MT; ++m) {

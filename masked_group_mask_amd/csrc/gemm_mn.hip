@@ -163,16 +163,20 @@ __global__ __launch_bounds__(64 * W) void gemm_mn_kernel(MnArgs a) {
 // Matrix-vector GEMM-MN for M = MT <= 4 tokens, reading the mask directly
 // (no reorder). One wave per output feature n (four per workgroup, all in one
 // group). A workgroup whose group is off for every token exits without
-// reading its weights. The weight row is streamed in 16-byte chunks
-// (consecutive lanes, consecutive chunks: whole cache lines), a whole block of
-// chunks per lane issued before any is used, so each wave keeps 8 KB per row
-// in flight; the token count is a template argument so that only MT rows of
-// x are held in registers (occupancy).
+// reading its weights. Per block of 4096 reduction elements: the block of x
+// of every token goes to LDS once per workgroup (direct loads, shared by the
+// four waves), then each lane issues its 8 16-byte weight chunks per matrix
+// (consecutive lanes, consecutive chunks: whole cache lines), and the
+// products read x from LDS once it has landed. The token count is a template
+// argument.
 template <bool SWIGLU, bool OUT_F32, int MT>
 __global__ __launch_bounds__(256) void gemv_mn_kernel(MnArgs a) {
   constexpr int U = 8;                // 16-byte chunks per lane per block
   constexpr int BLK = kWave * 8 * U;  // bf16 elements per block
-  const int n = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
+  constexpr int NW = SWIGLU ? 2 * U : U;  // weight loads per block
+  __shared__ __attribute__((aligned(16))) uint16_t sx[MT][BLK];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
+  const int n = blockIdx.x * 4 + wave;
   const int g = (blockIdx.x * 4) / a.G;
   const int NG = a.N / a.G;
   bool act[MT];
@@ -190,18 +194,21 @@ __global__ __launch_bounds__(256) void gemv_mn_kernel(MnArgs a) {
 #pragma unroll
   for (int m = 0; m < MT; ++m) s0[m] = s1[m] = 0.f;
   for (int k0 = 0; k0 < a.K; k0 += BLK) {
-    // The block's x chunks first (cache hits, shared by every wave), then the
-    // weight chunks, then the products: no load waits behind another's use.
-    u32x4 x[MT][U], w0[U], w1[U];
+    if (k0 > 0) __syncthreads();  // every wave is done with the previous block of x
+    // x -> LDS: instruction (m, u), u = wave, wave + 4, moves chunks 64 u .. 64 u + 63
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
       const rsrc_t xr = make_rsrc(a.A + (size_t)m * a.lda, (uint64_t)a.K * 2);
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
+      for (int i = 0; i < U / 4; ++i) {
+        const int u = wave + 4 * i;
         const int k = k0 + (u * kWave + lane) * 8;
-        x[m][u] = buf_ld16(xr, act[m] && k < a.K ? (uint32_t)k * 2u : kOffNone);
+        eng::load_lds(xr, (eng::lds_u16 *)&sx[m][u * kWave * 8], act[m] && k < a.K ? (uint32_t)k * 2u : kOffNone,
+                      0u);
       }
     }
+    __builtin_amdgcn_sched_barrier(0);
+    u32x4 w0[U], w1[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int k = k0 + (u * kWave + lane) * 8;
@@ -210,12 +217,15 @@ __global__ __launch_bounds__(256) void gemv_mn_kernel(MnArgs a) {
       if (SWIGLU) w1[u] = buf_ld16(w1r, off);
     }
     __builtin_amdgcn_sched_barrier(0);
+    WIDE_WAIT_VM_LGKM0(NW);  // this wave's x loads have landed; its weights may still be in flight
+    __syncthreads();         // and every other wave's
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
-        s0[m] = dot8(w0[u], x[m][u], s0[m]);
-        if (SWIGLU) s1[m] = dot8(w1[u], x[m][u], s1[m]);
+        const u32x4 x = *(const WIDE_LDS u32x4 *)((const WIDE_LDS uint16_t *)&sx[m][0] + (u * kWave + lane) * 8);
+        s0[m] = dot8(w0[u], x, s0[m]);
+        if (SWIGLU) s1[m] = dot8(w1[u], x, s1[m]);
       }
   }
 #pragma unroll
