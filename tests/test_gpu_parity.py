@@ -381,7 +381,8 @@ def test_attention_leftpad_and_bf16():
     assert (bits_of(out)[~keep] == 0).all()
 
 
-@pytest.mark.parametrize("Hq,Hk,Tk", [(32, 8, 1000), (40, 8, 4097), (8, 8, 256), (32, 4, 300), (32, 2, 130)])
+@pytest.mark.parametrize("Hq,Hk,Tk", [(32, 8, 1000), (40, 8, 4097), (8, 8, 256), (32, 4, 300), (32, 2, 130),
+                                      (8, 2, 20000)])  # the last: more than 256 splits per head
 @pytest.mark.parametrize("mode", ["mask", "counts"])
 def test_attention_decode(Hq, Hk, Tk, mode):
     B, d = 2, 128
