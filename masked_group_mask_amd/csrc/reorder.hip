@@ -117,82 +117,67 @@ __global__ __launch_bounds__(kReorderThreads) void reorder_kernel(const uint8_t 
   }
 }
 
-// The same partition with every row of the workgroup's columns held in
+// The same partition for one column per workgroup with its rows held in
 // registers (CH chunks of 512 rows, rows <= 512 CH): one round of mask loads
 // instead of one per chunk and pass. Pass 1 stores the active count of every
-// (chunk, column, wave); the counts become exclusive prefixes in LDS (chunk
-// totals scanned over chunks, then over the waves of a chunk), three
-// barriers in all; pass 2 ranks each row within its wave from the ballot it
-// recomputes from registers.
-template <int GPW, int CH>
+// (chunk, wave); the counts become exclusive prefixes in LDS (chunk totals
+// scanned over the chunks, then over the waves of a chunk), three barriers
+// in all; pass 2 ranks each row within its wave from the ballot it recomputes
+// from registers.
+template <int CH>
 __global__ __launch_bounds__(kReorderThreads) void reorder_reg_kernel(const uint8_t *__restrict__ mask,
                                                                       int rows, int groups,
                                                                       int32_t *__restrict__ perm,
                                                                       int32_t *__restrict__ counts) {
   const int b = blockIdx.y;
-  const int g0 = blockIdx.x * GPW;
-  const int ng = min(GPW, groups - g0);
+  const int g = blockIdx.x;
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
   const int lane = tid % kWave;
-  const uint8_t *mb = mask + (size_t)b * rows * groups + g0;
-  const bool aligned8 = ((groups % 8) == 0) && ((g0 % 8) == 0) &&
-                        ((reinterpret_cast<uintptr_t>(mask) % 8) == 0);
+  const uint8_t *mb = mask + (size_t)b * rows * groups + g;
 
-  __shared__ int s_c[CH][GPW][kReorderWaves];  // counts, then exclusive prefixes
-  __shared__ int s_pre[CH + 1][GPW];           // active rows before chunk i
+  __shared__ int s_c[CH][kReorderWaves];  // counts, then exclusive prefixes
+  __shared__ int s_pre[CH + 1];           // active rows before chunk i; the total last
 
-  uint64_t v[CH];  // byte j = column g0 + j of row i * 512 + tid
+  bool v[CH];  // row i * 512 + tid is active
 #pragma unroll
   for (int i = 0; i < CH; ++i) {
-    uint8_t by[GPW];
     const int r = i * kReorderThreads + tid;
-    load_mask_bytes<GPW>(mb + (size_t)r * groups, ng, aligned8, r < rows, by);
-    uint64_t w = 0;
-#pragma unroll
-    for (int j = 0; j < GPW; ++j) w |= (uint64_t)(by[j] != 0) << (8 * j);
-    v[i] = w;
+    v[i] = r < rows && mb[(size_t)r * groups] != 0;
   }
 #pragma unroll
-  for (int i = 0; i < CH; ++i)
-#pragma unroll
-    for (int j = 0; j < GPW; ++j) {
-      const int c = __popcll(__ballot((v[i] >> (8 * j)) & 1));
-      if (lane == 0) s_c[i][j][wave] = c;
-    }
+  for (int i = 0; i < CH; ++i) {
+    const int c = __popcll(__ballot(v[i]));
+    if (lane == 0) s_c[i][wave] = c;
+  }
   __syncthreads();
-  if (tid < GPW) {
+  if (tid == 0) {
     int run = 0;
     for (int i = 0; i < CH; ++i) {
-      s_pre[i][tid] = run;
-      for (int w = 0; w < kReorderWaves; ++w) run += s_c[i][tid][w];
+      s_pre[i] = run;
+      for (int w = 0; w < kReorderWaves; ++w) run += s_c[i][w];
     }
-    s_pre[CH][tid] = run;
-    if (tid < ng) counts[(size_t)b * groups + g0 + tid] = run;
+    s_pre[CH] = run;
+    counts[(size_t)b * groups + g] = run;
   }
   __syncthreads();
-  for (int k = tid; k < CH * GPW; k += kReorderThreads) {
-    const int i = k / GPW, j = k % GPW;
-    int acc = s_pre[i][j];
+  for (int i = tid; i < CH; i += kReorderThreads) {
+    int acc = s_pre[i];
     for (int w = 0; w < kReorderWaves; ++w) {
-      const int c = s_c[i][j][w];
-      s_c[i][j][w] = acc;
+      const int c = s_c[i][w];
+      s_c[i][w] = acc;
       acc += c;
     }
   }
   __syncthreads();
+  int32_t *pg = perm + ((size_t)b * groups + g) * rows;
 #pragma unroll
   for (int i = 0; i < CH; ++i) {
     const int r = i * kReorderThreads + tid;
-#pragma unroll
-    for (int j = 0; j < GPW; ++j) {
-      const bool act = (v[i] >> (8 * j)) & 1;
-      const uint64_t bal = __ballot(act);
-      if (r < rows && j < ng) {
-        const int before = s_c[i][j][wave] + rank_below(bal);
-        const int pos = act ? before : s_pre[CH][j] + (r - before);
-        perm[((size_t)b * groups + g0 + j) * rows + pos] = r;
-      }
+    const uint64_t bal = __ballot(v[i]);
+    if (r < rows) {
+      const int before = s_c[i][wave] + rank_below(bal);
+      pg[v[i] ? before : s_pre[CH] + (r - before)] = r;
     }
   }
 }
@@ -206,11 +191,11 @@ int launch_reorder(const uint8_t *mask, int batch, int rows, int groups, int32_t
     // against 2, 4 and 8 columns per workgroup: fastest at every size tried.
     const dim3 grid(groups, batch);
     if (rows <= 8 * kReorderThreads)
-      hipLaunchKernelGGL((reorder_reg_kernel<1, 8>), grid, block, 0, stream, mask, rows, groups, perm, counts);
+      hipLaunchKernelGGL(reorder_reg_kernel<8>, grid, block, 0, stream, mask, rows, groups, perm, counts);
     else if (rows <= 16 * kReorderThreads)
-      hipLaunchKernelGGL((reorder_reg_kernel<1, 16>), grid, block, 0, stream, mask, rows, groups, perm, counts);
+      hipLaunchKernelGGL(reorder_reg_kernel<16>, grid, block, 0, stream, mask, rows, groups, perm, counts);
     else
-      hipLaunchKernelGGL((reorder_reg_kernel<1, 32>), grid, block, 0, stream, mask, rows, groups, perm, counts);
+      hipLaunchKernelGGL(reorder_reg_kernel<32>, grid, block, 0, stream, mask, rows, groups, perm, counts);
   } else if (groups >= 16) {
     const dim3 grid((groups + 7) / 8, batch);
     hipLaunchKernelGGL(reorder_kernel<8>, grid, block, 0, stream, mask, rows, groups, perm, counts);
