@@ -162,6 +162,46 @@ def bench_router(torch, wl, s, steps=50, rank=32):
     return out
 
 
+def bench_torch_dense(torch, s, ours_dense_ms: dict, steps=10, warmup=3):
+    """Context row: the layer's dense bf16 GEMMs through torch (hipBLASLt),
+    beside this library's kernels run on all-ones masks (the all-ones
+    overhead; the page reports 98.60% of dense throughput at 0% sparsity).
+    Attention is not compared. gate/up is two GEMMs plus torch's SiLU and
+    product."""
+    import torch.nn.functional as F
+    dev = "cuda"
+    r = lambda *shp: torch.randn(*shp, device=dev).to(torch.bfloat16)  # noqa: E731
+    X = r(s.M, s.D)
+    O = r(s.M, s.Hq * s.d)
+    H = r(s.M, s.Dff)
+    Wq, Wo = r(s.Hq * s.d, s.D) * 0.02, r(s.D, s.Hq * s.d) * 0.02
+    Wg, Wu, Wd = r(s.Dff, s.D) * 0.02, r(s.Dff, s.D) * 0.02, r(s.D, s.Dff) * 0.02
+    ops = {
+        "q_proj": lambda: F.linear(X, Wq),
+        "o_proj": lambda: F.linear(O, Wo),
+        "gate_up_swiglu": lambda: F.silu(F.linear(X, Wg)) * F.linear(X, Wu),
+        "down_proj": lambda: F.linear(H, Wd),
+    }
+    per = {}
+    for name, fn in ops.items():
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        per[name] = e0.elapsed_time(e1) / steps
+    return {
+        "what": "torch F.linear (hipBLASLt) dense bf16 GEMMs of the same layer; attention not compared",
+        "per_op_ms": per,
+        "library_all_ones_ms": {k: ours_dense_ms[k] for k in per},
+        "library_throughput_vs_torch": {k: per[k] / ours_dense_ms[k] for k in per},
+    }
+
+
 def measured_traffic(op: str):
     """Bytes per launch of `op` from profiles/traffic.json (two rocprofv3
     counter passes, scaled by the same counters on a copy of known size), or
@@ -235,6 +275,7 @@ def main():
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-router", action="store_true")
+    ap.add_argument("--no-torch-dense", action="store_true")
     ap.add_argument("--only", metavar="OP", default=None,
                     help="profiling aid: after one full masked step, run only this op --steps times")
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -323,6 +364,9 @@ def main():
         "dense_per_op_ms": dense_per_op,
         "roofline": roof,
     }
+    if not args.no_dense and not args.no_torch_dense and s.Hq:
+        out["torch_dense"] = bench_torch_dense(torch, s, out["dense_per_op_ms"])
+        log("torch dense GEMMs (ms): " + ", ".join(f"{k} {v:.3f}" for k, v in out["torch_dense"]["per_op_ms"].items()))
     if not args.no_router:
         out["router"] = bench_router(torch, wl, s)
         log("routers (+reorder): " + ", ".join(f"{k} {v * 1e3:.1f} us"
