@@ -52,7 +52,10 @@ def time_steps(layer, which, steps, warmup, torch):
     wall = time.perf_counter() - t0
     per_op = {op: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(steps)]))
               for j, op in enumerate(PREFILL_OPS)}
-    return wall / steps * 1e3, per_op
+    step_ms = [evs[i][0].elapsed_time(evs[i][-1]) for i in range(steps)]
+    spread = {"p10": float(np.percentile(step_ms, 10)), "median": float(np.median(step_ms)),
+              "p90": float(np.percentile(step_ms, 90))}
+    return wall / steps * 1e3, per_op, spread
 
 
 def hold_gpu(torch, ms: float) -> None:
@@ -257,7 +260,14 @@ def cpu_baseline(s, host, rows: int):
           + 2 * metrics.gemm_mn_flops(mf, s.D, s.G_ffn) + metrics.gemm_k_flops(mf, s.D, s.G_ffn))
     rep = s.Hq // s.Hk
     fl += int(sum(4 * s.d * rep * int(ma[i].sum()) * (int(t) + 1) for i, t in enumerate(sel)))
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), cpu)
+    except OSError:
+        pass
     return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "cpu": cpu, "blas": np.show_config(mode="dicts").get("Build Dependencies", {}).get("blas", {}).get("name", "?"),
             "sample": f"{len(sel)} of {s.M} token rows of the same layer (all routed ops, float64), {dt:.1f} s",
             "seconds": dt}
 
@@ -330,11 +340,11 @@ def main():
         return
 
     log("timing masked layer")
-    ms, per_op = time_steps(layer, "masked", args.steps, args.warmup, torch)
+    ms, per_op, spread = time_steps(layer, "masked", args.steps, args.warmup, torch)
     log(f"masked: {ms:.3f} ms/step  " + " ".join(f"{k}={v:.3f}" for k, v in per_op.items()))
     dense_ms, dense_per_op = (None, None)
     if not args.no_dense:
-        dense_ms, dense_per_op = time_steps(layer, "dense", args.steps, args.warmup, torch)
+        dense_ms, dense_per_op, _ = time_steps(layer, "dense", args.steps, args.warmup, torch)
         log(f"dense:  {dense_ms:.3f} ms/step  " + " ".join(f"{k}={v:.3f}" for k, v in dense_per_op.items()))
 
     value = total_flops / (ms * 1e-3) / 1e12
@@ -360,6 +370,7 @@ def main():
         "dense_ms_per_step": dense_ms,
         "active_gflop_per_step": total_flops / 1e9,
         "per_op_ms": per_op,
+        "step_ms_events": spread,
         "per_op_tflops": {k: flops[k] / (per_op[k] * 1e-3) / 1e12 for k in flops},
         "dense_per_op_ms": dense_per_op,
         "roofline": roof,
