@@ -204,6 +204,24 @@ int wide_router(const wide_bf16 *X, int64_t ldx, const wide_bf16 *W1, const wide
                 uint8_t *mask, float *logits, int32_t *perm, int32_t *counts,
                 wide_stream_t stream);
 
+/*
+ * wide_attn_grouped -- wide_attn with routing groups finer than the KV heads
+ * (the page's sub-GQA granularity, section 3.1: G_attn = (Hq/groups) * d,
+ * down to one query head per group). `groups` is a multiple of Hk that
+ * divides Hq; query head h is gated by routing group h / (Hq/groups) and
+ * still reads KV head h / (Hq/Hk). mask is [B][Tq][groups]; perm and counts
+ * are wide_reorder(mask, B, Tq, groups, ...) output ([B][groups][Tq] and
+ * [B][groups]). groups = Hk is exactly wide_attn. Other arguments, output
+ * rules, requirements and errors as wide_attn; WIDE_ERR_INVALID_ARG when
+ * groups is not a multiple of Hk dividing Hq.
+ */
+int wide_attn_grouped(const wide_bf16 *Q, const wide_bf16 *K, const wide_bf16 *V, void *O,
+                      int o_dtype, int64_t B, int64_t Tq, int64_t Tk, int64_t Hq, int64_t Hk,
+                      int64_t groups, int64_t d, int causal, float scale,
+                      const int32_t *leftpad, const int32_t *perm, const int32_t *counts,
+                      const uint8_t *mask, void *workspace, size_t workspace_bytes,
+                      wide_stream_t stream);
+
 /* Bytes of device workspace wide_attn needs for these sizes (0 if none). */
 size_t wide_attn_workspace_bytes(int64_t B, int64_t Tq, int64_t Tk, int64_t Hq,
                                  int64_t Hk, int64_t d);

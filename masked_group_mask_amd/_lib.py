@@ -36,6 +36,8 @@ _SIGS = {
                   _ptr, _ptr, _ptr, _ptr, _ptr, _size, _ptr],
     "wide_router": [_ptr, _i64, _ptr, _ptr, _i64, _i64, _i64, _i64, _i64, _ptr, _ptr, _ptr, _ptr,
                     _ptr],
+    "wide_attn_grouped": [_ptr, _ptr, _ptr, _ptr, _int, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _int,
+                          _f32, _ptr, _ptr, _ptr, _ptr, _ptr, _size, _ptr],
     "wide_attn_workspace_bytes": [_i64] * 6,
     "wide_status_string": [_int],
     "wide_abi_version": [],
@@ -258,8 +260,10 @@ def attn(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, perm: Optional[torch
          counts: Optional[torch.Tensor] = None, mask: Optional[torch.Tensor] = None,
          causal: bool = True, scale: float = 0.0, leftpad: Optional[torch.Tensor] = None,
          out: Optional[torch.Tensor] = None, out_dtype=torch.bfloat16,
-         workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Head-group-masked GQA attention; Q [B][Tq][Hq][d], K/V [B][Tk][Hk][d]."""
+         workspace: Optional[torch.Tensor] = None, groups: Optional[int] = None) -> torch.Tensor:
+    """Head-group-masked GQA attention; Q [B][Tq][Hq][d], K/V [B][Tk][Hk][d].
+    groups: routing groups (default Hk); finer groups gate fewer query heads
+    each (mask [B][Tq][groups], perm/counts from reorder of that mask)."""
     for t, n in ((Q, "Q"), (K, "K"), (V, "V")):
         _need(t, n, torch.bfloat16, 4)
         if not t.is_contiguous():
@@ -282,7 +286,12 @@ def attn(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, perm: Optional[torch
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=Q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _call("wide_attn", _p(Q), _p(K), _p(V), _p(out), _dt(out.dtype), B, Tq, Tk, Hq, Hk, d,
-          int(bool(causal)), float(scale), _p(leftpad), _p(perm), _p(counts), _p(mask),
-          _p(workspace), ws_bytes, _stream())
+    if groups is None or groups == Hk:
+        _call("wide_attn", _p(Q), _p(K), _p(V), _p(out), _dt(out.dtype), B, Tq, Tk, Hq, Hk, d,
+              int(bool(causal)), float(scale), _p(leftpad), _p(perm), _p(counts), _p(mask),
+              _p(workspace), ws_bytes, _stream())
+    else:
+        _call("wide_attn_grouped", _p(Q), _p(K), _p(V), _p(out), _dt(out.dtype), B, Tq, Tk, Hq, Hk,
+              int(groups), d, int(bool(causal)), float(scale), _p(leftpad), _p(perm), _p(counts),
+              _p(mask), _p(workspace), ws_bytes, _stream())
     return out

@@ -187,15 +187,16 @@ size_t wide_attn_workspace_bytes(int64_t B, int64_t Tq, int64_t Tk, int64_t Hq, 
   return wide::attn_workspace_bytes(B, Tq, Tk, Hq, Hk, d);
 }
 
-int wide_attn(const wide_bf16 *Q, const wide_bf16 *K, const wide_bf16 *V, void *O, int o_dtype,
-              int64_t B, int64_t Tq, int64_t Tk, int64_t Hq, int64_t Hk, int64_t d, int causal,
-              float scale, const int32_t *leftpad, const int32_t *perm, const int32_t *counts,
-              const uint8_t *mask, void *workspace, size_t workspace_bytes,
-              wide_stream_t stream) {
+int wide_attn_grouped(const wide_bf16 *Q, const wide_bf16 *K, const wide_bf16 *V, void *O, int o_dtype,
+                      int64_t B, int64_t Tq, int64_t Tk, int64_t Hq, int64_t Hk, int64_t groups, int64_t d,
+                      int causal, float scale, const int32_t *leftpad, const int32_t *perm,
+                      const int32_t *counts, const uint8_t *mask, void *workspace, size_t workspace_bytes,
+                      wide_stream_t stream) {
   if (!Q || !K || !V || !O) return WIDE_ERR_INVALID_ARG;
   if (B < 1 || Tq < 1 || Tk < 1 || Hq < 1 || Hk < 1 || d < 1) return WIDE_ERR_INVALID_ARG;
   if (B > 65535 || Hq > 65535 || Tq > kI32Max || Tk > kI32Max) return WIDE_ERR_INVALID_ARG;
   if (Hq % Hk != 0 || Tk < Tq || !valid_dtype(o_dtype)) return WIDE_ERR_INVALID_ARG;
+  if (groups < Hk || groups % Hk != 0 || Hq % groups != 0) return WIDE_ERR_INVALID_ARG;
   if (causal != 0 && causal != 1) return WIDE_ERR_INVALID_ARG;
   if (!(scale >= 0.f) || !isfinite(scale)) return WIDE_ERR_INVALID_ARG;
   if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O)) return WIDE_ERR_INVALID_ARG;
@@ -229,6 +230,7 @@ int wide_attn(const wide_bf16 *Q, const wide_bf16 *K, const wide_bf16 *V, void *
   a.Tk = (int)Tk;
   a.Hq = (int)Hq;
   a.Hk = (int)Hk;
+  a.NG = (int)groups;
   a.d = (int)d;
   a.causal = causal;
   a.scale = scale == 0.f ? 1.0f / sqrtf((float)d) : scale;
@@ -238,6 +240,15 @@ int wide_attn(const wide_bf16 *Q, const wide_bf16 *K, const wide_bf16 *V, void *
   a.mask = perm ? nullptr : mask;
   a.workspace = workspace;
   return wide::launch_attn(a, reinterpret_cast<hipStream_t>(stream));
+}
+
+int wide_attn(const wide_bf16 *Q, const wide_bf16 *K, const wide_bf16 *V, void *O, int o_dtype,
+              int64_t B, int64_t Tq, int64_t Tk, int64_t Hq, int64_t Hk, int64_t d, int causal,
+              float scale, const int32_t *leftpad, const int32_t *perm, const int32_t *counts,
+              const uint8_t *mask, void *workspace, size_t workspace_bytes,
+              wide_stream_t stream) {
+  return wide_attn_grouped(Q, K, V, O, o_dtype, B, Tq, Tk, Hq, Hk, Hk, d, causal, scale, leftpad, perm,
+                           counts, mask, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -91,13 +91,14 @@ __global__ __launch_bounds__(kAThreads) void attn_prefill_kernel(AttnArgs a) {
   const int tile = ntile - 1 - (int)blockIdx.y;
   const int b = blockIdx.z;
   const int rep = a.Hq / a.Hk;
-  const int g = h / rep;
-  const int cnt = a.counts[(size_t)b * a.Hk + g];
+  const int g = h / rep;                  // KV head
+  const int grp = h / (a.Hq / a.NG);      // routing group of the head
+  const int cnt = a.counts[(size_t)b * a.NG + grp];
   const int s0 = tile * kAq;
   if (s0 >= cnt) return;  // level 0
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int c = lane % 16, q = lane / 16;
-  if (tid < kAq) sPos[tid] = s0 + tid < cnt ? a.perm[((size_t)b * a.Hk + g) * a.Tq + s0 + tid] : -1;
+  if (tid < kAq) sPos[tid] = s0 + tid < cnt ? a.perm[((size_t)b * a.NG + grp) * a.Tq + s0 + tid] : -1;
   __syncthreads();
 
   const int delta = a.Tk - a.Tq;
@@ -317,9 +318,18 @@ __global__ __launch_bounds__(kAThreads) void attn_prefill_kernel(AttnArgs a) {
 constexpr int kDecKeys = 64;       // keys per split (one wave)
 constexpr int kDecPart = kAd + 4;  // floats per partial: o[128], m, z (+pad)
 
+// Routing group g of sequence b is on for its (single) decoding token.
 __device__ __forceinline__ bool group_active(const AttnArgs &a, int b, int g) {
-  if (a.mask) return a.mask[(size_t)b * a.Hk + g] != 0;
-  return a.counts[(size_t)b * a.Hk + g] > 0;
+  if (a.mask) return a.mask[(size_t)b * a.NG + g] != 0;
+  return a.counts[(size_t)b * a.NG + g] > 0;
+}
+
+// Some routing group of KV head g (its NG / Hk groups) is on.
+__device__ __forceinline__ bool kv_head_active(const AttnArgs &a, int b, int g) {
+  const int per = a.NG / a.Hk;
+  bool on = false;
+  for (int j = 0; j < per; ++j) on |= group_active(a, b, g * per + j);
+  return on;
 }
 
 // One split = 64 keys of one active (b, g) on one wave, for all Hq/Hk heads of
@@ -339,7 +349,7 @@ __global__ __launch_bounds__(kWave) void attn_decode_split_kernel(AttnArgs a, in
   const int split = blockIdx.x;
   const int g = blockIdx.y;
   const int b = blockIdx.z;
-  if (!group_active(a, b, g)) return;  // the group is off for this token: nothing is read
+  if (!kv_head_active(a, b, g)) return;  // every head of the KV head is off: nothing is read
   const int rep = a.Hq / a.Hk;
   const int lane = threadIdx.x;
   const int q = lane / 16, c16 = lane % 16;
@@ -490,8 +500,7 @@ __global__ __launch_bounds__(kMergeThreads) void attn_decode_merge_kernel(AttnAr
   const int h = blockIdx.x;
   const int b = blockIdx.y;
   const int d0 = blockIdx.z * kMergeDims;
-  const int rep = a.Hq / a.Hk;
-  if (!group_active(a, b, h / rep)) return;
+  if (!group_active(a, b, h / (a.Hq / a.NG))) return;
   const int tid = threadIdx.x;
   const float *ws = reinterpret_cast<const float *>(a.workspace) + ((size_t)b * a.Hq + h) * nsplit * kDecPart;
   float mloc = -INFINITY;

@@ -69,6 +69,7 @@ struct AttnArgs {
   void *O;
   int o_f32;
   int B, Tq, Tk, Hq, Hk, d;
+  int NG;  // routing groups: a multiple of Hk dividing Hq; head h is gated by group h / (Hq / NG)
   int causal;
   float scale;
   const int32_t *leftpad;

@@ -184,8 +184,11 @@ def attention(Q_bits, K_bits, V_bits, mask, causal: bool = True,
               q_tile: int = 128) -> np.ndarray:
     """Head-group-masked GQA attention.
 
-    Q: [B][Tq][Hq][d]; K, V: [B][Tk][Hk][d] (bf16 bits); mask: [B][Tq][Hk].
-    Query head h uses KV head g = h // (Hq/Hk) and is gated by mask[b, t, g].
+    Q: [B][Tq][Hq][d]; K, V: [B][Tk][Hk][d] (bf16 bits); mask: [B][Tq][NG]
+    with NG routing groups, a multiple of Hk that divides Hq (NG = Hk: one
+    group per KV head, section 3.1 Eq. 2; NG > Hk: the finer sub-GQA groups,
+    down to one query head each). Query head h uses KV head h // (Hq/Hk) and
+    is gated by mask[b, t, h // (Hq/NG)].
     For an active (b, t, h) the valid keys are j in [jmin, jmax) with
     jmin = leftpad[b] (0 without leftpad) and jmax = t + (Tk - Tq) + 1 when
     causal, Tk otherwise; o = sum_j softmax_j(scale * q.k_j) v_j over the valid
@@ -203,9 +206,12 @@ def attention(Q_bits, K_bits, V_bits, mask, causal: bool = True,
     _, Tk, Hk, _ = K.shape
     if Hq % Hk:
         raise ValueError("Hq must be a multiple of Hk")
-    if mask.shape != (B, Tq, Hk):
-        raise ValueError("mask must be [B][Tq][Hk]")
+    mask = np.asarray(mask)
+    NG = mask.shape[2] if mask.ndim == 3 else -1
+    if mask.shape[:2] != (B, Tq) or NG < Hk or NG % Hk or Hq % NG:
+        raise ValueError("mask must be [B][Tq][NG] with NG a multiple of Hk dividing Hq")
     rep = Hq // Hk
+    hpg = Hq // NG  # query heads per routing group
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     delta = Tk - Tq
@@ -223,16 +229,16 @@ def attention(Q_bits, K_bits, V_bits, mask, causal: bool = True,
         for g in range(Hk):
             Kg = from_bf16(K[b, :, g, :])            # [Tk][d]
             Vg = from_bf16(V[b, :, g, :])
-            act = [(i, t) for (i, t) in items if mask[b, t, g] != 0]
-            for s0 in range(0, len(act), q_tile):
-                blk = act[s0:s0 + q_tile]
-                idx = np.array([i for i, _ in blk])
-                ts = np.array([t for _, t in blk])
-                valid = keys[None, :] >= jmin
-                if causal:
-                    valid = valid & (keys[None, :] <= ts[:, None] + delta)
-                has_key = valid.any(axis=1)
-                for h in range(g * rep, (g + 1) * rep):
+            for h in range(g * rep, (g + 1) * rep):
+                act = [(i, t) for (i, t) in items if mask[b, t, h // hpg] != 0]
+                for s0 in range(0, len(act), q_tile):
+                    blk = act[s0:s0 + q_tile]
+                    idx = np.array([i for i, _ in blk])
+                    ts = np.array([t for _, t in blk])
+                    valid = keys[None, :] >= jmin
+                    if causal:
+                        valid = valid & (keys[None, :] <= ts[:, None] + delta)
+                    has_key = valid.any(axis=1)
                     q = from_bf16(Q[b, ts, h, :])          # [n][d]
                     s = (q @ Kg.T) * scale                  # [n][Tk]
                     s = np.where(valid, s, -np.inf)

@@ -132,6 +132,15 @@ def test_attn_validation(lib):
     assert at(lib, Tq=1, Tk=4096, perm=None, counts=None, mask=P(6), ws=P(7), wsb=need - 4) == INVALID
 
 
+def test_attn_grouped_validation(lib):
+    def call(groups, Hq=8, Hk=2):
+        return lib.wide_attn_grouped(P(0), P(1), P(2), P(3), 1, 1, 16, 16, Hq, Hk, groups, 128, 1,
+                                     ctypes.c_float(0.0), None, P(4), P(5), None, None, 0, None)
+    assert call(3) == INVALID       # not a multiple of Hk
+    assert call(1) == INVALID       # fewer groups than KV heads
+    assert call(12, Hq=8) == INVALID  # does not divide Hq
+
+
 def test_router_validation(lib):
     def call(X=P(0), ldx=64, W1=P(1), W2=P(2), B=1, T=32, D=64, r=32, NG=8, mask=P(3), logits=None,
              perm=None, counts=None):

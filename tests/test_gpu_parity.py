@@ -407,6 +407,45 @@ def test_attention_decode(Hq, Hk, Tk, mode):
     assert (out.cpu().numpy().view(np.uint32)[~keep] == 0).all()
 
 
+@pytest.mark.parametrize("NG", [4, 8])   # two heads per routing group, then one
+def test_attention_sub_gqa_groups_prefill(NG):
+    """Routing groups finer than the KV heads (sub-GQA granularity): query
+    head h is gated by group h // (Hq/NG) and reads KV head h // (Hq/Hk)."""
+    B, T, Hq, Hk, d = 2, 300, 8, 2, 128
+    Q = wl.random_bf16(130, (B, T, Hq, d))
+    K = wl.random_bf16(131, (B, T, Hk, d), 0.5)
+    V = wl.random_bf16(132, (B, T, Hk, d))
+    mask = wl.random_mask(133 + NG, (B, T, NG), 0.5)
+    lp = [0, 40]
+    say("attention sub-GQA prefill", NG)
+    md = to_dev(mask, torch)
+    perm, counts = W().reorder(md)
+    out = W().attn(to_dev(Q, torch), to_dev(K, torch), to_dev(V, torch), perm=perm, counts=counts,
+                   leftpad=to_dev(np.array(lp, np.int32), torch), out_dtype=torch.float32, groups=NG)
+    torch.cuda.synchronize()
+    want = ref.attention(Q, K, V, mask, leftpad=lp)
+    check_attn(f32_of(out), want, f"sub-GQA prefill NG={NG}")
+    keep = np.repeat(mask != 0, Hq // NG, axis=2)
+    assert (out.cpu().numpy().view(np.uint32)[~keep] == 0).all()
+
+
+@pytest.mark.parametrize("NG", [16, 32])
+def test_attention_sub_gqa_groups_decode(NG):
+    B, Tk, Hq, Hk, d = 2, 1500, 32, 8, 128
+    Q = wl.random_bf16(140, (B, 1, Hq, d), 1.0)
+    K = wl.random_bf16(141, (B, Tk, Hk, d), 1.0)
+    V = wl.random_bf16(142, (B, Tk, Hk, d), 1.0)
+    mask = wl.random_mask(143 + NG, (B, 1, NG), 0.5)
+    say("attention sub-GQA decode", NG)
+    out = W().attn(to_dev(Q, torch), to_dev(K, torch), to_dev(V, torch), mask=to_dev(mask, torch),
+                   out_dtype=torch.float32, groups=NG)
+    torch.cuda.synchronize()
+    want = ref.attention(Q, K, V, mask)
+    check_attn(f32_of(out), want, f"sub-GQA decode NG={NG}")
+    keep = np.repeat(mask != 0, Hq // NG, axis=2)
+    assert (out.cpu().numpy().view(np.uint32)[~keep] == 0).all()
+
+
 def test_attention_decode_workspace_reuse():
     """One workspace (uninitialised) through consecutive decoding calls of
     different sizes: nothing a call leaves there may leak into the next."""

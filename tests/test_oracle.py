@@ -497,3 +497,52 @@ def test_router_mask_invariant_to_positive_scaling():
     X, W1, W2 = _router_inputs(240, M=40, NG=7)
     X2 = wl.f32_to_bf16_bits(ref.from_bf16(X).astype(np.float32) * np.float32(4.0))  # exact power of two
     assert np.array_equal(ref.router_mask(X2, W1, W2), ref.router_mask(X, W1, W2))
+
+
+# ---------------------------------------------------------------------------
+# Sub-GQA routing groups (section 3.1: G_attn down to one query head)
+# ---------------------------------------------------------------------------
+
+def _attn_inputs(seed, B=2, T=9, Hq=8, Hk=2, d=16):
+    Q = wl.random_bf16(seed, (B, T, Hq, d))
+    K = wl.random_bf16(seed + 1, (B, T, Hk, d))
+    V = wl.random_bf16(seed + 2, (B, T, Hk, d))
+    return Q, K, V
+
+
+def test_attention_finer_groups_reduce_to_kv_groups():
+    """Routing groups finer than the KV heads that all carry their KV head's
+    decision give exactly the one-group-per-KV-head result."""
+    Q, K, V = _attn_inputs(500)
+    m = wl.random_mask(501, (2, 9, 2), 0.5)
+    want = ref.attention(Q, K, V, m)
+    for NG in (4, 8):
+        fine = np.repeat(m, NG // 2, axis=2)
+        assert np.array_equal(ref.attention(Q, K, V, fine), want)
+
+
+def test_attention_per_head_mask_gates_only_its_head():
+    """With one group per query head, switching a head's group off zeroes that
+    head only; every other head equals the all-on result; flops count only
+    the heads that run."""
+    Q, K, V = _attn_inputs(510)
+    on = np.ones((2, 9, 8), np.uint8)
+    full = ref.attention(Q, K, V, on)
+    m = on.copy()
+    m[1, 4, 5] = 0
+    m[0, :, 2] = 0
+    got = ref.attention(Q, K, V, m)
+    assert (got[1, 4, 5] == 0).all() and (got[0, :, 2] == 0).all()
+    keep = np.ones_like(got, dtype=bool)
+    keep[1, 4, 5] = False
+    keep[0, :, 2] = False
+    assert np.array_equal(got[keep], full[keep])
+    assert ref.flops_attention(m, 9, 8, 16) == ref.flops_attention(on, 9, 8, 16) - 4 * 16 * (5 + sum(range(1, 10)))
+
+
+def test_attention_rejects_groups_not_aligned_to_kv_heads():
+    Q, K, V = _attn_inputs(520)
+    with pytest.raises(ValueError):
+        ref.attention(Q, K, V, np.ones((2, 9, 3), np.uint8))   # 3 groups: not a multiple of Hk = 2
+    with pytest.raises(ValueError):
+        ref.attention(Q, K, V, np.ones((2, 9, 1), np.uint8))   # fewer groups than KV heads
