@@ -6,24 +6,28 @@
 // active rows, causal key range cut at the largest active query position,
 // scatter of the normalised rows).
 //
-// Prefill: a workgroup owns (batch b, query head h, sorted query tile) of 128
-// rows taken from perm[b][g] with g = h / (Hq/Hk). Because perm lists active
+// Prefill: a workgroup owns (batch b, query head h, sorted query tile) of 256
+// rows taken from perm[b][grp] of the head's routing group grp = h / (Hq/NG)
+// (NG = Hk by default: one group per KV head; finer sub-GQA groups down to one
+// head each); the head reads KV head h / (Hq/Hk). Because perm lists active
 // rows in ascending position, the tile's last active row bounds the causal
 // key range and each wave's own last row bounds the tiles it must compute.
-// Level 0: a tile past counts[b][g] exits. Level 1: only active Q rows are
+// Level 0: a tile past counts[b][grp] exits. Level 1: only active Q rows are
 // gathered. Level 2: a wave with no active row, or whose rows all precede a
 // key tile, skips that tile's MFMAs.
 // The score tile is computed transposed, S^T = K Q^T, with
 // v_mfma_f32_16x16x32_bf16, so every lane holds one query's scores; the
 // running max, the rescale of the output and the row sums are then lane-local
 // except for two cross-lane max steps. P^T feeds the PV product straight from
-// registers; V is staged transposed in LDS. Softmax runs in fp32 with exp2 and
+// registers; V is staged in LDS as loaded and its transposed fragments come
+// from the gfx950 transposing LDS read. Softmax runs in fp32 with exp2 and
 // the scale folded with log2(e).
 //
 // Decode (Tq = 1): the reorder is bypassed and the routing byte (or count) is
-// read per (b, g). A split-KV kernel lets the Hq/Hk heads of an active group
-// share each K/V chunk and writes (max, sum, unnormalised output) partials; a
-// second kernel merges the splits with log-sum-exp weights.
+// read per (b, group). A split-KV kernel (one wave per 64 keys of a KV head)
+// serves all query heads of the KV head at once on the matrix cores and
+// writes (max, sum, unnormalised output) partials; a second kernel merges the
+// splits of each active head with log-sum-exp weights.
 #include <math.h>
 
 #include "common.hpp"

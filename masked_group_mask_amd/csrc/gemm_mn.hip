@@ -16,12 +16,14 @@
 // in the one partial tile per group and is not taken.
 //
 // The tile runs on the shared MFMA main loop: 256 sorted rows x BN weight
-// rows, BN = 256 (8 waves) when a group spans 256 of them, else 128 or 64 (4
-// waves). The fused SwiGLU variant stages BN/2 gate rows and the matching
-// BN/2 up rows and writes BN/2 outputs.
+// rows, BN = 256 or 320 (8 waves) when the group size is a multiple of it,
+// else 128 or 64 (4 waves). The fused SwiGLU variant stages BN/2 gate rows and
+// the matching BN/2 up rows (BN = 256 when G is a multiple of 128) and writes
+// BN/2 outputs.
 //
-// For M <= 4 with no reorder (one decode step), a matrix-vector kernel reads
-// the mask bytes directly and streams only the active groups' weight rows.
+// For M <= 4 with no reorder (decode steps of up to four sequences), a
+// matrix-vector kernel reads the mask bytes directly and streams only the
+// active groups' weight rows, with x shared through LDS.
 #include "common.hpp"
 #include "launch.hpp"
 #include "mma_engine.hpp"
