@@ -148,6 +148,33 @@ int wide_gemm_k(const wide_bf16 *A, int64_t lda, const wide_bf16 *B, int64_t ldb
                 int64_t G, const uint8_t *mask, wide_stream_t stream);
 
 /*
+ * wide_gemm_k_ws -- wide_gemm_k (the same product, Appendix B, Eq. 21) with a
+ * caller-owned workspace. When the 256 x 256 output tiles leave a last round
+ * on the device's compute units at most half full, each tile of that round is
+ * split into slices of K computed by separate workgroups; the workspace holds
+ * the partial tiles of all slices but the last, and a second kernel adds them
+ * into C.
+ *   workspace: device memory of at least wide_gemm_k_workspace_bytes(M, N, K)
+ *     bytes, 16-byte aligned, not overlapping A, B, C or mask. Its contents on
+ *     entry are ignored and overwritten; calls that share a workspace must not
+ *     run at the same time (e.g. on two streams). NULL, or a size of 0 when the
+ *     plan needs none, is wide_gemm_k.
+ * Results: as wide_gemm_k, bitwise reproducible for a given shape and device.
+ * A split tile's sum is C = (beta C + last slice) + slice 0 + slice 1 + ...,
+ * which rounds differently from wide_gemm_k's single pass over K.
+ * Requirements and errors as wide_gemm_k; WIDE_ERR_INVALID_ARG when a
+ * workspace is given that is smaller than needed, misaligned or overlapping.
+ */
+int wide_gemm_k_ws(const wide_bf16 *A, int64_t lda, const wide_bf16 *B, int64_t ldb,
+                   float *C, int64_t ldc, int beta, int64_t M, int64_t N, int64_t K,
+                   int64_t G, const uint8_t *mask, void *workspace, size_t workspace_bytes,
+                   wide_stream_t stream);
+
+/* Bytes of device workspace wide_gemm_k_ws needs for an M x N x K product on
+ * the current device (0: no tile is split; also 0 for sizes out of range). */
+size_t wide_gemm_k_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/*
  * wide_attn -- head-group-masked causal GQA attention (section 3.1, Eq. 2;
  * Appendix B, Algorithm 4 and its decoding paragraph).
  *

@@ -32,6 +32,9 @@ _SIGS = {
     "wide_gemm_mn_swiglu": [_ptr, _i64, _ptr, _ptr, _i64, _ptr, _i64, _int, _i64, _i64, _i64,
                             _i64, _ptr, _ptr, _ptr, _ptr],
     "wide_gemm_k": [_ptr, _i64, _ptr, _i64, _ptr, _i64, _int, _i64, _i64, _i64, _i64, _ptr, _ptr],
+    "wide_gemm_k_ws": [_ptr, _i64, _ptr, _i64, _ptr, _i64, _int, _i64, _i64, _i64, _i64, _ptr, _ptr, _size,
+                       _ptr],
+    "wide_gemm_k_workspace_bytes": [_i64] * 3,
     "wide_attn": [_ptr, _ptr, _ptr, _ptr, _int, _i64, _i64, _i64, _i64, _i64, _i64, _int, _f32,
                   _ptr, _ptr, _ptr, _ptr, _ptr, _size, _ptr],
     "wide_router": [_ptr, _i64, _ptr, _ptr, _i64, _i64, _i64, _i64, _i64, _ptr, _ptr, _ptr, _ptr,
@@ -42,7 +45,8 @@ _SIGS = {
     "wide_status_string": [_int],
     "wide_abi_version": [],
 }
-_RESTYPES = {"wide_attn_workspace_bytes": _size, "wide_status_string": ctypes.c_char_p}
+_RESTYPES = {"wide_attn_workspace_bytes": _size, "wide_gemm_k_workspace_bytes": _size,
+             "wide_status_string": ctypes.c_char_p}
 
 EXPORTED = tuple(_SIGS)
 
@@ -229,9 +233,16 @@ def gemm_mn_swiglu(A: torch.Tensor, Wg: torch.Tensor, Wu: torch.Tensor, G: int,
     return out
 
 
+def gemm_k_workspace_bytes(M: int, N: int, K: int) -> int:
+    return int(load().wide_gemm_k_workspace_bytes(M, N, K))
+
+
 def gemm_k(A: torch.Tensor, B: torch.Tensor, G: int, mask: torch.Tensor,
-           out: Optional[torch.Tensor] = None, beta: int = 0) -> torch.Tensor:
-    """C = beta*C + sum over active K-groups of A B^T (fp32 output)."""
+           out: Optional[torch.Tensor] = None, beta: int = 0,
+           workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """C = beta*C + sum over active K-groups of A B^T (fp32 output).
+    workspace: optional device buffer of gemm_k_workspace_bytes(M, N, K)
+    bytes; with it the last, partly filled round of tiles is split along K."""
     _need(A, "A", torch.bfloat16, 2)
     _need(B, "B", torch.bfloat16, 2)
     _need(mask, "mask", torch.uint8)
@@ -247,8 +258,13 @@ def gemm_k(A: torch.Tensor, B: torch.Tensor, G: int, mask: torch.Tensor,
     _need(out, "out", torch.float32, 2)
     if tuple(out.shape) != (M, N):
         raise ValueError("out shape mismatch")
-    _call("wide_gemm_k", _p(A), _rowmajor(A, "A"), _p(B), _rowmajor(B, "B"), _p(out),
-          _rowmajor(out, "out"), int(beta), M, N, K, G, _p(mask), _stream())
+    ws, wsb = None, 0
+    if workspace is not None:
+        if workspace.device != A.device or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous tensor on A's device")
+        ws, wsb = _p(workspace), workspace.numel() * workspace.element_size()
+    _call("wide_gemm_k_ws", _p(A), _rowmajor(A, "A"), _p(B), _rowmajor(B, "B"), _p(out),
+          _rowmajor(out, "out"), int(beta), M, N, K, G, _p(mask), ws, wsb, _stream())
     return out
 
 

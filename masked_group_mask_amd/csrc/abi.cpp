@@ -128,6 +128,17 @@ int wide_gemm_mn_swiglu(const wide_bf16 *A, int64_t lda, const wide_bf16 *Wg, co
 int wide_gemm_k(const wide_bf16 *A, int64_t lda, const wide_bf16 *B, int64_t ldb, float *C,
                 int64_t ldc, int beta, int64_t M, int64_t N, int64_t K, int64_t G,
                 const uint8_t *mask, wide_stream_t stream) {
+  return wide_gemm_k_ws(A, lda, B, ldb, C, ldc, beta, M, N, K, G, mask, nullptr, 0, stream);
+}
+
+size_t wide_gemm_k_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  if (M < 1 || N < 1 || K < 1 || M > kI32Max || N > kI32Max || K > kI32Max) return 0;
+  return wide::gemm_k_workspace_bytes((int)M, (int)N, (int)K);
+}
+
+int wide_gemm_k_ws(const wide_bf16 *A, int64_t lda, const wide_bf16 *B, int64_t ldb, float *C,
+                   int64_t ldc, int beta, int64_t M, int64_t N, int64_t K, int64_t G,
+                   const uint8_t *mask, void *workspace, size_t workspace_bytes, wide_stream_t stream) {
   if (!A || !B || !C || !mask) return WIDE_ERR_INVALID_ARG;
   if (M < 1 || N < 1 || K < 1 || G < 1) return WIDE_ERR_INVALID_ARG;
   if (M > kI32Max || N > kI32Max || K > kI32Max) return WIDE_ERR_INVALID_ARG;
@@ -142,8 +153,18 @@ int wide_gemm_k(const wide_bf16 *A, int64_t lda, const wide_bf16 *B, int64_t ldb
   // A tile of 256 rows and a B tile of 128 rows are addressed with 32-bit byte offsets.
   if ((uint64_t)lda * 512u > 0x7fffffffull || (uint64_t)ldb * 512u > 0x7fffffffull)
     return WIDE_ERR_UNSUPPORTED;
+  if (workspace != nullptr) {
+    const size_t need = wide::gemm_k_workspace_bytes((int)M, (int)N, (int)K);
+    if (workspace_bytes < need || !aligned16(workspace)) return WIDE_ERR_INVALID_ARG;
+    if (need > 0 && (overlap(workspace, need, A, span_bytes(M, K, lda, 2)) ||
+                     overlap(workspace, need, B, span_bytes(N, K, ldb, 2)) || overlap(workspace, need, C, cb) ||
+                     overlap(workspace, need, mask, (size_t)M * (K / G))))
+      return WIDE_ERR_INVALID_ARG;
+    if (need == 0) workspace = nullptr;
+  }
   if (!device_ok()) return WIDE_ERR_NO_DEVICE;
-  wide::KArgs a{A, lda, B, ldb, C, ldc, beta, (int)M, (int)N, (int)K, (int)G, mask, 0, 0};
+  wide::KArgs a{A, lda, B, ldb, C, ldc, beta, (int)M, (int)N, (int)K, (int)G, mask,
+                static_cast<float *>(workspace), workspace_bytes, 0, 0, 0, 1};
   return wide::launch_gemm_k(a, reinterpret_cast<hipStream_t>(stream));
 }
 

@@ -107,11 +107,11 @@ struct KLoader {
   rsrc_t ar, br, none;
   uint32_t aoff[S::AI], boff[S::BI];
   const WIDE_LDS uint32_t *bits;
-  int nk, steps_per_group, NG, wave, lane;
+  int nk, kb, steps_per_group, NG, wave, lane;  // steps kb .. kb + nk - 1 of K
   u32x4 wlo, whi;  // bit words (rows 0..127, 128..255) of the group of the next stage
 
   __device__ __forceinline__ void fetch(int t) {
-    const int g = min(t / steps_per_group, NG - 1);
+    const int g = min((t + kb) / steps_per_group, NG - 1);
     wlo = *(const WIDE_LDS u32x4 *)(bits + g * 8);
     whi = *(const WIDE_LDS u32x4 *)(bits + g * 8 + 4);
   }
@@ -130,7 +130,7 @@ struct KLoader {
     }
     const bool live = t < nk;
     const rsrc_t ra = live ? ar : none, rb = live ? br : none;
-    const uint32_t k0 = (uint32_t)t * eng::kBK * 2u;
+    const uint32_t k0 = (uint32_t)(t + kb) * eng::kBK * 2u;
 #pragma unroll
     for (int i = 0; i < S::AI; ++i)
       eng::load_lds(ra, eng::load_dst<S::WAVES>(sa, wave, i), ((p >> i) & 1u) ? aoff[i] : kOffNone, k0);
@@ -156,11 +156,19 @@ __global__ __launch_bounds__(64 * W) void gemm_k_kernel(KArgs a) {
 
   const int MT = (a.M + eng::kBM - 1) / eng::kBM;
   int mt, tn, n0;
+  int part = 0, nparts = 1, slot = 0;  // K slice of this workgroup; slot: split tile index
   if (a.split_tail) {  // half of a 256 x 256 tile of the raster
     eng::tile_of(a.tile_base + (int)blockIdx.x / 2, MT, a.N / 256, mt, tn);
     n0 = tn * 256 + ((int)blockIdx.x % 2) * BN;
   } else {
-    eng::tile_of(a.tile_base + (int)blockIdx.x, MT, a.N / BN, mt, tn);
+    int L = (int)blockIdx.x;
+    if (a.ksplit > 1 && L >= a.head) {
+      slot = (L - a.head) / a.ksplit;
+      part = (L - a.head) % a.ksplit;
+      nparts = a.ksplit;
+      L = a.head + slot;
+    }
+    eng::tile_of(a.tile_base + L, MT, a.N / BN, mt, tn);
     n0 = tn * BN;
   }
   const int m0 = mt * eng::kBM;
@@ -191,7 +199,9 @@ __global__ __launch_bounds__(64 * W) void gemm_k_kernel(KArgs a) {
       ld.boff[i] = (uint32_t)r * (uint32_t)a.ldb * 2u + eng::load_chunk_bytes(r, lane);
     }
     ld.bits = (const WIDE_LDS uint32_t *)&sBits[0][0];
-    ld.nk = a.K / eng::kBK;
+    const int nk_all = a.K / eng::kBK;
+    ld.kb = part * nk_all / nparts;
+    ld.nk = (part + 1) * nk_all / nparts - ld.kb;
     ld.steps_per_group = a.G / eng::kBK;
     ld.NG = a.K / a.G;
     ld.wave = wave;
@@ -201,8 +211,22 @@ __global__ __launch_bounds__(64 * W) void gemm_k_kernel(KArgs a) {
                                 (eng::lds_u16 *)sB1, (eng::lds_u16 *)sA2, (eng::lds_u16 *)sB2, acc, wm, wn, lane);
   }
 
-  // C = beta * C + acc; a lane holds row (lane % 16) of A fragment j and
-  // features 4 (lane / 16) .. +3 of B fragment i.
+  // A lane holds row (lane % 16) of A fragment j and features
+  // 4 (lane / 16) .. +3 of B fragment i.
+  if (part < nparts - 1) {
+    // K slices other than the last: the partial tile goes to the workspace
+    // (256 x BN fp32, row-major, one per slice), for the fixup kernel.
+    float *wt = a.ws + ((size_t)slot * (nparts - 1) + part) * (size_t)(eng::kBM * BN);
+#pragma unroll
+    for (int j = 0; j < S::FM; ++j) {
+      float *wrow = wt + (size_t)(wm * S::TM + j * 16 + lane % 16) * BN + wn * S::TN + 4 * (lane / 16);
+#pragma unroll
+      for (int i = 0; i < S::FN; ++i) *reinterpret_cast<f32x4 *>(wrow + i * 16) = acc[i][j];
+    }
+    return;
+  }
+  // C = beta * C + acc (for a K-split tile, the last slice's part; the
+  // fixup kernel adds the others).
 #pragma unroll
   for (int j = 0; j < S::FM; ++j) {
     const int m = m0 + wm * S::TM + j * 16 + lane % 16;
@@ -323,16 +347,78 @@ int cu_count() {
   return n;
 }
 
-// Tiled launches. With N a multiple of 256 the 8-wave 256 x 256 kernel runs;
-// when its tiles leave a last round at most half full (640 tiles on 256 CUs
-// run as 3 rounds, 2.5 of work), the leftover tiles are covered by twice as
-// many 256 x 128 workgroups of the 4-wave kernel in a second launch, which
-// take one round of half the length. Each output element is still computed
-// by one workgroup with a fixed summation order.
+// Second pass of the K-split tiles: adds the workspace partials of the
+// other slices to C, in slice order, so C = (beta C + last slice) + slice 0 +
+// slice 1 + ... for every run. One thread per 4 consecutive features of a
+// tile row (64 workgroups per tile).
+__global__ __launch_bounds__(256) void gemm_k_fixup_kernel(KArgs a) {
+  constexpr int Q = 256 / 4;                  // 4-feature quads per tile row
+  constexpr int PER_TILE = eng::kBM * Q / 256;  // workgroups per tile
+  constexpr size_t TILE = (size_t)eng::kBM * 256;
+  const int slot = blockIdx.x / PER_TILE;
+  const int e = (blockIdx.x % PER_TILE) * 256 + threadIdx.x;
+  const int r = e / Q, q = e % Q;
+  const int MT = (a.M + eng::kBM - 1) / eng::kBM;
+  int mt, tn;
+  eng::tile_of(a.head + slot, MT, a.N / 256, mt, tn);
+  const int m = mt * eng::kBM + r;
+  if (m >= a.M) return;
+  float *c = a.C + (size_t)m * a.ldc + tn * 256 + 4 * q;
+  f32x4 v = *reinterpret_cast<const f32x4 *>(c);
+  const float *w = a.ws + (size_t)slot * (a.ksplit - 1) * TILE + (size_t)r * 256 + 4 * q;
+  for (int p = 0; p < a.ksplit - 1; ++p) v += *reinterpret_cast<const f32x4 *>(w + p * TILE);
+  *reinterpret_cast<f32x4 *>(c) = v;
+}
+
+namespace {
+
+// Tiles of the 8-wave 256 x 256 kernel and how its last, partly filled round
+// is spread: with T tiles on C compute units, the T mod C tiles of that round
+// (all T when T < C) are each split into S slices of K when they fill at most
+// half of it, S = min(C / leftover, 8, K-steps / 8) (at least 2).
+struct KSplitPlan {
+  int tiles, head, ksplit;
+};
+
+KSplitPlan ksplit_plan(int M, int N, int K) {
+  KSplitPlan p{0, 0, 1};
+  if (M <= 4 || N % 256 != 0) return p;
+  const int cus = cu_count();
+  p.tiles = ((M + eng::kBM - 1) / eng::kBM) * (N / 256);
+  p.head = p.tiles;
+  const int tail = p.tiles % cus;
+  if (tail == 0 || 2 * tail > cus) return p;
+  const int s = min(min(cus / tail, 8), (K / eng::kBK) / 8);
+  if (s < 2) return p;
+  p.head = p.tiles - tail;
+  p.ksplit = s;
+  return p;
+}
+
+size_t plan_bytes(const KSplitPlan &p) {
+  return p.ksplit > 1 ? (size_t)(p.tiles - p.head) * (size_t)(p.ksplit - 1) * eng::kBM * 256 * sizeof(float) : 0;
+}
+
+}  // namespace
+
+size_t gemm_k_workspace_bytes(int M, int N, int K) { return plan_bytes(ksplit_plan(M, N, K)); }
+
+// Tiled launches. With N a multiple of 256 the 8-wave 256 x 256 kernel runs.
+// When its tiles leave a last round at most half full (640 tiles on 256 CUs
+// run as 3 rounds, 2.5 of work) and the caller gave the workspace, each
+// leftover tile is split along K over S workgroups of the same launch, which
+// run after the full rounds (one round of 1/S the length), and a fixup
+// kernel adds the slices. Without a workspace the leftover tiles are covered
+// by twice as many 256 x 128 workgroups of the 4-wave kernel in a second
+// launch (measured on MI355X: barely faster than a third full round). Each
+// output element's summation order is fixed by the shape, so results are
+// reproducible bit for bit.
 int launch_gemm_k(const KArgs &a0, hipStream_t s) {
   KArgs a = a0;
   a.tile_base = 0;
   a.split_tail = 0;
+  a.head = 0;
+  a.ksplit = 1;
   const int mt = (a.M + eng::kBM - 1) / eng::kBM;
   if (a.M <= 4) {
     const dim3 grid(a.N / 4), block(256);
@@ -343,14 +429,23 @@ int launch_gemm_k(const KArgs &a0, hipStream_t s) {
       default: hipLaunchKernelGGL(gemv_k_kernel<4>, grid, block, 0, s, a); break;
     }
   } else if (a.N % 256 == 0) {
-    const int tiles = mt * (a.N / 256), cus = cu_count();
-    const int tail = tiles % cus;
-    const int head = tiles > cus && tail > 0 && 2 * tail <= cus ? tiles - tail : tiles;
-    hipLaunchKernelGGL((gemm_k_kernel<256, 8>), dim3(head), dim3(512), 0, s, a);
-    if (head < tiles) {
-      a.tile_base = head;
-      a.split_tail = 1;
-      hipLaunchKernelGGL((gemm_k_kernel<128, 4>), dim3(2 * (tiles - head)), dim3(256), 0, s, a);
+    const KSplitPlan p = ksplit_plan(a.M, a.N, a.K);
+    if (p.ksplit > 1 && a.ws != nullptr && a.ws_bytes >= plan_bytes(p)) {
+      const int tail = p.tiles - p.head;
+      a.head = p.head;
+      a.ksplit = p.ksplit;
+      hipLaunchKernelGGL((gemm_k_kernel<256, 8>), dim3(p.head + tail * p.ksplit), dim3(512), 0, s, a);
+      hipLaunchKernelGGL(gemm_k_fixup_kernel, dim3(tail * (eng::kBM * 64 / 256)), dim3(256), 0, s, a);
+    } else {
+      const int tiles = mt * (a.N / 256), cus = cu_count();
+      const int tail = tiles % cus;
+      const int head = tiles > cus && tail > 0 && 2 * tail <= cus ? tiles - tail : tiles;
+      hipLaunchKernelGGL((gemm_k_kernel<256, 8>), dim3(head), dim3(512), 0, s, a);
+      if (head < tiles) {
+        a.tile_base = head;
+        a.split_tail = 1;
+        hipLaunchKernelGGL((gemm_k_kernel<128, 4>), dim3(2 * (tiles - head)), dim3(256), 0, s, a);
+      }
     }
   } else {
     hipLaunchKernelGGL((gemm_k_kernel<128, 4>), dim3(mt * (a.N / 128)), dim3(256), 0, s, a);

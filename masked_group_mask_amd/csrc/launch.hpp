@@ -56,13 +56,23 @@ struct KArgs {
   int beta;
   int M, N, K, G;
   const uint8_t *mask;
+  // Caller's workspace for the K-split tiles (may be null: then no K split).
+  float *ws;
+  size_t ws_bytes;
   // Set by the launcher: the tiled kernels cover logical 256 x 256 tiles
   // tile_base, tile_base + 1, ... of the raster; with split_tail each one is
-  // covered by two 256 x 128 workgroups.
+  // covered by two 256 x 128 workgroups. With ksplit > 1 the tiles from
+  // `head` on are each covered by ksplit workgroups that own consecutive
+  // slices of the K range.
   int tile_base;
   int split_tail;
+  int head;
+  int ksplit;
 };
 int launch_gemm_k(const KArgs &a, hipStream_t stream);
+// Bytes of workspace the K-split plan of an M x N x K product needs on the
+// current device (0 when the plan splits nothing).
+size_t gemm_k_workspace_bytes(int M, int N, int K);
 
 struct AttnArgs {
   const uint16_t *Q, *K, *V;

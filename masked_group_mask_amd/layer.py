@@ -55,6 +55,9 @@ class PrefillLayer:
         self.h = torch.empty((M, s.Dff), dtype=torch.bfloat16, device=dev)
         self.y_attn = torch.empty((M, s.D), dtype=torch.float32, device=dev)
         self.y_ffn = torch.empty((M, s.D), dtype=torch.float32, device=dev)
+        # One GEMM-K workspace for o_proj and down_proj (they run in turn).
+        wsb = max(mg.gemm_k_workspace_bytes(M, s.D, s.Hq * s.d), mg.gemm_k_workspace_bytes(M, s.D, s.Dff))
+        self.ws_k = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
         if B != 1:
             raise ValueError("the prefill layer driver flattens tokens with B = 1")
 
@@ -75,12 +78,13 @@ class PrefillLayer:
                     counts=self.cnt_a, out=self.o)
         elif op == "o_proj":
             mg.gemm_k(self.o.view(s.M, s.Hq * s.d), self.wo, s.G_attn, ma.view(s.M, s.Hk),
-                      out=self.y_attn)
+                      out=self.y_attn, workspace=self.ws_k)
         elif op == "gate_up_swiglu":
             mg.gemm_mn_swiglu(self.x, self.wg, self.wu, s.G_ffn, perm=self.perm_f[0],
                               counts=self.cnt_f[0], out=self.h)
         elif op == "down_proj":
-            mg.gemm_k(self.h, self.wd, s.G_ffn, mf.view(s.M, s.NG_ffn), out=self.y_ffn)
+            mg.gemm_k(self.h, self.wd, s.G_ffn, mf.view(s.M, s.NG_ffn), out=self.y_ffn,
+                      workspace=self.ws_k)
         else:
             raise ValueError(f"unknown op {op!r}")
 

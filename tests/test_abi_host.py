@@ -98,6 +98,35 @@ def gk(lib, **kw):
                            a["M"], a["N"], a["K"], a["G"], a["mask"], None)
 
 
+def gkw(lib, ws, wsb, M, N, K, G=128):
+    """wide_gemm_k_ws on fake pointers spaced far enough apart for these sizes."""
+    base = 1 << 40
+    A, B, C, mask = (ctypes.c_void_p(base + i * (1 << 34)) for i in range(4))
+    return lib.wide_gemm_k_ws(A, K, B, K, C, N, 0, M, N, K, G, mask, ws, wsb, None)
+
+
+def test_gemm_k_workspace_plan(lib):
+    """Workspace sizes of the K-split plan (the answers hold for any device
+    with at least 8 compute units and none above 512 in the last case)."""
+    f = lib.wide_gemm_k_workspace_bytes
+    tile = 256 * 256 * 4
+    assert f(256, 256, 4096) == 7 * tile    # one tile: 8 slices of 8 K-steps
+    assert f(256, 256, 512) == 0            # 8 K-steps: too short to split
+    assert f(4, 256, 4096) == 0             # matrix-vector path
+    assert f(256, 384, 4096) == 0           # N not a multiple of 256: no split
+    assert f(8192, 4096, 4096) == 0         # 512 tiles: whole rounds (256 CUs) or a last round over half full
+    assert f(0, 256, 4096) == 0 and f(256, -1, 4096) == 0
+
+
+def test_gemm_k_workspace_validation(lib):
+    need = lib.wide_gemm_k_workspace_bytes(256, 256, 4096)
+    ws = ctypes.c_void_p((1 << 40) + 8 * (1 << 34))
+    assert gkw(lib, ws, need - 16, 256, 256, 4096) == INVALID                 # too small
+    assert gkw(lib, ctypes.c_void_p(ws.value + 4), need, 256, 256, 4096) == INVALID  # misaligned
+    alias = ctypes.c_void_p((1 << 40) + 2 * (1 << 34))                        # C's address
+    assert gkw(lib, alias, need, 256, 256, 4096) == INVALID
+
+
 def test_gemm_k_validation(lib):
     assert gk(lib, mask=None) == INVALID
     assert gk(lib, K=200, lda=256, ldb=256) == INVALID     # K % G

@@ -289,6 +289,43 @@ def test_gemm_k_leftover_tiles_beta():
     check_gemm(f32_of(out), ref.gemm_k(A, B, mask, G) + C0, "gemm_k leftover tiles beta=1")
 
 
+KSPLIT_CASES = [  # M, N, K, G; 256 x 256 tiles and the K slices the plan gives them on 256 CUs
+    (256, 256, 4096, 128),    # 1 tile in 8 slices of 8 K-steps
+    (512, 768, 2048, 128),    # 6 tiles in 4 slices
+    (1000, 512, 1024, 64),    # 8 tiles, ragged last row tile, 2 slices
+    (4352, 4096, 1024, 128),  # 272 tiles: 256 whole, the 16 left over in 2 slices
+]
+
+
+@pytest.mark.parametrize("beta", [0, 1])
+@pytest.mark.parametrize("M,N,K,G", KSPLIT_CASES)
+def test_gemm_k_ksplit(M, N, K, G, beta):
+    """With a workspace the partly filled last round of tiles is split along
+    K and a second kernel adds the slices; the workspace starts as NaN garbage,
+    which must never reach the result."""
+    A = wl.random_bf16(M + 80, (M, K))
+    B = wl.random_bf16(N + 81, (N, K), 0.05)
+    mask = wl.random_mask(M + K + 82, (M, K // G), 0.5)
+    mask[:3] = 0  # rows with no active group
+    C0 = ref.from_bf16(wl.random_bf16(83, (M, N)).view(np.uint16)).astype(np.float32)
+    need = W().gemm_k_workspace_bytes(M, N, K)
+    assert need > 0, "this shape must take the K-split plan"
+    say("gemm_k ksplit", M, N, K, G, "beta", beta, "workspace", need)
+    Ad, Bd, md = to_dev(A, torch), to_dev(B, torch), to_dev(mask, torch)
+    results = []
+    for _ in range(2):
+        ws = torch.full((need // 4,), float("nan"), dtype=torch.float32, device="cuda")
+        out = to_dev(C0, torch) if beta else torch.full((M, N), float("nan"), device="cuda")
+        W().gemm_k(Ad, Bd, G, md, out=out, beta=beta, workspace=ws)
+        results.append(out)
+    torch.cuda.synchronize()
+    want = ref.gemm_k(A, B, mask, G) + (C0 if beta else 0)
+    check_gemm(f32_of(results[0]), want, f"gemm_k ksplit {M}x{N}x{K} G{G} beta={beta}")
+    assert torch.equal(results[0], results[1]), "K-split GEMM-K is not bitwise reproducible"
+    if not beta:
+        assert (results[0].cpu().numpy()[:3] == 0).all()
+
+
 @pytest.mark.parametrize("p", [0.0, 1.0])
 def test_gemm_k_all_or_nothing(p):
     M, N, K, G = 150, 128, 512, 128
