@@ -125,6 +125,46 @@ int wide_gemm_mn_swiglu(const wide_bf16 *A, int64_t lda, const wide_bf16 *Wg,
                         const uint8_t *mask, wide_stream_t stream);
 
 /*
+ * wide_gemm_mn_ws, wide_gemm_mn_swiglu_ws -- wide_gemm_mn and
+ * wide_gemm_mn_swiglu (Figure 1; Appendix B, Algorithm 2 and its split-K
+ * variant) with a caller-owned workspace. The workgroups then derive the list
+ * of active tiles from counts on the device (the host still never reads
+ * them), take the tiles in that order, and when the active tiles leave a
+ * last round on the compute units at most half full, every tile of that
+ * round is split into slices of K computed by separate workgroups; a second
+ * kernel sums the slices in slice order, applies the epilogue (SwiGLU for
+ * the _swiglu form) and scatters the active rows. The page's split-K variant
+ * reduces the slices with atomics; here the order is fixed, so results are
+ * bitwise reproducible for a given shape, mask and device.
+ *   workspace: device memory of at least wide_gemm_mn_workspace_bytes(M, N,
+ *     K, G, swiglu) bytes, 16-byte aligned, overlapping no other argument.
+ *     Contents on entry are ignored and overwritten; calls sharing a
+ *     workspace must not run at the same time. NULL (or a size of 0 when the
+ *     function returns 0) is the plain call. Ignored when perm == NULL.
+ * Results: as the plain call; a split tile's fp32 sums are formed as slice 0
+ * + slice 1 + ... and may round differently from a single pass over K.
+ * Requirements and errors as the plain call; WIDE_ERR_INVALID_ARG when a
+ * workspace is given that is smaller than needed, misaligned or overlapping.
+ */
+int wide_gemm_mn_ws(const wide_bf16 *A, int64_t lda, const wide_bf16 *B, int64_t ldb,
+                    void *C, int64_t ldc, int c_dtype, int64_t M, int64_t N, int64_t K,
+                    int64_t G, const int32_t *perm, const int32_t *counts,
+                    const uint8_t *mask, void *workspace, size_t workspace_bytes,
+                    wide_stream_t stream);
+int wide_gemm_mn_swiglu_ws(const wide_bf16 *A, int64_t lda, const wide_bf16 *Wg,
+                           const wide_bf16 *Wu, int64_t ldb, void *H, int64_t ldh,
+                           int h_dtype, int64_t M, int64_t N, int64_t K, int64_t G,
+                           const int32_t *perm, const int32_t *counts,
+                           const uint8_t *mask, void *workspace, size_t workspace_bytes,
+                           wide_stream_t stream);
+
+/* Bytes of device workspace wide_gemm_mn_ws (swiglu = 0) or
+ * wide_gemm_mn_swiglu_ws (swiglu = 1) needs on the current device: a small
+ * header plus one fp32 tile of 256 rows per compute unit (0 when K is too
+ * short for any split, or for sizes out of range). */
+size_t wide_gemm_mn_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t G, int swiglu);
+
+/*
  * wide_gemm_k -- K-axis routed GEMM, GEMM-K (Appendix B, Eq. 21 and
  * Algorithm 3):
  *

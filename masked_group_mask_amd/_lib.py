@@ -31,6 +31,11 @@ _SIGS = {
                      _ptr, _ptr, _ptr, _ptr],
     "wide_gemm_mn_swiglu": [_ptr, _i64, _ptr, _ptr, _i64, _ptr, _i64, _int, _i64, _i64, _i64,
                             _i64, _ptr, _ptr, _ptr, _ptr],
+    "wide_gemm_mn_ws": [_ptr, _i64, _ptr, _i64, _ptr, _i64, _int, _i64, _i64, _i64, _i64,
+                        _ptr, _ptr, _ptr, _ptr, _size, _ptr],
+    "wide_gemm_mn_swiglu_ws": [_ptr, _i64, _ptr, _ptr, _i64, _ptr, _i64, _int, _i64, _i64, _i64,
+                               _i64, _ptr, _ptr, _ptr, _ptr, _size, _ptr],
+    "wide_gemm_mn_workspace_bytes": [_i64, _i64, _i64, _i64, _int],
     "wide_gemm_k": [_ptr, _i64, _ptr, _i64, _ptr, _i64, _int, _i64, _i64, _i64, _i64, _ptr, _ptr],
     "wide_gemm_k_ws": [_ptr, _i64, _ptr, _i64, _ptr, _i64, _int, _i64, _i64, _i64, _i64, _ptr, _ptr, _size,
                        _ptr],
@@ -46,6 +51,7 @@ _SIGS = {
     "wide_abi_version": [],
 }
 _RESTYPES = {"wide_attn_workspace_bytes": _size, "wide_gemm_k_workspace_bytes": _size,
+             "wide_gemm_mn_workspace_bytes": _size,
              "wide_status_string": ctypes.c_char_p}
 
 EXPORTED = tuple(_SIGS)
@@ -186,11 +192,26 @@ def _mn_common(A, G, perm, counts, mask):
     return lda
 
 
+def gemm_mn_workspace_bytes(M: int, N: int, K: int, G: int, swiglu: bool = False) -> int:
+    return int(load().wide_gemm_mn_workspace_bytes(M, N, K, G, int(bool(swiglu))))
+
+
+def _ws(workspace: Optional[torch.Tensor], A: torch.Tensor):
+    if workspace is None:
+        return None, 0
+    if workspace.device != A.device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on A's device")
+    return _p(workspace), workspace.numel() * workspace.element_size()
+
+
 def gemm_mn(A: torch.Tensor, B: torch.Tensor, G: int, perm: Optional[torch.Tensor] = None,
             counts: Optional[torch.Tensor] = None, mask: Optional[torch.Tensor] = None,
-            out: Optional[torch.Tensor] = None, out_dtype=torch.bfloat16) -> torch.Tensor:
+            out: Optional[torch.Tensor] = None, out_dtype=torch.bfloat16,
+            workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """C = A B^T on the active (token, group) entries; others keep `out`'s values
-    (zeros if `out` is allocated here)."""
+    (zeros if `out` is allocated here). workspace: optional device buffer of
+    gemm_mn_workspace_bytes(M, N, K, G) bytes; with it the active tiles are
+    scheduled on the device and a partly filled last round is split along K."""
     lda = _mn_common(A, G, perm, counts, mask)
     _need(B, "B", torch.bfloat16, 2)
     ldb = _rowmajor(B, "B")
@@ -203,16 +224,18 @@ def gemm_mn(A: torch.Tensor, B: torch.Tensor, G: int, perm: Optional[torch.Tenso
     _need(out, "out", out.dtype, 2)
     if tuple(out.shape) != (M, N):
         raise ValueError("out shape mismatch")
-    _call("wide_gemm_mn", _p(A), lda, _p(B), ldb, _p(out), _rowmajor(out, "out"), _dt(out.dtype),
-          M, N, K, G, _p(perm), _p(counts), _p(mask), _stream())
+    ws, wsb = _ws(workspace, A)
+    _call("wide_gemm_mn_ws", _p(A), lda, _p(B), ldb, _p(out), _rowmajor(out, "out"), _dt(out.dtype),
+          M, N, K, G, _p(perm), _p(counts), _p(mask), ws, wsb, _stream())
     return out
 
 
 def gemm_mn_swiglu(A: torch.Tensor, Wg: torch.Tensor, Wu: torch.Tensor, G: int,
                    perm: Optional[torch.Tensor] = None, counts: Optional[torch.Tensor] = None,
                    mask: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
-                   out_dtype=torch.bfloat16) -> torch.Tensor:
-    """H = SiLU(A Wg^T) * (A Wu^T) on the active entries."""
+                   out_dtype=torch.bfloat16, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """H = SiLU(A Wg^T) * (A Wu^T) on the active entries. workspace: as gemm_mn
+    (gemm_mn_workspace_bytes(M, N, K, G, swiglu=True) bytes)."""
     lda = _mn_common(A, G, perm, counts, mask)
     _need(Wg, "Wg", torch.bfloat16, 2)
     _need(Wu, "Wu", torch.bfloat16, 2)
@@ -227,9 +250,10 @@ def gemm_mn_swiglu(A: torch.Tensor, Wg: torch.Tensor, Wu: torch.Tensor, G: int,
         out = torch.zeros((M, N), dtype=out_dtype, device=A.device)
     if tuple(out.shape) != (M, N):
         raise ValueError("out shape mismatch")
-    _call("wide_gemm_mn_swiglu", _p(A), lda, _p(Wg), _p(Wu), ldb, _p(out),
+    ws, wsb = _ws(workspace, A)
+    _call("wide_gemm_mn_swiglu_ws", _p(A), lda, _p(Wg), _p(Wu), ldb, _p(out),
           _rowmajor(out, "out"), _dt(out.dtype), M, N, K, G, _p(perm), _p(counts), _p(mask),
-          _stream())
+          ws, wsb, _stream())
     return out
 
 
@@ -258,11 +282,7 @@ def gemm_k(A: torch.Tensor, B: torch.Tensor, G: int, mask: torch.Tensor,
     _need(out, "out", torch.float32, 2)
     if tuple(out.shape) != (M, N):
         raise ValueError("out shape mismatch")
-    ws, wsb = None, 0
-    if workspace is not None:
-        if workspace.device != A.device or not workspace.is_contiguous():
-            raise ValueError("workspace must be a contiguous tensor on A's device")
-        ws, wsb = _p(workspace), workspace.numel() * workspace.element_size()
+    ws, wsb = _ws(workspace, A)
     _call("wide_gemm_k_ws", _p(A), _rowmajor(A, "A"), _p(B), _rowmajor(B, "B"), _p(out),
           _rowmajor(out, "out"), int(beta), M, N, K, G, _p(mask), ws, wsb, _stream())
     return out

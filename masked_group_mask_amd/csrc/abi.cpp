@@ -68,6 +68,49 @@ int check_mn(const wide_bf16 *A, int64_t lda, const wide_bf16 *B0, const wide_bf
   return WIDE_OK;
 }
 
+// Validates a GEMM-MN workspace; on success `ws` is the pointer the launcher
+// takes (null when no workspace applies: no perm, or a plan that splits
+// nothing).
+int check_mn_ws(const wide_bf16 *A, int64_t lda, const wide_bf16 *B0, const wide_bf16 *B1,
+                int64_t ldb, const void *C, int64_t ldc, int c_dtype, int64_t M, int64_t N,
+                int64_t K, int64_t G, const int32_t *perm, const int32_t *counts, void *&ws,
+                size_t ws_bytes) {
+  if (ws == nullptr) return WIDE_OK;
+  if (perm == nullptr) {
+    ws = nullptr;
+    return WIDE_OK;
+  }
+  const size_t need = wide::gemm_mn_workspace_bytes((int)M, (int)N, (int)K, (int)G, B1 != nullptr);
+  if (ws_bytes < need || !aligned16(ws)) return WIDE_ERR_INVALID_ARG;
+  if (need == 0) {
+    ws = nullptr;
+    return WIDE_OK;
+  }
+  const size_t cb = span_bytes(M, N, ldc, c_dtype == WIDE_DTYPE_F32 ? 4 : 2);
+  const size_t ng = (size_t)(N / G);
+  if (overlap(ws, need, A, span_bytes(M, K, lda, 2)) || overlap(ws, need, B0, span_bytes(N, K, ldb, 2)) ||
+      (B1 && overlap(ws, need, B1, span_bytes(N, K, ldb, 2))) || overlap(ws, need, C, cb) ||
+      overlap(ws, need, perm, ng * (size_t)M * 4) || overlap(ws, need, counts, ng * 4))
+    return WIDE_ERR_INVALID_ARG;
+  return WIDE_OK;
+}
+
+int gemm_mn_impl(const wide_bf16 *A, int64_t lda, const wide_bf16 *B0, const wide_bf16 *B1, int64_t ldb,
+                 void *C, int64_t ldc, int c_dtype, int64_t M, int64_t N, int64_t K, int64_t G,
+                 const int32_t *perm, const int32_t *counts, const uint8_t *mask, void *ws,
+                 size_t ws_bytes, wide_stream_t stream) {
+  int st = check_mn(A, lda, B0, B1, ldb, C, ldc, c_dtype, M, N, K, G, perm, counts, mask);
+  if (st != WIDE_OK) return st;
+  st = check_mn_ws(A, lda, B0, B1, ldb, C, ldc, c_dtype, M, N, K, G, perm, counts, ws, ws_bytes);
+  if (st != WIDE_OK) return st;
+  if (!device_ok()) return WIDE_ERR_NO_DEVICE;
+  wide::MnArgs a{A, lda, B0, B1, ldb, C, ldc, c_dtype == WIDE_DTYPE_F32, (int)M, (int)N,
+                 (int)K, (int)G, perm, counts, mask};
+  a.ws = ws;
+  a.ws_bytes = ws_bytes;
+  return wide::launch_gemm_mn(a, reinterpret_cast<hipStream_t>(stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -104,12 +147,8 @@ int wide_gemm_mn(const wide_bf16 *A, int64_t lda, const wide_bf16 *B, int64_t ld
                  int64_t ldc, int c_dtype, int64_t M, int64_t N, int64_t K, int64_t G,
                  const int32_t *perm, const int32_t *counts, const uint8_t *mask,
                  wide_stream_t stream) {
-  const int st = check_mn(A, lda, B, nullptr, ldb, C, ldc, c_dtype, M, N, K, G, perm, counts, mask);
-  if (st != WIDE_OK) return st;
-  if (!device_ok()) return WIDE_ERR_NO_DEVICE;
-  wide::MnArgs a{A, lda, B, nullptr, ldb, C, ldc, c_dtype == WIDE_DTYPE_F32, (int)M, (int)N,
-                 (int)K, (int)G, perm, counts, mask};
-  return wide::launch_gemm_mn(a, reinterpret_cast<hipStream_t>(stream));
+  return gemm_mn_impl(A, lda, B, nullptr, ldb, C, ldc, c_dtype, M, N, K, G, perm, counts, mask, nullptr, 0,
+                      stream);
 }
 
 int wide_gemm_mn_swiglu(const wide_bf16 *A, int64_t lda, const wide_bf16 *Wg, const wide_bf16 *Wu,
@@ -117,12 +156,30 @@ int wide_gemm_mn_swiglu(const wide_bf16 *A, int64_t lda, const wide_bf16 *Wg, co
                         int64_t K, int64_t G, const int32_t *perm, const int32_t *counts,
                         const uint8_t *mask, wide_stream_t stream) {
   if (!Wu) return WIDE_ERR_INVALID_ARG;
-  const int st = check_mn(A, lda, Wg, Wu, ldb, H, ldh, h_dtype, M, N, K, G, perm, counts, mask);
-  if (st != WIDE_OK) return st;
-  if (!device_ok()) return WIDE_ERR_NO_DEVICE;
-  wide::MnArgs a{A, lda, Wg, Wu, ldb, H, ldh, h_dtype == WIDE_DTYPE_F32, (int)M, (int)N,
-                 (int)K, (int)G, perm, counts, mask};
-  return wide::launch_gemm_mn(a, reinterpret_cast<hipStream_t>(stream));
+  return gemm_mn_impl(A, lda, Wg, Wu, ldb, H, ldh, h_dtype, M, N, K, G, perm, counts, mask, nullptr, 0, stream);
+}
+
+size_t wide_gemm_mn_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t G, int swiglu) {
+  if (M < 1 || N < 1 || K < 1 || G < 1 || M > kI32Max || N > kI32Max || K > kI32Max || N % G != 0) return 0;
+  return wide::gemm_mn_workspace_bytes((int)M, (int)N, (int)K, (int)G, swiglu != 0);
+}
+
+int wide_gemm_mn_ws(const wide_bf16 *A, int64_t lda, const wide_bf16 *B, int64_t ldb, void *C,
+                    int64_t ldc, int c_dtype, int64_t M, int64_t N, int64_t K, int64_t G,
+                    const int32_t *perm, const int32_t *counts, const uint8_t *mask, void *workspace,
+                    size_t workspace_bytes, wide_stream_t stream) {
+  return gemm_mn_impl(A, lda, B, nullptr, ldb, C, ldc, c_dtype, M, N, K, G, perm, counts, mask, workspace,
+                      workspace_bytes, stream);
+}
+
+int wide_gemm_mn_swiglu_ws(const wide_bf16 *A, int64_t lda, const wide_bf16 *Wg, const wide_bf16 *Wu,
+                           int64_t ldb, void *H, int64_t ldh, int h_dtype, int64_t M, int64_t N,
+                           int64_t K, int64_t G, const int32_t *perm, const int32_t *counts,
+                           const uint8_t *mask, void *workspace, size_t workspace_bytes,
+                           wide_stream_t stream) {
+  if (!Wu) return WIDE_ERR_INVALID_ARG;
+  return gemm_mn_impl(A, lda, Wg, Wu, ldb, H, ldh, h_dtype, M, N, K, G, perm, counts, mask, workspace,
+                      workspace_bytes, stream);
 }
 
 int wide_gemm_k(const wide_bf16 *A, int64_t lda, const wide_bf16 *B, int64_t ldb, float *C,

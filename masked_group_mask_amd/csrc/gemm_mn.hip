@@ -61,16 +61,16 @@ struct MnLoader {
   static constexpr int kLoadGap = SPLIT ? 1 : 0;
   rsrc_t ar, br0, br1, none;
   uint32_t aoff[S::AI], boff[S::BI];
-  int nk, K, wave;
+  int nk, kb, K, wave;  // steps kb .. kb + nk - 1 of K
   int kchunk;  // first k (elements) of this lane's 16-byte chunk within a stage
 
   __device__ __forceinline__ void prefetch(int) const {}
 
   __device__ __forceinline__ void operator()(int t, eng::lds_u16 *sa, eng::lds_u16 *sb) const {
     const bool live = t < nk;
-    const uint32_t k0 = (uint32_t)t * eng::kBK * 2u;
+    const uint32_t k0 = (uint32_t)(t + kb) * eng::kBK * 2u;
     // K tail: a chunk at or past K is loaded out of range (zeros)
-    const bool in = t * eng::kBK + kchunk < K;
+    const bool in = (t + kb) * eng::kBK + kchunk < K;
     const rsrc_t ra = live ? ar : none;
 #pragma unroll
     for (int i = 0; i < S::AI; ++i) eng::load_lds(ra, eng::load_dst<S::WAVES>(sa, wave, i), in ? aoff[i] : kOffNone, k0);
@@ -83,7 +83,102 @@ struct MnLoader {
   }
 };
 
-template <int BN, int W, bool SWIGLU, bool OUT_F32>
+// ---- Device-side schedule of the active tiles (workspace path) ----------
+//
+// The active tiles are known only on the device (counts are never read on the
+// host), so every workgroup derives the same schedule from counts: group g
+// has ceil(counts[g] / 256) row tiles times G / BN_OUT column tiles, numbered
+// group by group (row tile major, column tile minor, so the column tiles of
+// one row tile, which gather the same rows, are neighbours). With A active
+// tiles on C compute units (one tile workgroup per CU), the A mod C tiles of
+// the last round (all A when A < C) are split into S = min(C / L, 8,
+// K-steps / 8) slices of K when they fill at most half of it (S >= 2), so
+// that round takes about 1/S of a tile's time. Workgroup p < W (W whole
+// tiles) takes whole tile xcd_remap(p, W) (each XCD a contiguous range);
+// workgroup W + q takes slice q % S of split tile W + q / S. Every slice
+// writes its fp32 partial tile to the workspace, and gemm_mn_fixup_kernel
+// sums the slices in slice order and applies the epilogue.
+//
+// Workspace layout: int4 header {L, S, W, 0}; int4 {g, s0, n0, counts[g]}
+// per split tile; from kMnHdrBytes on, the partial tiles [slot][slice][256][BN].
+constexpr int kMnHdrInts = 4 * (1 + 1024);
+constexpr int kMaxSlices = 8;  // K slices per split tile
+constexpr int kFixRows = 16;   // rows of a split tile per fixup workgroup
+constexpr size_t kMnHdrBytes = kMnHdrInts * sizeof(int);
+
+struct MnPlan {
+  int A, W, L, S;
+};
+
+// Exclusive prefix of v over the workgroup; `total` receives the sum.
+// `tmp` holds one int per wave.
+template <int THREADS>
+__device__ __forceinline__ int block_excl_scan(int v, int &total, int *tmp) {
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  if (lane == kWave - 1) tmp[wave] = x;
+  __syncthreads();
+  int before = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < THREADS / kWave; ++w) {
+    const int t = tmp[w];
+    before += w < wave ? t : 0;
+    tot += t;
+  }
+  total = tot;
+  __syncthreads();
+  return before + x - v;
+}
+
+// Thread t owns groups [t per, (t + 1) per); returns the schedule and this
+// thread's (first tile, tile count).
+template <int THREADS>
+__device__ __forceinline__ MnPlan mn_plan(const MnArgs &a, int ntg, int nk, int *tmp, int &first, int &mine) {
+  const int NG = a.N / a.G;
+  const int per = (NG + THREADS - 1) / THREADS;
+  const int g0 = min((int)threadIdx.x * per, NG), g1 = min(g0 + per, NG);
+  mine = 0;
+  for (int g = g0; g < g1; ++g) mine += (a.counts[g] + eng::kBM - 1) / eng::kBM * ntg;
+  MnPlan p;
+  first = block_excl_scan<THREADS>(mine, p.A, tmp);
+  const int C = a.cus;
+  p.L = p.A % C;
+  p.S = 1;
+  if (p.L > 0 && 2 * p.L <= C) p.S = min(min(C / p.L, kMaxSlices), nk / 8);
+  if (p.S < 2) {
+    p.S = 1;
+    p.L = 0;
+  }
+  p.W = p.A - p.L;
+  return p;
+}
+
+// The (group, index within the group) of logical tile j < A; one thread finds
+// it, the result is read back from LDS.
+__device__ __forceinline__ void mn_find(const MnArgs &a, int ntg, int j, int first, int mine, int *out) {
+  if (j >= first && j < first + mine) {
+    const int NG = a.N / a.G;
+    const int per = (NG + blockDim.x - 1) / blockDim.x;
+    int acc = first;
+    for (int g = min((int)threadIdx.x * per, NG); g < NG; ++g) {
+      const int tg = (a.counts[g] + eng::kBM - 1) / eng::kBM * ntg;
+      if (j < acc + tg) {
+        out[0] = g;
+        out[1] = j - acc;
+        break;
+      }
+      acc += tg;
+    }
+  }
+  __syncthreads();
+}
+
+template <int BN, int W, bool SWIGLU, bool OUT_F32, bool SCHED>
 __global__ __launch_bounds__(64 * W) void gemm_mn_kernel(MnArgs a) {
   using S = eng::Shape<BN, W>;
   constexpr int BN_OUT = SWIGLU ? BN / 2 : BN;
@@ -96,13 +191,44 @@ __global__ __launch_bounds__(64 * W) void gemm_mn_kernel(MnArgs a) {
   __shared__ __attribute__((aligned(1024))) uint16_t sB2[B3];
   __shared__ int sRows[eng::kBM];
 
-  const int MT = (a.M + eng::kBM - 1) / eng::kBM, NT = a.N / BN_OUT;
-  int mt, tn;
-  eng::tile_of(blockIdx.x, MT, NT, mt, tn);
-  const int n0 = tn * BN_OUT, g = n0 / a.G;
+  const int nk_all = (a.K + eng::kBK - 1) / eng::kBK;
+  int n0, g, mt;
+  int part = 0, nparts = 1, slot = 0;  // K slice of this workgroup; slot: split tile index
+  if constexpr (SCHED) {
+    __shared__ int sTmp[W + 2];
+    const int ntg = a.G / BN_OUT;
+    int first, mine;
+    const MnPlan p = mn_plan<S::THREADS>(a, ntg, nk_all, sTmp, first, mine);
+    int *hdr = static_cast<int *>(a.ws);
+    if (blockIdx.x == 0 && threadIdx.x == 0) *reinterpret_cast<int4 *>(hdr) = int4{p.L, p.S, p.W, 0};
+    const int p_id = blockIdx.x;
+    if (p_id >= p.W + p.L * p.S) return;  // no work left for this workgroup
+    int j;
+    if (p_id < p.W) {
+      j = xcd_remap(p_id, p.W);
+    } else {
+      slot = (p_id - p.W) / p.S;
+      part = (p_id - p.W) % p.S;
+      nparts = p.S;
+      j = p.W + slot;
+    }
+    mn_find(a, ntg, j, first, mine, sTmp + W);
+    g = sTmp[W];
+    const int local = sTmp[W + 1];
+    mt = local / ntg;
+    n0 = g * a.G + (local % ntg) * BN_OUT;
+    if (nparts > 1 && part == 0 && threadIdx.x == 0)
+      reinterpret_cast<int4 *>(hdr)[1 + slot] = int4{g, mt * eng::kBM, n0, a.counts[g]};
+  } else {
+    const int MT = (a.M + eng::kBM - 1) / eng::kBM, NT = a.N / BN_OUT;
+    int tn;
+    eng::tile_of(blockIdx.x, MT, NT, mt, tn);
+    n0 = tn * BN_OUT;
+    g = n0 / a.G;
+  }
   const int cnt = a.counts[g];
   const int s0 = mt * eng::kBM;
-  if (s0 >= cnt) return;  // level 0
+  if (s0 >= cnt) return;  // level 0 (never taken by a scheduled tile)
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int wm = wave / S::WNW, wn = wave % S::WNW;
   if (tid < eng::kBM) sRows[tid] = s0 + tid < cnt ? a.perm[(size_t)g * a.M + s0 + tid] : -1;
@@ -126,7 +252,8 @@ __global__ __launch_bounds__(64 * W) void gemm_mn_kernel(MnArgs a) {
     const int rb = SWIGLU ? r % (BN / 2) : r;
     ld.boff[i] = (uint32_t)rb * (uint32_t)a.ldb * 2u + eng::load_chunk_bytes(r, lane);
   }
-  ld.nk = (a.K + eng::kBK - 1) / eng::kBK;
+  ld.kb = part * nk_all / nparts;
+  ld.nk = (part + 1) * nk_all / nparts - ld.kb;
   ld.K = a.K;
   ld.wave = wave;
   ld.kchunk = (int)(eng::load_chunk_bytes(eng::load_row<W>(wave, 0, lane), lane) / 2);
@@ -139,8 +266,23 @@ __global__ __launch_bounds__(64 * W) void gemm_mn_kernel(MnArgs a) {
   eng::mainloop<S, BN, SWIGLU>(ld.nk, ld, (eng::lds_u16 *)sA0, (eng::lds_u16 *)sB0, (eng::lds_u16 *)sA1,
                                (eng::lds_u16 *)sB1, (eng::lds_u16 *)sA2, (eng::lds_u16 *)sB2, acc, wm, wn, lane);
 
-  // Scatter: a lane holds sorted row (lane % 16) of A fragment j and
-  // features 4 (lane / 16) .. +3 of B fragment i.
+  // A lane holds sorted row (lane % 16) of A fragment j and features
+  // 4 (lane / 16) .. +3 of B fragment i.
+  if (nparts > 1) {
+    // A K slice: the fp32 partial tile (stage-row order of B, gate then up
+    // rows for SwiGLU) goes to the workspace for the fixup kernel.
+    float *wt = reinterpret_cast<float *>(static_cast<char *>(a.ws) + kMnHdrBytes) +
+                ((size_t)slot * nparts + part) * (size_t)(eng::kBM * BN);
+#pragma unroll
+    for (int j = 0; j < S::FM; ++j) {
+      float *wrow = wt + (size_t)(wm * S::TM + j * 16 + lane % 16) * BN + 4 * (lane / 16);
+#pragma unroll
+      for (int i = 0; i < S::FN; ++i)
+        *reinterpret_cast<f32x4 *>(wrow + eng::b_frag_row<S, BN, SWIGLU>(wn, i)) = acc[i][j];
+    }
+    return;
+  }
+  // Scatter through perm.
   const bool vec = a.ldc % 4 == 0 && reinterpret_cast<uintptr_t>(a.C) % 16 == 0;
 #pragma unroll
   for (int j = 0; j < S::FM; ++j) {
@@ -159,6 +301,51 @@ __global__ __launch_bounds__(64 * W) void gemm_mn_kernel(MnArgs a) {
       for (int i = 0; i < S::FN; ++i)
         store_out4<OUT_F32>(a.C, rowoff + n0 + wn * S::TN + i * 16 + 4 * (lane / 16), acc[i][j], vec);
     }
+  }
+}
+
+// Second pass of the K-split tiles: for every active row of a split tile,
+// sums the slices' partials in slice order, applies the epilogue (SwiGLU or
+// none) and scatters through perm. kFixRows rows per workgroup (16
+// workgroups per split tile), one thread per 4 consecutive outputs, the
+// loads of all slices issued before the sum.
+template <int BN, bool SWIGLU, bool OUT_F32>
+__global__ __launch_bounds__(256) void gemm_mn_fixup_kernel(MnArgs a) {
+  constexpr int BN_OUT = SWIGLU ? BN / 2 : BN, Q = BN_OUT / 4, PER_TILE = eng::kBM / kFixRows;
+  constexpr size_t TILE = (size_t)eng::kBM * BN;
+  const int *hdr = static_cast<const int *>(a.ws);
+  const int4 h = *reinterpret_cast<const int4 *>(hdr);
+  const int L = h.x, S = h.y;
+  const int slot = blockIdx.x / PER_TILE, rb = blockIdx.x % PER_TILE;
+  if (slot >= L) return;
+  const int4 info = reinterpret_cast<const int4 *>(hdr)[1 + slot];
+  const int g = info.x, s0 = info.y, n0 = info.z, cnt = info.w;
+  const float *base = reinterpret_cast<const float *>(static_cast<const char *>(a.ws) + kMnHdrBytes) +
+                      (size_t)slot * S * TILE;
+  const bool vec = a.ldc % 4 == 0 && reinterpret_cast<uintptr_t>(a.C) % 16 == 0;
+  for (int e = threadIdx.x; e < kFixRows * Q; e += 256) {
+    const int r = rb * kFixRows + e / Q, q = e % Q;
+    if (s0 + r >= cnt) continue;
+    const int phys = a.perm[(size_t)g * a.M + s0 + r];
+    const float *src = base + (size_t)r * BN + 4 * q;
+    f32x4 pv[kMaxSlices], pu[kMaxSlices];
+#pragma unroll
+    for (int p = 0; p < kMaxSlices; ++p) {
+      if (p < S) {
+        pv[p] = *reinterpret_cast<const f32x4 *>(src + p * TILE);
+        if (SWIGLU) pu[p] = *reinterpret_cast<const f32x4 *>(src + p * TILE + BN / 2);
+      }
+    }
+    f32x4 v = {0.f, 0.f, 0.f, 0.f}, u = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int p = 0; p < kMaxSlices; ++p) {
+      if (p < S) {
+        v += pv[p];
+        if (SWIGLU) u += pu[p];
+      }
+    }
+    if (SWIGLU) v = f32x4{silu(v[0]) * u[0], silu(v[1]) * u[1], silu(v[2]) * u[2], silu(v[3]) * u[3]};
+    store_out4<OUT_F32>(a.C, (size_t)phys * a.ldc + n0 + 4 * q, v, vec);
   }
 }
 
@@ -244,7 +431,15 @@ template <int BN, int W, bool SWIGLU, bool F32>
 static void launch_tiled(const MnArgs &a, hipStream_t s) {
   constexpr int BN_OUT = SWIGLU ? BN / 2 : BN;
   const int tiles = (a.N / BN_OUT) * ((a.M + eng::kBM - 1) / eng::kBM);
-  hipLaunchKernelGGL((gemm_mn_kernel<BN, W, SWIGLU, F32>), dim3(tiles), dim3(64 * W), 0, s, a);
+  if (a.ws != nullptr) {
+    // every schedule has at most tiles - L + C <= tiles + C work items, and
+    // at most C / 2 split tiles
+    hipLaunchKernelGGL((gemm_mn_kernel<BN, W, SWIGLU, F32, true>), dim3(tiles + a.cus), dim3(64 * W), 0, s, a);
+    hipLaunchKernelGGL((gemm_mn_fixup_kernel<BN, SWIGLU, F32>), dim3((eng::kBM / kFixRows) * (a.cus / 2)),
+                       dim3(256), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((gemm_mn_kernel<BN, W, SWIGLU, F32, false>), dim3(tiles), dim3(64 * W), 0, s, a);
+  }
 }
 
 template <bool SWIGLU, bool F32>
@@ -258,8 +453,29 @@ static void launch_gemv(const MnArgs &a, hipStream_t s) {
   }
 }
 
-int launch_gemm_mn(const MnArgs &a, hipStream_t s) {
+// Output tile width BN of the tiled kernel chosen for a group size.
+static int tile_bn(int G, bool swiglu) {
+  if (swiglu) return G % 128 == 0 ? 256 : 128;
+  if (G % 256 == 0) return 256;
+  if (G % 320 == 0) return 320;
+  return G % 128 == 0 ? 128 : 64;
+}
+
+size_t gemm_mn_workspace_bytes(int M, int N, int K, int G, bool swiglu) {
+  (void)M;
+  (void)N;
+  const int nk = (K + eng::kBK - 1) / eng::kBK;
+  const int cus = cu_count();
+  if (nk / 8 < 2 || cus > 1024) return 0;  // no slice plan: the unscheduled path runs
+  return kMnHdrBytes + (size_t)cus * eng::kBM * tile_bn(G, swiglu) * sizeof(float);
+}
+
+int launch_gemm_mn(const MnArgs &a0, hipStream_t s) {
+  MnArgs a = a0;
   const bool swiglu = a.B1 != nullptr;
+  a.cus = cu_count();
+  const size_t need = gemm_mn_workspace_bytes(a.M, a.N, a.K, a.G, swiglu);
+  if (need == 0 || a.ws_bytes < need) a.ws = nullptr;
   if (a.perm == nullptr) {
     if (swiglu) {
       if (a.c_f32) launch_gemv<true, true>(a, s); else launch_gemv<true, false>(a, s);

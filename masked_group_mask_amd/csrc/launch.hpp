@@ -43,8 +43,16 @@ struct MnArgs {
   const int32_t *perm;
   const int32_t *counts;
   const uint8_t *mask;
+  // Caller's workspace (may be null). With one, the tiled path schedules the
+  // active tiles on the device and splits a partly filled last round along K.
+  void *ws = nullptr;
+  size_t ws_bytes = 0;
+  int cus = 0;  // set by the launcher: compute units of the device
 };
 int launch_gemm_mn(const MnArgs &a, hipStream_t stream);
+// Bytes of workspace the scheduled GEMM-MN path needs on the current device
+// (0 when it would never split a tile: the path then runs without one).
+size_t gemm_mn_workspace_bytes(int M, int N, int K, int G, bool swiglu);
 
 struct KArgs {
   const uint16_t *A;

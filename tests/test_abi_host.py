@@ -90,6 +90,53 @@ def test_gemm_mn_swiglu_validation(lib):
     assert f(P(0), 64, P(1), P(2), 64, P(2), 256, 0, 32, 256, 64, 128, P(3), P(4), None, None) == INVALID
 
 
+def mnw(lib, ws, wsb, M, N, K, G, swiglu=False, perm=True):
+    """wide_gemm_mn_ws / wide_gemm_mn_swiglu_ws on fake pointers spaced far
+    enough apart for these sizes."""
+    base = 1 << 40
+    A, B, U, C, pm, cn = (ctypes.c_void_p(base + i * (1 << 34)) for i in range(6))
+    if not perm:
+        pm, cn = None, None
+    mask = ctypes.c_void_p(base + 6 * (1 << 34))
+    if swiglu:
+        return lib.wide_gemm_mn_swiglu_ws(A, K, B, U, K, C, N, 1, M, N, K, G, pm, cn, mask, ws, wsb, None)
+    return lib.wide_gemm_mn_ws(A, K, B, K, C, N, 1, M, N, K, G, pm, cn, mask, ws, wsb, None)
+
+
+def test_gemm_mn_workspace_plan(lib):
+    """Workspace of the scheduled GEMM-MN path: a header plus one fp32 tile of
+    256 rows x the tile width per compute unit (256 CUs when no device
+    answers), and none when K is too short for any split (fewer than 16
+    K-steps of 64)."""
+    f = lib.wide_gemm_mn_workspace_bytes
+    hdr = 4 * 4 * 1025
+    cus = f(8192, 5120, 5120, 640, 0) - hdr
+    assert cus % (256 * 320 * 4) == 0 and cus > 0
+    cus //= 256 * 320 * 4
+    assert f(8192, 5120, 5120, 640, 0) == hdr + cus * 256 * 320 * 4    # 320-wide tiles
+    assert f(8192, 17408, 5120, 128, 1) == hdr + cus * 256 * 256 * 4   # fused SwiGLU tile
+    assert f(1000, 512, 1000, 64, 0) == hdr + cus * 256 * 64 * 4       # 64-wide tiles
+    assert f(1000, 512, 960, 64, 0) == 0                                # 15 K-steps
+    assert f(0, 512, 4096, 64, 0) == 0 and f(10, 500, 4096, 64, 0) == 0  # bad sizes
+
+
+def test_gemm_mn_workspace_validation(lib):
+    M, N, K, G = 1000, 1280, 1024, 640
+    need = lib.wide_gemm_mn_workspace_bytes(M, N, K, G, 0)
+    ws = ctypes.c_void_p((1 << 40) + 8 * (1 << 34))
+    assert mnw(lib, ws, need - 16, M, N, K, G) == INVALID                      # too small
+    assert mnw(lib, ctypes.c_void_p(ws.value + 4), need, M, N, K, G) == INVALID  # misaligned
+    alias = ctypes.c_void_p((1 << 40) + 3 * (1 << 34))                         # C's address
+    assert mnw(lib, alias, need, M, N, K, G) == INVALID
+    alias = ctypes.c_void_p((1 << 40) + 4 * (1 << 34))                         # perm's address
+    assert mnw(lib, alias, need, M, N, K, G) == INVALID
+    need_sw = lib.wide_gemm_mn_workspace_bytes(M, N, K, 128, 1)
+    alias = ctypes.c_void_p((1 << 40) + 2 * (1 << 34))                         # up weights
+    assert mnw(lib, alias, need_sw, M, N, K, 128, swiglu=True) == INVALID
+    # without perm (matrix-vector path, M <= 4) the workspace is ignored
+    assert mnw(lib, ctypes.c_void_p(ws.value + 4), 0, 4, N, K, G, perm=False) != INVALID
+
+
 def gk(lib, **kw):
     a = dict(A=P(0), lda=256, B=P(1), ldb=256, C=P(2), ldc=128, beta=0, M=32, N=128, K=256,
              G=128, mask=P(3))

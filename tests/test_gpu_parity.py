@@ -207,6 +207,124 @@ def test_gemm_mn_swiglu(M, N, K, G, dt):
         assert (bits_of(out)[~keep] == 0).all()
 
 
+def _mn_active_tiles(mask2d, G, bn_out):
+    """Active tiles of the scheduled GEMM-MN path, counted on the host from
+    the mask: ceil(count_g / 256) row tiles times G / bn_out column tiles."""
+    counts = mask2d.astype(bool).sum(axis=0)
+    return int(((counts + 255) // 256).sum()) * (G // bn_out)
+
+
+def _run_mn_ws(Ad, Bd, Bu, perm, counts, G, out_dtype, ws, M, N):
+    out = torch.zeros((M, N), dtype=out_dtype, device="cuda")
+    if Bu is None:
+        W().gemm_mn(Ad, Bd, G, perm=perm, counts=counts, out=out, workspace=ws)
+    else:
+        W().gemm_mn_swiglu(Ad, Bd, Bu, G, perm=perm, counts=counts, out=out, workspace=ws)
+    return out
+
+
+# M, N, K, G, swiglu, bn_out of the tile the launcher picks, p(active)
+MN_WS_CASES = [
+    (1000, 1280, 1024, 640, False, 320, 0.5),  # 320-wide tiles, 2 column tiles per group
+    (700, 512, 2048, 128, True, 128, 0.5),     # fused SwiGLU tile
+    (300, 512, 1000, 64, False, 64, 0.5),      # 4-wave 64-wide tile, K tail inside the last slice
+    (4352, 4096, 1024, 128, True, 128, 0.5),   # more tiles than CUs, a short last round
+    (500, 640, 4096, 640, False, 320, 0.5),    # 2 tiles in 8 slices
+    (2000, 1024, 1536, 256, False, 256, 0.0),  # nothing active: the fixup finds no split tile
+]
+
+
+@pytest.mark.parametrize("M,N,K,G,swiglu,bn_out,p", MN_WS_CASES)
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_gemm_mn_scheduled_ksplit(M, N, K, G, swiglu, bn_out, p, dt):
+    """With a workspace the tiles are scheduled from counts on the device and
+    the tiles of a partly filled last round are split along K (summed by a
+    fixup kernel). The workspace starts as NaN garbage; entries of inactive
+    (token, group) pairs stay untouched; two runs agree bit for bit."""
+    A = wl.random_bf16(M + 90, (M, K))
+    B = wl.random_bf16(N + 91, (N, K), 0.05)
+    U = wl.random_bf16(N + 92, (N, K), 0.05) if swiglu else None
+    mask = wl.random_mask(M + N + 93, (M, N // G), p)
+    out_dtype = torch.float32 if dt == "f32" else torch.bfloat16
+    need = W().gemm_mn_workspace_bytes(M, N, K, G, swiglu)
+    assert need > 0
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    A_t = _mn_active_tiles(mask, G, bn_out)
+    split = 0 < A_t % cus <= cus // 2
+    if p > 0:
+        assert split, f"{A_t} active tiles on {cus} CUs: this case must split its last round"
+    say("gemm_mn scheduled", M, N, K, G, "swiglu" if swiglu else "", dt, "tiles", A_t, "split", split)
+    perm, counts = W().reorder(to_dev(mask[None], torch))
+    Ad, Bd = to_dev(A, torch), to_dev(B, torch)
+    Bu = to_dev(U, torch) if swiglu else None
+    outs = []
+    for _ in range(2):
+        ws = torch.full((need // 4,), float("nan"), dtype=torch.float32, device="cuda")
+        outs.append(_run_mn_ws(Ad, Bd, Bu, perm[0], counts[0], G, out_dtype, ws, M, N))
+    torch.cuda.synchronize()
+    want = ref.gemm_mn(A, B, mask, G)
+    if swiglu:
+        want = ref.swiglu(want, ref.gemm_mn(A, U, mask, G))
+    keep = ref.expand(mask, G)
+    if dt == "f32":
+        check_gemm(f32_of(outs[0]), want, f"gemm_mn scheduled {M}x{N}x{K} G{G}")
+        assert (outs[0].cpu().numpy().view(np.uint32)[~keep] == 0).all(), "inactive entries were written"
+    else:
+        check_bf16_store(bits_of(outs[0])[keep], want[keep], f"gemm_mn scheduled bf16 {M}x{N}x{K}")
+        assert (bits_of(outs[0])[~keep] == 0).all(), "inactive entries were written"
+    assert torch.equal(outs[0], outs[1]), "scheduled GEMM-MN is not bitwise reproducible"
+
+
+def test_gemm_mn_workspace_reused_across_shapes():
+    """One workspace through consecutive calls of different shapes (the second
+    smaller, then a SwiGLU call): stale headers and partials of the earlier
+    call must not leak into the later ones."""
+    cases = [(1000, 1280, 1024, 640, False), (300, 640, 1024, 640, False), (500, 512, 2048, 128, True)]
+    need = max(W().gemm_mn_workspace_bytes(M, N, K, G, sw) for M, N, K, G, sw in cases)
+    ws = torch.full((need // 4,), float("nan"), dtype=torch.float32, device="cuda")
+    for i, (M, N, K, G, sw) in enumerate(cases):
+        A = wl.random_bf16(200 + i, (M, K))
+        B = wl.random_bf16(210 + i, (N, K), 0.05)
+        U = wl.random_bf16(220 + i, (N, K), 0.05) if sw else None
+        mask = wl.random_mask(230 + i, (M, N // G), 0.5)
+        say("gemm_mn workspace reuse", i, M, N, K, G, sw)
+        perm, counts = W().reorder(to_dev(mask[None], torch))
+        Ad, Bd = to_dev(A, torch), to_dev(B, torch)
+        Bu = to_dev(U, torch) if sw else None
+        got = _run_mn_ws(Ad, Bd, Bu, perm[0], counts[0], G, torch.float32, ws, M, N)
+        torch.cuda.synchronize()
+        want = ref.gemm_mn(A, B, mask, G)
+        if sw:
+            want = ref.swiglu(want, ref.gemm_mn(A, U, mask, G))
+        check_gemm(f32_of(got), want, f"gemm_mn workspace reuse {i}")
+        assert (got.cpu().numpy().view(np.uint32)[~ref.expand(mask, G)] == 0).all()
+
+
+def test_gemm_mn_scheduled_equals_plain_without_split():
+    """When the last round is more than half full nothing is split: the
+    scheduled path computes every tile exactly as the plain call does, so the
+    two results agree bit for bit (only the tile order differs)."""
+    M, N, K, G = 700, 9216, 1024, 128
+    A = wl.random_bf16(240, (M, K))
+    B = wl.random_bf16(241, (N, K), 0.05)
+    mask = wl.random_mask(242, (M, N // G), 0.5)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    A_t = _mn_active_tiles(mask, G, 128)
+    say("gemm_mn scheduled vs plain", M, N, K, G, "tiles", A_t, "cus", cus)
+    if 0 < A_t % cus <= cus // 2:
+        pytest.skip(f"{A_t} tiles on {cus} CUs would split")
+    need = W().gemm_mn_workspace_bytes(M, N, K, G, False)
+    assert need > 0
+    perm, counts = W().reorder(to_dev(mask[None], torch))
+    Ad, Bd = to_dev(A, torch), to_dev(B, torch)
+    ws = torch.full((need // 4,), float("nan"), dtype=torch.float32, device="cuda")
+    got = _run_mn_ws(Ad, Bd, None, perm[0], counts[0], G, torch.float32, ws, M, N)
+    plain = _run_mn_ws(Ad, Bd, None, perm[0], counts[0], G, torch.float32, None, M, N)
+    torch.cuda.synchronize()
+    assert torch.equal(got, plain)
+    check_gemm(f32_of(got), ref.gemm_mn(A, B, mask, G), "gemm_mn scheduled, no split")
+
+
 @pytest.mark.parametrize("M", [1, 2, 3, 4])
 @pytest.mark.parametrize("swiglu", [False, True])
 @pytest.mark.parametrize("K", [512, 9000])  # one partial block; three blocks of 4096 with a ragged last one
