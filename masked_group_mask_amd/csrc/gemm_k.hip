@@ -31,6 +31,7 @@
 namespace wide {
 
 constexpr int kKMaxGroups = 512;
+constexpr int kKRasterM = 32;  // m-tiles per raster group (eng::tile_of)
 
 // Builds the tile's bit table: bit r of word i of group g says whether tile
 // row 32 i + r keeps group g. Thread t reads the mask row of tile row t % 256
@@ -158,7 +159,7 @@ __global__ __launch_bounds__(64 * W) void gemm_k_kernel(KArgs a) {
   int mt, tn, n0;
   int part = 0, nparts = 1, slot = 0;  // K slice of this workgroup; slot: split tile index
   if (a.split_tail) {  // half of a 256 x 256 tile of the raster
-    eng::tile_of(a.tile_base + (int)blockIdx.x / 2, MT, a.N / 256, mt, tn);
+    eng::tile_of<kKRasterM>(a.tile_base + (int)blockIdx.x / 2, MT, a.N / 256, mt, tn);
     n0 = tn * 256 + ((int)blockIdx.x % 2) * BN;
   } else {
     int L = (int)blockIdx.x;
@@ -168,7 +169,7 @@ __global__ __launch_bounds__(64 * W) void gemm_k_kernel(KArgs a) {
       nparts = a.ksplit;
       L = a.head + slot;
     }
-    eng::tile_of(a.tile_base + L, MT, a.N / BN, mt, tn);
+    eng::tile_of<kKRasterM>(a.tile_base + L, MT, a.N / BN, mt, tn);
     n0 = tn * BN;
   }
   const int m0 = mt * eng::kBM;
@@ -360,7 +361,7 @@ __global__ __launch_bounds__(256) void gemm_k_fixup_kernel(KArgs a) {
   const int r = e / Q, q = e % Q;
   const int MT = (a.M + eng::kBM - 1) / eng::kBM;
   int mt, tn;
-  eng::tile_of(a.head + slot, MT, a.N / 256, mt, tn);
+  eng::tile_of<kKRasterM>(a.head + slot, MT, a.N / 256, mt, tn);
   const int m = mt * eng::kBM + r;
   if (m >= a.M) return;
   float *c = a.C + (size_t)m * a.ldc + tn * 256 + 4 * q;

@@ -222,7 +222,7 @@ __global__ __launch_bounds__(64 * W) void gemm_mn_kernel(MnArgs a) {
   } else {
     const int MT = (a.M + eng::kBM - 1) / eng::kBM, NT = a.N / BN_OUT;
     int tn;
-    eng::tile_of(blockIdx.x, MT, NT, mt, tn);
+    eng::tile_of<8>(blockIdx.x, MT, NT, mt, tn);  // 8 m-tiles per raster group
     n0 = tn * BN_OUT;
     g = n0 / a.G;
   }
