@@ -63,3 +63,44 @@ def test_decode_graph_replays_match_eager():
     torch.cuda.synchronize()
     for name, a, b in zip(names, snapshot(layer), want):
         assert np.array_equal(a, b), f"eager after replays: {name} differs"
+
+
+def prefill_outputs(layer):
+    return [layer.perm_a, layer.cnt_a, layer.perm_f, layer.cnt_f, layer.q, layer.o, layer.y_attn,
+            layer.h, layer.y_ffn]
+
+
+def test_prefill_graph_replays_match_eager():
+    """The masked prefill step (reorders, scheduled GEMM-MN with K-split last
+    rounds and their fixups, attention, K-split GEMM-K) captured as a HIP
+    graph: the workspace header the fixups read is rewritten by every replay,
+    and every replay reproduces the eager step bit for bit."""
+    from masked_group_mask_amd.layer import PrefillLayer
+    s = wl.shape("qwen14b_prefill", T=1024, p_attn=0.5, p_ffn=0.5, G_ffn=128)
+    say("prefill graph replay", s.T, s.D, s.Dff)
+    layer = PrefillLayer(s, wl.make_layer(s, seed=6), with_dense=False)
+    names = ["perm_a", "cnt_a", "perm_f", "cnt_f", "q", "o", "y_attn", "h", "y_ffn"]
+
+    def snap():
+        return [t.detach().view(torch.uint8).cpu().numpy().copy() for t in prefill_outputs(layer)]
+
+    for t in prefill_outputs(layer):
+        t.zero_()
+    layer.step("masked")
+    torch.cuda.synchronize()
+    want = snap()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        layer.step("masked")
+    torch.cuda.synchronize()
+    for r in range(3):
+        for t in prefill_outputs(layer):
+            t.zero_()
+        layer.ws.fill_(255)                              # stale workspace between replays
+        junk = torch.randn(512, 512, device="cuda") @ torch.randn(512, 512, device="cuda")
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for name, a, b in zip(names, snap(), want):
+            assert np.array_equal(a, b), f"replay {r}: {name} differs from the eager step"
+        del junk
