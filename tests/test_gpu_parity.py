@@ -648,3 +648,75 @@ def test_attention_decode_leftpad():
                    leftpad=to_dev(np.array(lp, np.int32), torch), out_dtype=torch.float32)
     torch.cuda.synchronize()
     check_attn(f32_of(out), ref.attention(Q, K, V, mask, leftpad=lp), "decode leftpad")
+
+
+# ---------------------------------------------------------------------------
+# Group counts at the tile boundaries
+# ---------------------------------------------------------------------------
+
+BOUNDARY_COUNTS = [0, 1, 255, 256, 257, 512, 600]   # M = 600: none, one row, BM-1, BM, BM+1, 2 BM, all
+
+
+def boundary_mask(seed, M=600):
+    """[M][7] mask whose group g keeps exactly BOUNDARY_COUNTS[g] rows, at
+    random positions (rows 0 and M-1 among them where the count allows)."""
+    rng = np.random.default_rng(seed)
+    mask = np.zeros((M, len(BOUNDARY_COUNTS)), np.uint8)
+    for g, c in enumerate(BOUNDARY_COUNTS):
+        rows = rng.permutation(M)[:c]
+        mask[rows, g] = 1
+    return mask
+
+
+@pytest.mark.parametrize("scheduled", [False, True])
+def test_boundary_counts_gemms(scheduled):
+    """GEMM-MN (plain or scheduled with a workspace), fused SwiGLU and GEMM-K
+    with group counts 0, 1, BM-1, BM, BM+1, 2 BM and M."""
+    M, G, K = 600, 128, 1024
+    NG = len(BOUNDARY_COUNTS)
+    N = NG * G
+    mask = boundary_mask(400)
+    assert (mask.sum(axis=0) == BOUNDARY_COUNTS).all()
+    A = wl.random_bf16(401, (M, K))
+    B = wl.random_bf16(402, (N, K), 0.05)
+    U = wl.random_bf16(403, (N, K), 0.05)
+    say("boundary counts", "scheduled" if scheduled else "plain")
+    perm, counts = W().reorder(to_dev(mask[None], torch))
+    assert np.array_equal(counts.cpu().numpy()[0], BOUNDARY_COUNTS)
+    Ad, Bd, Ud = to_dev(A, torch), to_dev(B, torch), to_dev(U, torch)
+    ws = None
+    if scheduled:
+        ws = torch.full((W().gemm_mn_workspace_bytes(M, N, K, G, True) // 4,), float("nan"),
+                        dtype=torch.float32, device="cuda")
+    q = _run_mn_ws(Ad, Bd, None, perm[0], counts[0], G, torch.float32, ws, M, N)
+    h = _run_mn_ws(Ad, Bd, Ud, perm[0], counts[0], G, torch.float32, ws, M, N)
+    torch.cuda.synchronize()
+    keep = ref.expand(mask, G)
+    want_q = ref.gemm_mn(A, B, mask, G)
+    check_gemm(f32_of(q), want_q, "boundary gemm_mn")
+    assert (q.cpu().numpy().view(np.uint32)[~keep] == 0).all()
+    want_h = ref.swiglu(want_q, ref.gemm_mn(A, U, mask, G))
+    check_gemm(f32_of(h), want_h, "boundary swiglu")
+    assert (h.cpu().numpy().view(np.uint32)[~keep] == 0).all()
+    # GEMM-K over the same groups: A is [M][NG*G]
+    Ak = wl.random_bf16(404, (M, N))
+    Bk = wl.random_bf16(405, (512, N), 0.05)
+    y = W().gemm_k(to_dev(Ak, torch), to_dev(Bk, torch), G, to_dev(mask, torch))
+    torch.cuda.synchronize()
+    check_gemm(f32_of(y), ref.gemm_k(Ak, Bk, mask, G), "boundary gemm_k")
+
+
+def test_boundary_counts_attention():
+    """Attention prefill with the same per-group counts (one routing group per
+    KV head, 7 KV heads, 2 query heads each), causal and not."""
+    B, T, Hk, d = 1, 600, len(BOUNDARY_COUNTS), 128
+    Hq = 2 * Hk
+    mask = boundary_mask(410)[None]
+    Q = wl.random_bf16(411, (B, T, Hq, d), 1.0)
+    K = wl.random_bf16(412, (B, T, Hk, d), 1.0)
+    V = wl.random_bf16(413, (B, T, Hk, d), 1.0)
+    keep = np.repeat(mask != 0, Hq // Hk, axis=2)
+    for causal in (True, False):
+        out = run_attn(Q, K, V, mask, causal)
+        check_attn(f32_of(out), ref.attention(Q, K, V, mask, causal=causal), f"boundary attn causal={causal}")
+        assert (out.cpu().numpy().view(np.uint32)[~keep] == 0).all()
