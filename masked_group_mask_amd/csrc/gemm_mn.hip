@@ -21,6 +21,13 @@
 // the matching BN/2 up rows (BN = 256 when G is a multiple of 128) and writes
 // BN/2 outputs.
 //
+// With a caller workspace the active tiles are scheduled on the device: every
+// workgroup derives the same numbering of the active tiles from counts
+// (group by group, each XCD a contiguous range), and when they leave a last
+// round on the compute units at most half full, the tiles of that round are
+// split along K (the page's split-K variant of Algorithm 2) and a fixup
+// kernel sums the slices in a fixed order before the epilogue.
+//
 // For M <= 4 with no reorder (decode steps of up to four sequences), a
 // matrix-vector kernel reads the mask bytes directly and streams only the
 // active groups' weight rows, with x shared through LDS.
