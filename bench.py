@@ -276,7 +276,7 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="qwen14b_prefill")
     ap.add_argument("--sparsity", type=float, default=0.5)
     ap.add_argument("--g-ffn", type=int, default=128)
