@@ -720,3 +720,49 @@ def test_boundary_counts_attention():
         out = run_attn(Q, K, V, mask, causal)
         check_attn(f32_of(out), ref.attention(Q, K, V, mask, causal=causal), f"boundary attn causal={causal}")
         assert (out.cpu().numpy().view(np.uint32)[~keep] == 0).all()
+
+
+def _random_mn_cases(n=16, seed=2024):
+    """Seeded random shapes for the scheduled GEMM-MN path: group sizes 64 to
+    640 (each tile width the launcher picks), K with and without a tail,
+    M from 5 to 3000, activity from none to all, both epilogues and stores."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < n:
+        G = int(rng.choice([64, 128, 192, 256, 320, 640]))
+        sw = bool(rng.integers(0, 2))
+        NG = int(rng.integers(1, 6))
+        K = int(rng.choice([1024, 1096, 1536, 2000, 4096]))
+        M = int(rng.choice([5, 77, 256, 300, 1000, 3000]))
+        if M * NG * G * K * (2 if sw else 1) > 4e9:    # keep the fp64 oracle quick
+            continue
+        cases.append((M, NG * G, K, G, sw, float(rng.choice([0.0, 0.1, 0.5, 0.9, 1.0])),
+                      str(rng.choice(["f32", "bf16"]))))
+    return cases
+
+
+@pytest.mark.parametrize("M,N,K,G,swiglu,p,dt", _random_mn_cases())
+def test_gemm_mn_scheduled_random_shapes(M, N, K, G, swiglu, p, dt):
+    A = wl.random_bf16(M + 500, (M, K))
+    B = wl.random_bf16(N + 501, (N, K), 0.05)
+    U = wl.random_bf16(N + 502, (N, K), 0.05) if swiglu else None
+    mask = wl.random_mask(M + N + K + 503, (M, N // G), p)
+    need = W().gemm_mn_workspace_bytes(M, N, K, G, swiglu)
+    say("gemm_mn scheduled random", M, N, K, G, swiglu, p, dt, "workspace", need)
+    ws = torch.full((max(need, 16) // 4,), float("nan"), dtype=torch.float32, device="cuda")
+    perm, counts = W().reorder(to_dev(mask[None], torch))
+    out_dtype = torch.float32 if dt == "f32" else torch.bfloat16
+    out = _run_mn_ws(to_dev(A, torch), to_dev(B, torch), to_dev(U, torch) if swiglu else None, perm[0], counts[0],
+                     G, out_dtype, ws if need else None, M, N)
+    torch.cuda.synchronize()
+    want = ref.gemm_mn(A, B, mask, G)
+    if swiglu:
+        want = ref.swiglu(want, ref.gemm_mn(A, U, mask, G))
+    keep = ref.expand(mask, G)
+    if dt == "f32":
+        check_gemm(f32_of(out), want, "scheduled random")
+        assert (out.cpu().numpy().view(np.uint32)[~keep] == 0).all()
+    else:
+        if keep.any():
+            check_bf16_store(bits_of(out)[keep], want[keep], "scheduled random bf16")
+        assert (bits_of(out)[~keep] == 0).all()
