@@ -442,7 +442,7 @@ static void launch_tiled(const MnArgs &a, hipStream_t s) {
     // every schedule has at most tiles - L + C <= tiles + C work items, and
     // at most C / 2 split tiles
     hipLaunchKernelGGL((gemm_mn_kernel<BN, W, SWIGLU, F32, true>), dim3(tiles + a.cus), dim3(64 * W), 0, s, a);
-    hipLaunchKernelGGL((gemm_mn_fixup_kernel<BN, SWIGLU, F32>), dim3((eng::kBM / kFixRows) * (a.cus / 2)),
+    hipLaunchKernelGGL((gemm_mn_fixup_kernel<BN, SWIGLU, F32>), dim3((eng::kBM / kFixRows) * max(a.cus / 2, 1)),
                        dim3(256), 0, s, a);
   } else {
     hipLaunchKernelGGL((gemm_mn_kernel<BN, W, SWIGLU, F32, false>), dim3(tiles), dim3(64 * W), 0, s, a);
