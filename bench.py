@@ -311,10 +311,17 @@ def main():
         n = args.copy_bytes // 4
         src = torch.ones(n, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
-        for _ in range(args.steps):
-            torch.mul(src, 1.0, out=dst)  # reads n*4 bytes, writes n*4 bytes
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.mul(src, 1.0, out=dst)  # reads n*4 bytes, writes n*4 bytes
         torch.cuda.synchronize()
-        log(f"copied {n * 4} bytes {args.steps} times")
+        e0.record()
+        for _ in range(args.steps):
+            torch.mul(src, 1.0, out=dst)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        log(f"copied {n * 4} bytes {args.steps} times: {ms:.3f} ms each, "
+            f"{2 * n * 4 / (ms * 1e-3) / 1e9:.0f} GB/s read + write")
         return
 
     p = 1.0 - args.sparsity
