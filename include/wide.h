@@ -13,7 +13,8 @@
  * Common conventions
  *   - Every pointer argument is a DEVICE pointer owned by the caller. The
  *     library never allocates, frees or keeps caller memory; its only scratch
- *     is the attention workspace the caller passes in.
+ *     is the workspace the caller passes in (decoding attention, the split-K
+ *     GEMM paths).
  *   - bf16 tensors are raw IEEE bfloat16 bits (wide_bf16). Matrices are
  *     row-major with the given leading dimension (in elements). Weights are
  *     [out_features][in_features], so every GEMM computes C = A * B^T with
@@ -165,6 +166,25 @@ int wide_gemm_mn_swiglu_ws(const wide_bf16 *A, int64_t lda, const wide_bf16 *Wg,
 size_t wide_gemm_mn_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t G, int swiglu);
 
 /*
+ * wide_order_by_pattern -- a row order for GEMM-K (Appendix B, Eq. 21): the
+ * stable sort of the token rows by the reflected Gray code rank of their
+ * routing pattern over the first min(groups, 8) groups (group 0 the most
+ * significant bit). Rows whose masks agree on those groups become adjacent,
+ * and since neighbouring Gray codes differ in one group, every group's active
+ * rows form few long runs: whole 16-row MFMA fragments then skip a group.
+ * The order is a scheduling choice of this library; GEMM-K's result does not
+ * depend on it.
+ *   mask  [rows][groups] uint8, nonzero = active.
+ *   order out, [rows] int32: order[j] is the token row at sorted position j;
+ *         rows with equal keys keep ascending order.
+ * One workgroup, no scratch memory, nothing read on the host.
+ * Errors: WIDE_ERR_INVALID_ARG for null pointers, rows or groups < 1 or
+ * >= 2^31, or an order that overlaps the mask.
+ */
+int wide_order_by_pattern(const uint8_t *mask, int64_t rows, int64_t groups, int32_t *order,
+                          wide_stream_t stream);
+
+/*
  * wide_gemm_k -- K-axis routed GEMM, GEMM-K (Appendix B, Eq. 21 and
  * Algorithm 3):
  *
@@ -174,18 +194,31 @@ size_t wide_gemm_mn_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t G, 
  *   A [M][K] bf16 (lda), B [N][K] bf16 (ldb), C [M][N] fp32 (ldc).
  *   mask [M][K/G] uint8. beta is 0 or 1. With beta = 0 every entry of C is
  *   written, exact 0 for rows with no active group.
- * The mask is read directly (no reorder output is needed): the A segment of
- * an inactive (row, group) pair is never loaded, and a tile with no active
- * pair only scales its part of C. Summation order is fixed: results are
- * bitwise reproducible run to run.
+ *   order: NULL, or a permutation of 0 .. M-1 (wide_order_by_pattern). With
+ *     it, and N % 256 == 0, the output tiles cover sorted positions: A rows
+ *     are gathered and C rows scattered through the order, a tile runs only
+ *     the K-groups some of its rows keep, and a 16-row MFMA fragment none of
+ *     whose rows keeps the current group skips its multiply-adds. The result
+ *     is the same sum over the same products (the skipped work adds zeros);
+ *     only a K-split tile's grouping of partial sums can differ. An entry
+ *     outside [0, M) is dropped (its row is left unwritten), never
+ *     dereferenced. Ignored for M <= 4 and when N % 256 != 0.
+ * The page's Algorithm 3 gives every (sorted row tile of one group, K-group)
+ * pair a pipeline and adds each partial into C with atomics; here a tile
+ * covers all groups of its rows and keeps C in registers, and the order
+ * replaces the per-group sorted rows of wide_reorder, because one order serves
+ * every group without moving any partial sum.
+ * The A segment of an inactive (row, group) pair is never loaded, and a tile
+ * with no active pair only scales its part of C. Summation order is fixed:
+ * results are bitwise reproducible run to run.
  * Requirements: K % G == 0; lda, ldb >= K and multiples of 8; ldc >= N and a
- * multiple of 4; 16-byte aligned A, B, C; C must not overlap A, B or mask.
- * WIDE_ERR_UNSUPPORTED unless G % 64 == 0, K / G <= 512, N % 128 == 0,
- * lda < 2^22 and ldb < 2^22.
+ * multiple of 4; 16-byte aligned A, B, C; C must not overlap A, B, mask or
+ * order. WIDE_ERR_UNSUPPORTED unless G % 64 == 0, K / G <= 512,
+ * N % 128 == 0, lda < 2^22 and ldb < 2^22.
  */
 int wide_gemm_k(const wide_bf16 *A, int64_t lda, const wide_bf16 *B, int64_t ldb,
                 float *C, int64_t ldc, int beta, int64_t M, int64_t N, int64_t K,
-                int64_t G, const uint8_t *mask, wide_stream_t stream);
+                int64_t G, const int32_t *order, const uint8_t *mask, wide_stream_t stream);
 
 /*
  * wide_gemm_k_ws -- wide_gemm_k (the same product, Appendix B, Eq. 21) with a
@@ -195,10 +228,10 @@ int wide_gemm_k(const wide_bf16 *A, int64_t lda, const wide_bf16 *B, int64_t ldb
  * the partial tiles of all slices but the last, and a second kernel adds them
  * into C.
  *   workspace: device memory of at least wide_gemm_k_workspace_bytes(M, N, K)
- *     bytes, 16-byte aligned, not overlapping A, B, C or mask. Its contents on
- *     entry are ignored and overwritten; calls that share a workspace must not
- *     run at the same time (e.g. on two streams). NULL, or a size of 0 when the
- *     plan needs none, is wide_gemm_k.
+ *     bytes, 16-byte aligned, not overlapping A, B, C, mask or order. Its
+ *     contents on entry are ignored and overwritten; calls that share a
+ *     workspace must not run at the same time (e.g. on two streams). NULL, or
+ *     a size of 0 when the plan needs none, is wide_gemm_k.
  * Results: as wide_gemm_k, bitwise reproducible for a given shape and device.
  * A split tile's sum is C = (beta C + last slice) + slice 0 + slice 1 + ...,
  * which rounds differently from wide_gemm_k's single pass over K.
@@ -207,8 +240,8 @@ int wide_gemm_k(const wide_bf16 *A, int64_t lda, const wide_bf16 *B, int64_t ldb
  */
 int wide_gemm_k_ws(const wide_bf16 *A, int64_t lda, const wide_bf16 *B, int64_t ldb,
                    float *C, int64_t ldc, int beta, int64_t M, int64_t N, int64_t K,
-                   int64_t G, const uint8_t *mask, void *workspace, size_t workspace_bytes,
-                   wide_stream_t stream);
+                   int64_t G, const int32_t *order, const uint8_t *mask, void *workspace,
+                   size_t workspace_bytes, wide_stream_t stream);
 
 /* Bytes of device workspace wide_gemm_k_ws needs for an M x N x K product on
  * the current device (0: no tile is split; also 0 for sizes out of range). */

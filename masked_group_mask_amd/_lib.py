@@ -36,9 +36,10 @@ _SIGS = {
     "wide_gemm_mn_swiglu_ws": [_ptr, _i64, _ptr, _ptr, _i64, _ptr, _i64, _int, _i64, _i64, _i64,
                                _i64, _ptr, _ptr, _ptr, _ptr, _size, _ptr],
     "wide_gemm_mn_workspace_bytes": [_i64, _i64, _i64, _i64, _int],
-    "wide_gemm_k": [_ptr, _i64, _ptr, _i64, _ptr, _i64, _int, _i64, _i64, _i64, _i64, _ptr, _ptr],
-    "wide_gemm_k_ws": [_ptr, _i64, _ptr, _i64, _ptr, _i64, _int, _i64, _i64, _i64, _i64, _ptr, _ptr, _size,
-                       _ptr],
+    "wide_order_by_pattern": [_ptr, _i64, _i64, _ptr, _ptr],
+    "wide_gemm_k": [_ptr, _i64, _ptr, _i64, _ptr, _i64, _int, _i64, _i64, _i64, _i64, _ptr, _ptr, _ptr],
+    "wide_gemm_k_ws": [_ptr, _i64, _ptr, _i64, _ptr, _i64, _int, _i64, _i64, _i64, _i64, _ptr, _ptr, _ptr,
+                       _size, _ptr],
     "wide_gemm_k_workspace_bytes": [_i64] * 3,
     "wide_attn": [_ptr, _ptr, _ptr, _ptr, _int, _i64, _i64, _i64, _i64, _i64, _i64, _int, _f32,
                   _ptr, _ptr, _ptr, _ptr, _ptr, _size, _ptr],
@@ -100,14 +101,38 @@ def _stream() -> ctypes.c_void_p:
 
 
 def _need(t: torch.Tensor, name: str, dtype, ndim: Optional[int] = None):
+    """Type, element type and rank; the device is checked by _on_device once
+    every size has been checked."""
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
-    if not t.is_cuda:
-        raise ValueError(f"{name} must be a device tensor")
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if ndim is not None and t.dim() != ndim:
         raise ValueError(f"{name} must have {ndim} dimensions, got {t.dim()}")
+
+
+def _on_device(first: torch.Tensor, **others) -> None:
+    """Every tensor is a device tensor on `first`'s device (last check before
+    pointers are handed to the library)."""
+    for name, t in (("first operand", first),) + tuple(others.items()):
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if t.device != first.device:
+            raise ValueError(f"{name} is on {t.device}, expected {first.device}")
+
+
+def _sized(t: Optional[torch.Tensor], name: str, dtype, numel: int, last: int):
+    """A contiguous routing tensor of exactly `numel` elements whose last
+    dimension is `last` (the kernels index it with these sizes)."""
+    if t is None:
+        return
+    _need(t, name, dtype)
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.numel() != numel or t.dim() == 0 or t.shape[-1] != last:
+        raise ValueError(f"{name} has shape {tuple(t.shape)}: expected {numel} elements, last dimension {last}")
 
 
 def _rowmajor(t: torch.Tensor, name: str) -> int:
@@ -144,8 +169,27 @@ def reorder(mask: torch.Tensor, perm: Optional[torch.Tensor] = None,
         raise ValueError("perm/counts shape mismatch")
     if not (perm.is_contiguous() and counts.is_contiguous()):
         raise ValueError("perm/counts must be contiguous")
+    _on_device(mask, perm=perm, counts=counts)
     _call("wide_reorder", _p(mask), B, T, NG, _p(perm), _p(counts), _stream())
     return perm, counts
+
+
+def order_by_pattern(mask: torch.Tensor, order: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """mask [M][NG] uint8 (or [1][M][NG]) -> order [M] int32: the token rows
+    stably sorted by the Gray-code rank of their pattern over the first
+    min(NG, 8) groups; GEMM-K's row order."""
+    _need(mask, "mask", torch.uint8)
+    if mask.dim() not in (2, 3) or (mask.dim() == 3 and mask.shape[0] != 1):
+        raise ValueError("mask must be [M][NG] or [1][M][NG]")
+    if not mask.is_contiguous():
+        raise ValueError("mask must be contiguous")
+    M, NG = mask.shape[-2], mask.shape[-1]
+    if order is None:
+        order = torch.empty(M, dtype=torch.int32, device=mask.device)
+    _sized(order, "order", torch.int32, M, M)
+    _on_device(mask, order=order)
+    _call("wide_order_by_pattern", _p(mask), M, NG, _p(order), _stream())
+    return order
 
 
 def router(X: torch.Tensor, W1: torch.Tensor, W2: torch.Tensor, B: int = 1,
@@ -172,23 +216,29 @@ def router(X: torch.Tensor, W1: torch.Tensor, W2: torch.Tensor, B: int = 1,
     logits = torch.empty((M, 2 * NG), dtype=torch.float32, device=dev) if with_logits else None
     perm = torch.empty((B, NG, T), dtype=torch.int32, device=dev) if with_reorder else None
     counts = torch.empty((B, NG), dtype=torch.int32, device=dev) if with_reorder else None
+    _on_device(X, W1=W1, W2=W2)
     _call("wide_router", _p(X), _rowmajor(X, "X"), _p(W1), _p(W2), B, T, D, r, NG, _p(mask),
           _p(logits), _p(perm), _p(counts), _stream())
     return mask, perm, counts, logits
 
 
-def _mn_common(A, G, perm, counts, mask):
+def _routing(M: int, NG: int, perm, counts, mask):
+    """perm [NG][M] int32 and counts [NG] int32 (a wide_reorder output with
+    batch 1) and mask [M][NG] uint8, checked against the problem's sizes
+    before any pointer reaches a kernel."""
+    if (perm is None) != (counts is None):
+        raise ValueError("perm and counts go together")
+    _sized(perm, "perm", torch.int32, NG * M, M)
+    _sized(counts, "counts", torch.int32, NG, NG)
+    _sized(mask, "mask", torch.uint8, M * NG, NG)
+
+
+def _mn_common(A, N, G, perm, counts, mask):
     _need(A, "A", torch.bfloat16, 2)
     lda = _rowmajor(A, "A")
-    if perm is not None:
-        _need(perm, "perm", torch.int32)
-        _need(counts, "counts", torch.int32)
-        if not (perm.is_contiguous() and counts.is_contiguous()):
-            raise ValueError("perm/counts must be contiguous")
-    if mask is not None:
-        _need(mask, "mask", torch.uint8)
-        if not mask.is_contiguous():
-            raise ValueError("mask must be contiguous")
+    if G < 1 or N % G:
+        raise ValueError(f"N = {N} is not a multiple of the group size {G}")
+    _routing(A.shape[0], N // G, perm, counts, mask)
     return lda
 
 
@@ -212,8 +262,8 @@ def gemm_mn(A: torch.Tensor, B: torch.Tensor, G: int, perm: Optional[torch.Tenso
     (zeros if `out` is allocated here). workspace: optional device buffer of
     gemm_mn_workspace_bytes(M, N, K, G) bytes; with it the active tiles are
     scheduled on the device and a partly filled last round is split along K."""
-    lda = _mn_common(A, G, perm, counts, mask)
     _need(B, "B", torch.bfloat16, 2)
+    lda = _mn_common(A, B.shape[0], G, perm, counts, mask)
     ldb = _rowmajor(B, "B")
     M, K = A.shape
     N = B.shape[0]
@@ -224,6 +274,7 @@ def gemm_mn(A: torch.Tensor, B: torch.Tensor, G: int, perm: Optional[torch.Tenso
     _need(out, "out", out.dtype, 2)
     if tuple(out.shape) != (M, N):
         raise ValueError("out shape mismatch")
+    _on_device(A, B=B, out=out, perm=perm, counts=counts, mask=mask, workspace=workspace)
     ws, wsb = _ws(workspace, A)
     _call("wide_gemm_mn_ws", _p(A), lda, _p(B), ldb, _p(out), _rowmajor(out, "out"), _dt(out.dtype),
           M, N, K, G, _p(perm), _p(counts), _p(mask), ws, wsb, _stream())
@@ -236,9 +287,9 @@ def gemm_mn_swiglu(A: torch.Tensor, Wg: torch.Tensor, Wu: torch.Tensor, G: int,
                    out_dtype=torch.bfloat16, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """H = SiLU(A Wg^T) * (A Wu^T) on the active entries. workspace: as gemm_mn
     (gemm_mn_workspace_bytes(M, N, K, G, swiglu=True) bytes)."""
-    lda = _mn_common(A, G, perm, counts, mask)
     _need(Wg, "Wg", torch.bfloat16, 2)
     _need(Wu, "Wu", torch.bfloat16, 2)
+    lda = _mn_common(A, Wg.shape[0], G, perm, counts, mask)
     ldb = _rowmajor(Wg, "Wg")
     if Wu.shape != Wg.shape or _rowmajor(Wu, "Wu") != ldb:
         raise ValueError("Wg and Wu must have the same shape and leading dimension")
@@ -248,8 +299,10 @@ def gemm_mn_swiglu(A: torch.Tensor, Wg: torch.Tensor, Wu: torch.Tensor, G: int,
         raise ValueError("A and Wg disagree on K")
     if out is None:
         out = torch.zeros((M, N), dtype=out_dtype, device=A.device)
+    _need(out, "out", out.dtype, 2)
     if tuple(out.shape) != (M, N):
         raise ValueError("out shape mismatch")
+    _on_device(A, Wg=Wg, Wu=Wu, out=out, perm=perm, counts=counts, mask=mask, workspace=workspace)
     ws, wsb = _ws(workspace, A)
     _call("wide_gemm_mn_swiglu_ws", _p(A), lda, _p(Wg), _p(Wu), ldb, _p(out),
           _rowmajor(out, "out"), _dt(out.dtype), M, N, K, G, _p(perm), _p(counts), _p(mask),
@@ -263,28 +316,34 @@ def gemm_k_workspace_bytes(M: int, N: int, K: int) -> int:
 
 def gemm_k(A: torch.Tensor, B: torch.Tensor, G: int, mask: torch.Tensor,
            out: Optional[torch.Tensor] = None, beta: int = 0,
-           workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+           workspace: Optional[torch.Tensor] = None, order: Optional[torch.Tensor] = None) -> torch.Tensor:
     """C = beta*C + sum over active K-groups of A B^T (fp32 output).
     workspace: optional device buffer of gemm_k_workspace_bytes(M, N, K)
-    bytes; with it the last, partly filled round of tiles is split along K."""
+    bytes; with it the last, partly filled round of tiles is split along K.
+    order: optional [M] int32 row permutation (order_by_pattern(mask)); with
+    it tiles skip the work of groups their rows do not keep."""
     _need(A, "A", torch.bfloat16, 2)
     _need(B, "B", torch.bfloat16, 2)
-    _need(mask, "mask", torch.uint8)
-    if not mask.is_contiguous():
-        raise ValueError("mask must be contiguous")
     M, K = A.shape
     N = B.shape[0]
     if B.shape[1] != K:
         raise ValueError("A and B disagree on K")
+    if G < 1 or K % G:
+        raise ValueError(f"K = {K} is not a multiple of the group size {G}")
+    if mask is None:
+        raise ValueError("gemm_k needs the mask")
+    _sized(mask, "mask", torch.uint8, M * (K // G), K // G)
+    _sized(order, "order", torch.int32, M, M)
     if out is None:
         out = torch.empty((M, N), dtype=torch.float32, device=A.device)
         beta = 0
     _need(out, "out", torch.float32, 2)
     if tuple(out.shape) != (M, N):
         raise ValueError("out shape mismatch")
+    _on_device(A, B=B, out=out, mask=mask, workspace=workspace, order=order)
     ws, wsb = _ws(workspace, A)
     _call("wide_gemm_k_ws", _p(A), _rowmajor(A, "A"), _p(B), _rowmajor(B, "B"), _p(out),
-          _rowmajor(out, "out"), int(beta), M, N, K, G, _p(mask), ws, wsb, _stream())
+          _rowmajor(out, "out"), int(beta), M, N, K, G, _p(order), _p(mask), ws, wsb, _stream())
     return out
 
 
@@ -308,19 +367,27 @@ def attn(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, perm: Optional[torch
     Bk, Tk, Hk, dk = K.shape
     if Bk != B or dk != d or tuple(V.shape) != tuple(K.shape):
         raise ValueError("Q/K/V shapes disagree")
-    for t, n, dt in ((perm, "perm", torch.int32), (counts, "counts", torch.int32),
-                     (mask, "mask", torch.uint8), (leftpad, "leftpad", torch.int32)):
-        if t is not None:
-            _need(t, n, dt)
-            if not t.is_contiguous():
-                raise ValueError(f"{n} must be contiguous")
+    NG = Hk if groups is None else int(groups)
+    if NG < 1:
+        raise ValueError("groups must be positive")
+    if (perm is None) != (counts is None):
+        raise ValueError("perm and counts go together")
+    _sized(perm, "perm", torch.int32, B * NG * Tq, Tq)
+    _sized(counts, "counts", torch.int32, B * NG, NG)
+    _sized(mask, "mask", torch.uint8, B * Tq * NG, NG)
+    _sized(leftpad, "leftpad", torch.int32, B, B)
     if out is None:
         out = torch.zeros((B, Tq, Hq, d), dtype=out_dtype, device=Q.device)
+    _need(out, "out", out.dtype, 4)
     if tuple(out.shape) != (B, Tq, Hq, d) or not out.is_contiguous():
         raise ValueError("out must be a contiguous [B][Tq][Hq][d] tensor")
+    _on_device(Q, K=K, V=V, out=out, perm=perm, counts=counts, mask=mask, leftpad=leftpad,
+               workspace=workspace)
     need = attn_workspace_bytes(B, Tq, Tk, Hq, Hk, d)
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=Q.device)
+    if workspace is not None and not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if groups is None or groups == Hk:
         _call("wide_attn", _p(Q), _p(K), _p(V), _p(out), _dt(out.dtype), B, Tq, Tk, Hq, Hk, d,

@@ -115,7 +115,7 @@ int gemm_mn_impl(const wide_bf16 *A, int64_t lda, const wide_bf16 *B0, const wid
 
 extern "C" {
 
-int wide_abi_version(void) { return 1; }
+int wide_abi_version(void) { return 2; }
 
 const char *wide_status_string(int status) {
   switch (status) {
@@ -182,10 +182,19 @@ int wide_gemm_mn_swiglu_ws(const wide_bf16 *A, int64_t lda, const wide_bf16 *Wg,
                       workspace_bytes, stream);
 }
 
+int wide_order_by_pattern(const uint8_t *mask, int64_t rows, int64_t groups, int32_t *order,
+                          wide_stream_t stream) {
+  if (!mask || !order) return WIDE_ERR_INVALID_ARG;
+  if (rows < 1 || groups < 1 || rows > kI32Max || groups > kI32Max) return WIDE_ERR_INVALID_ARG;
+  if (overlap(order, (size_t)rows * 4, mask, (size_t)rows * groups)) return WIDE_ERR_INVALID_ARG;
+  if (!device_ok()) return WIDE_ERR_NO_DEVICE;
+  return wide::launch_pattern_order(mask, (int)rows, (int)groups, order, reinterpret_cast<hipStream_t>(stream));
+}
+
 int wide_gemm_k(const wide_bf16 *A, int64_t lda, const wide_bf16 *B, int64_t ldb, float *C,
                 int64_t ldc, int beta, int64_t M, int64_t N, int64_t K, int64_t G,
-                const uint8_t *mask, wide_stream_t stream) {
-  return wide_gemm_k_ws(A, lda, B, ldb, C, ldc, beta, M, N, K, G, mask, nullptr, 0, stream);
+                const int32_t *order, const uint8_t *mask, wide_stream_t stream) {
+  return wide_gemm_k_ws(A, lda, B, ldb, C, ldc, beta, M, N, K, G, order, mask, nullptr, 0, stream);
 }
 
 size_t wide_gemm_k_workspace_bytes(int64_t M, int64_t N, int64_t K) {
@@ -195,7 +204,8 @@ size_t wide_gemm_k_workspace_bytes(int64_t M, int64_t N, int64_t K) {
 
 int wide_gemm_k_ws(const wide_bf16 *A, int64_t lda, const wide_bf16 *B, int64_t ldb, float *C,
                    int64_t ldc, int beta, int64_t M, int64_t N, int64_t K, int64_t G,
-                   const uint8_t *mask, void *workspace, size_t workspace_bytes, wide_stream_t stream) {
+                   const int32_t *order, const uint8_t *mask, void *workspace, size_t workspace_bytes,
+                   wide_stream_t stream) {
   if (!A || !B || !C || !mask) return WIDE_ERR_INVALID_ARG;
   if (M < 1 || N < 1 || K < 1 || G < 1) return WIDE_ERR_INVALID_ARG;
   if (M > kI32Max || N > kI32Max || K > kI32Max) return WIDE_ERR_INVALID_ARG;
@@ -204,7 +214,7 @@ int wide_gemm_k_ws(const wide_bf16 *A, int64_t lda, const wide_bf16 *B, int64_t 
   if (!aligned16(A) || !aligned16(B) || !aligned16(C)) return WIDE_ERR_INVALID_ARG;
   const size_t cb = span_bytes(M, N, ldc, 4);
   if (overlap(C, cb, A, span_bytes(M, K, lda, 2)) || overlap(C, cb, B, span_bytes(N, K, ldb, 2)) ||
-      overlap(C, cb, mask, (size_t)M * (K / G)))
+      overlap(C, cb, mask, (size_t)M * (K / G)) || (order && overlap(C, cb, order, (size_t)M * 4)))
     return WIDE_ERR_INVALID_ARG;
   if (G % 64 != 0 || K / G > 512 || N % 128 != 0) return WIDE_ERR_UNSUPPORTED;
   // A tile of 256 rows and a B tile of 128 rows are addressed with 32-bit byte offsets.
@@ -215,12 +225,13 @@ int wide_gemm_k_ws(const wide_bf16 *A, int64_t lda, const wide_bf16 *B, int64_t 
     if (workspace_bytes < need || !aligned16(workspace)) return WIDE_ERR_INVALID_ARG;
     if (need > 0 && (overlap(workspace, need, A, span_bytes(M, K, lda, 2)) ||
                      overlap(workspace, need, B, span_bytes(N, K, ldb, 2)) || overlap(workspace, need, C, cb) ||
-                     overlap(workspace, need, mask, (size_t)M * (K / G))))
+                     overlap(workspace, need, mask, (size_t)M * (K / G)) ||
+                     (order && overlap(workspace, need, order, (size_t)M * 4))))
       return WIDE_ERR_INVALID_ARG;
     if (need == 0) workspace = nullptr;
   }
   if (!device_ok()) return WIDE_ERR_NO_DEVICE;
-  wide::KArgs a{A, lda, B, ldb, C, ldc, beta, (int)M, (int)N, (int)K, (int)G, mask,
+  wide::KArgs a{A, lda, B, ldb, C, ldc, beta, (int)M, (int)N, (int)K, (int)G, mask, order,
                 static_cast<float *>(workspace), workspace_bytes, 0, 0, 0, 1};
   return wide::launch_gemm_k(a, reinterpret_cast<hipStream_t>(stream));
 }

@@ -37,17 +37,20 @@ constexpr int kKRasterM = 32;  // m-tiles per raster group (eng::tile_of)
 // row 32 i + r keeps group g. Thread t reads the mask row of tile row t % 256
 // (for the groups g = t / 256 mod THREADS / 256) and each wave turns one
 // group column of its 64 rows into two words by ballot. Returns whether any
-// row of the tile keeps any group. `flag` is one word of LDS that is free
-// during the prologue.
+// row of the tile keeps any group. `flag` is one word of a stage buffer (the
+// 4-wave tile has no LDS left for a word of its own); the barrier after every
+// wave has read it keeps the first stage loads, issued right after, from
+// overwriting it early.
+// `m` is the token row of this thread's tile row (tid % 256), or -1 for a
+// tile row past the end.
 template <int THREADS>
-__device__ __forceinline__ bool build_bits(const KArgs &a, int m0, WIDE_LDS uint32_t *bits, WIDE_LDS int *flag) {
+__device__ __forceinline__ bool build_bits(const KArgs &a, int m, WIDE_LDS uint32_t *bits, WIDE_LDS int *flag) {
   constexpr int PARTS = THREADS / 256;
   const int NG = a.K / a.G;
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int part = tid / 256, wrow = wave % 4;
-  const int m = m0 + tid % 256;
-  const uint8_t *row = a.mask + (size_t)m * NG;
-  const bool valid = m < a.M;
+  const bool valid = m >= 0;
+  const uint8_t *row = a.mask + (size_t)(valid ? m : 0) * NG;
   if (tid == 0) *flag = 0;
   __syncthreads();
   int any = 0;
@@ -93,7 +96,9 @@ __device__ __forceinline__ bool build_bits(const KArgs &a, int m0, WIDE_LDS uint
   }
   if (any && lane == 0) *flag = 1;
   __syncthreads();
-  return *flag != 0;
+  const bool r = *flag != 0;
+  __syncthreads();
+  return r;
 }
 
 // Stage loader of the tile: A rows predicated by the bit table, B rows
@@ -176,7 +181,9 @@ __global__ __launch_bounds__(64 * W) void gemm_k_kernel(KArgs a) {
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
   const int wm = wave / S::WNW, wn = wave % S::WNW;
 
-  const bool any = build_bits<S::THREADS>(a, m0, (WIDE_LDS uint32_t *)&sBits[0][0], (WIDE_LDS int *)sA1);
+  const int mrow = m0 + (int)threadIdx.x % eng::kBM;
+  const bool any = build_bits<S::THREADS>(a, mrow < a.M ? mrow : -1, (WIDE_LDS uint32_t *)&sBits[0][0],
+                                          (WIDE_LDS int *)sA1);
   eng::Acc<S> acc;
 #pragma unroll
   for (int i = 0; i < S::FN; ++i)
@@ -232,6 +239,294 @@ __global__ __launch_bounds__(64 * W) void gemm_k_kernel(KArgs a) {
   for (int j = 0; j < S::FM; ++j) {
     const int m = m0 + wm * S::TM + j * 16 + lane % 16;
     if (m >= a.M) continue;
+    float *crow = a.C + (size_t)m * a.ldc + n0 + wn * S::TN + 4 * (lane / 16);
+#pragma unroll
+    for (int i = 0; i < S::FN; ++i) {
+      f32x4 v = acc[i][j];
+      if (a.beta) v += *reinterpret_cast<const f32x4 *>(crow + i * 16);
+      *reinterpret_cast<f32x4 *>(crow + i * 16) = v;
+    }
+  }
+}
+
+// ---- Ordered GEMM-K: rows sorted by routing pattern, inactive work skipped --
+//
+// With `order` (a permutation of the token rows that puts rows with the same
+// routing pattern next to each other, e.g. wide_order_by_pattern), a
+// workgroup owns the tile of sorted positions m0 .. m0+256 and features
+// n0 .. n0+256. Its A rows are gathered through the order and its C rows
+// scattered back through it; the accumulators stay in registers in tile
+// order, so no partial result is ever moved between rows. Then:
+//   - the k-loop runs only over the K-groups some row of the tile keeps
+//     (the tile's live groups, listed once from the bit table);
+//   - a load instruction whose 8 rows all skip the step's group is not issued;
+//   - a wave's 16-row A fragment none of whose rows keeps the step's group
+//     skips its multiply-adds (a wave-uniform branch around its 4 MFMAs).
+// An output row's sum runs over the same products in the same order as in
+// the unordered kernel: the work skipped adds exact zeros there.
+//
+// One step: the A and B fragments of the stage are read, then for every A
+// fragment jj its MFMAs (when live), followed in the first half by one of
+// the next stage's 8 load instructions, so the loads stay spread over the
+// step whatever is skipped. The bit words of the group two steps ahead are
+// read from LDS during a step, so no load waits on them.
+struct OrdStep {
+  uint32_t fl;   // bit jj: this wave's A fragment jj has a row that keeps the step's group
+  uint32_t lb;   // byte i: the rows of this wave's A load instruction i that keep it
+  uint32_t li;   // bit i: A load instruction i is issued (its 16-row fragment is live)
+  uint32_t k0;   // byte offset of the step's 64-deep slice of K
+};
+
+// What a step needs from LDS: the 8 bit words of its group (the bit table
+// compacted to live-group order) and the group itself. Read right after a
+// barrier, decoded a step later, so no wait is ever spent on them.
+struct OrdRaw {
+  u32x4 lo, hi;
+  int g;
+  int kk;
+  bool on;
+};
+
+__device__ __forceinline__ OrdRaw ord_fetch(const WIDE_LDS uint32_t *bits, const WIDE_LDS uint16_t *live, int gi,
+                                            int kk, bool on) {
+  OrdRaw r;
+  r.on = on;
+  r.kk = kk;
+  if (on) {
+    r.lo = *(const WIDE_LDS u32x4 *)(bits + gi * 8);
+    r.hi = *(const WIDE_LDS u32x4 *)(bits + gi * 8 + 4);
+    r.g = live[gi];
+  } else {
+    r.lo = r.hi = u32x4{0u, 0u, 0u, 0u};
+    r.g = 0;
+  }
+  return r;
+}
+
+// Decoding for wave (wm, wave): A fragment jj covers tile rows 128 wm + 16 jj
+// .. +15 (half jj % 2 of bit word 4 wm + jj / 2); A load instruction i covers
+// tile rows 8 (wave + 8 i) .. +7 (byte wave % 4 of bit word 2 i + wave / 4),
+// one half of the 16-row fragment in half (wave % 4) / 2 of that word. A load
+// is left out only when that whole fragment is dead: a live fragment is
+// multiplied in full, so its inactive rows must hold the zeros an
+// out-of-range load writes, not an older stage.
+__device__ __forceinline__ OrdStep ord_decode(const OrdRaw &raw, int G, int wm, int wave) {
+  OrdStep r{0u, 0u, 0u, 0u};
+  if (!raw.on) return r;
+  const uint32_t w[8] = {raw.lo[0], raw.lo[1], raw.lo[2], raw.lo[3], raw.hi[0], raw.hi[1], raw.hi[2], raw.hi[3]};
+#pragma unroll
+  for (int jj = 0; jj < 8; ++jj) {
+    const uint32_t word = wm == 0 ? w[jj / 2] : w[4 + jj / 2];
+    r.fl |= (((word >> (16 * (jj % 2))) & 0xffffu) != 0u ? 1u : 0u) << jj;
+  }
+  const int bsh = 8 * (wave % 4), fsh = 16 * ((wave % 4) / 2);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t word = wave < 4 ? w[2 * i] : w[2 * i + 1];
+    r.lb |= ((word >> bsh) & 0xffu) << (8 * i);
+    r.li |= (((word >> fsh) & 0xffffu) != 0u ? 1u : 0u) << i;
+  }
+  r.fl = (uint32_t)__builtin_amdgcn_readfirstlane(r.fl);
+  r.lb = (uint32_t)__builtin_amdgcn_readfirstlane(r.lb);
+  r.li = (uint32_t)__builtin_amdgcn_readfirstlane(r.li);
+  const int g = __builtin_amdgcn_readfirstlane(raw.g);  // wave-uniform: buffer offsets need SGPRs
+  r.k0 = (uint32_t)(g * G + raw.kk * eng::kBK) * 2u;
+  return r;
+}
+
+__global__ __launch_bounds__(512) void gemm_k_ordered_kernel(KArgs a) {
+  using S = eng::Shape<256, 8>;
+  constexpr int BN = 256;
+  __shared__ __attribute__((aligned(1024))) uint16_t sA0[S::A_ELEMS];
+  __shared__ __attribute__((aligned(1024))) uint16_t sB0[S::B_ELEMS];
+  __shared__ __attribute__((aligned(1024))) uint16_t sA1[S::A_ELEMS];
+  __shared__ __attribute__((aligned(1024))) uint16_t sB1[S::B_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint32_t sBits[kKMaxGroups][8];
+  __shared__ int sRows[eng::kBM];
+  __shared__ uint16_t sLive[kKMaxGroups];
+  __shared__ int sScan[S::WAVES + 1];
+
+  const int MT = (a.M + eng::kBM - 1) / eng::kBM;
+  int mt, tn;
+  int part = 0, nparts = 1, slot = 0;
+  {
+    int L = (int)blockIdx.x;
+    if (a.ksplit > 1 && L >= a.head) {
+      slot = (L - a.head) / a.ksplit;
+      part = (L - a.head) % a.ksplit;
+      nparts = a.ksplit;
+      L = a.head + slot;
+    }
+    eng::tile_of<kKRasterM>(a.tile_base + L, MT, a.N / BN, mt, tn);
+  }
+  const int m0 = mt * eng::kBM, n0 = tn * BN;
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int wm = wave / S::WNW, wn = wave % S::WNW;
+  const int NG = a.K / a.G;
+  if (tid < eng::kBM) {
+    // an entry outside [0, M) (not a permutation) is dropped, never dereferenced
+    const int m = m0 + tid < a.M ? a.order[m0 + tid] : -1;
+    sRows[tid] = (unsigned)m < (unsigned)a.M ? m : -1;
+  }
+  __syncthreads();
+  WIDE_LDS uint32_t *bits = (WIDE_LDS uint32_t *)&sBits[0][0];
+  const bool any = build_bits<S::THREADS>(a, sRows[tid % eng::kBM], bits, (WIDE_LDS int *)sA1);
+
+  eng::Acc<S> acc;
+#pragma unroll
+  for (int i = 0; i < S::FN; ++i)
+#pragma unroll
+    for (int j = 0; j < S::FM; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  if (any) {
+    // List the live groups in ascending order (one thread per group).
+    int nlive = 0;
+    for (int g0 = 0; g0 < NG; g0 += S::THREADS) {
+      const int g = g0 + tid;
+      bool on = false;
+      if (g < NG) {
+        const u32x4 lo = *(const WIDE_LDS u32x4 *)(bits + g * 8), hi = *(const WIDE_LDS u32x4 *)(bits + g * 8 + 4);
+        on = ((lo[0] | lo[1] | lo[2] | lo[3]) | (hi[0] | hi[1] | hi[2] | hi[3])) != 0u;
+      }
+      const uint64_t bal = __ballot(on);
+      if (lane == 0) sScan[wave] = __popcll(bal);
+      __syncthreads();
+      int before = nlive, tot = 0;
+#pragma unroll
+      for (int w = 0; w < S::WAVES; ++w) {
+        const int c = sScan[w];
+        before += w < wave ? c : 0;
+        tot += c;
+      }
+      if (on) sLive[before + rank_below(bal)] = (uint16_t)g;
+      nlive += tot;
+      __syncthreads();
+    }
+    // Compact the bit table to live-group order (row gi = group sLive[gi]):
+    // all reads, a barrier, then the writes (a slot may be another's source).
+    {
+      u32x4 lo = u32x4{0u, 0u, 0u, 0u}, hi = lo;
+      const bool mine = tid < nlive;
+      if (mine) {
+        const int g = sLive[tid];
+        lo = *(const WIDE_LDS u32x4 *)(bits + g * 8);
+        hi = *(const WIDE_LDS u32x4 *)(bits + g * 8 + 4);
+      }
+      __syncthreads();
+      if (mine) {
+        *(WIDE_LDS u32x4 *)(bits + tid * 8) = lo;
+        *(WIDE_LDS u32x4 *)(bits + tid * 8 + 4) = hi;
+      }
+      __syncthreads();
+    }
+    const int spg = a.G / eng::kBK;
+    const int nk_all = nlive * spg;
+    const int kb = part * nk_all / nparts;
+    const int nk = (part + 1) * nk_all / nparts - kb;
+
+    const rsrc_t ar = make_rsrc(a.A, (uint64_t)a.M * a.lda * 2);
+    const rsrc_t br = make_rsrc(a.B + (size_t)n0 * a.ldb, (uint64_t)BN * a.ldb * 2);
+    uint32_t aoff[S::AI], boff[S::BI];
+#pragma unroll
+    for (int i = 0; i < S::AI; ++i) {
+      const int r = eng::load_row<8>(wave, i, lane);
+      const int phys = sRows[r];
+      aoff[i] = phys >= 0 ? (uint32_t)phys * (uint32_t)a.lda * 2u + eng::load_chunk_bytes(r, lane) : kOffNone;
+    }
+#pragma unroll
+    for (int i = 0; i < S::BI; ++i) {
+      const int r = eng::load_row<8>(wave, i, lane);
+      boff[i] = (uint32_t)r * (uint32_t)a.ldb * 2u + eng::load_chunk_bytes(r, lane);
+    }
+    const WIDE_LDS uint16_t *live = (const WIDE_LDS uint16_t *)sLive;
+    const int wv = __builtin_amdgcn_readfirstlane(wave), wmu = __builtin_amdgcn_readfirstlane(wm);
+    // One load slot: slots 2i are A instruction i (not issued when its whole
+    // 16-row fragment skips the group), slots 2i + 1 B instruction i.
+    auto load_slot = [&](int q, const OrdStep &st, eng::lds_u16 *sa, eng::lds_u16 *sb, bool on) {
+      const int i = q / 2;
+      if (q % 2 == 0) {
+        const uint32_t byte = (st.lb >> (8 * i)) & 0xffu;
+        if (on && ((st.li >> i) & 1u))
+          eng::load_lds(ar, eng::load_dst<8>(sa, wave, i), ((byte >> (lane / 8)) & 1u) ? aoff[i] : kOffNone, st.k0);
+      } else if (on) {
+        eng::load_lds(br, eng::load_dst<8>(sb, wave, i), boff[i], st.k0);
+      }
+    };
+    auto compute = [&](const eng::lds_u16 *sa, const eng::lds_u16 *sb, uint32_t fl, const OrdStep &nx,
+                       eng::lds_u16 *na, eng::lds_u16 *nb, bool nx_on) {
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        u32x4 fb[S::FN], fa[S::FM];
+#pragma unroll
+        for (int i = 0; i < S::FN; ++i) {
+          const int row = wn * S::TN + i * 16 + lane % 16;
+          fb[i] = *(const WIDE_LDS u32x4 *)(sb + row * eng::kBK + (((s * 4 + lane / 16) ^ eng::swz(row)) * 8));
+        }
+#pragma unroll
+        for (int jj = 0; jj < S::FM; ++jj) {
+          const int row = wm * S::TM + jj * 16 + lane % 16;
+          fa[jj] = *(const WIDE_LDS u32x4 *)(sa + row * eng::kBK + (((s * 4 + lane / 16) ^ eng::swz(row)) * 8));
+        }
+        // keep the fragment reads here, ahead of the branches
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int jj = 0; jj < S::FM; ++jj) {
+          if (fl & (1u << jj)) {
+#pragma unroll
+            for (int i = 0; i < S::FN; ++i) acc[i][jj] = mfma16x16x32(fb[i], fa[jj], acc[i][jj]);
+          }
+          if (s == 0) {
+            __builtin_amdgcn_sched_barrier(0);
+            load_slot(jj, nx, na, nb, nx_on);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+      }
+    };
+
+    eng::lds_u16 *a0 = (eng::lds_u16 *)sA0, *b0 = (eng::lds_u16 *)sB0;
+    eng::lds_u16 *a1 = (eng::lds_u16 *)sA1, *b1 = (eng::lds_u16 *)sB1;
+    // step counters of the step after next: group index and step within it
+    int gi2 = (kb + 2) / spg, kk2 = (kb + 2) % spg;
+    OrdStep cur = ord_decode(ord_fetch(bits, live, kb / spg, kb % spg, nk > 0), a.G, wmu, wv);
+    OrdStep nxt = ord_decode(ord_fetch(bits, live, (kb + 1) / spg, (kb + 1) % spg, nk > 1), a.G, wmu, wv);
+#pragma unroll
+    for (int q = 0; q < S::NLOAD; ++q) load_slot(q, cur, a0, b0, nk > 0);
+    for (int t = 0; t < nk; ++t) {
+      WIDE_WAIT_VM_LGKM0(0);
+      WIDE_BARRIER();
+      // the step after next: read now, decoded at the end of this step
+      const OrdRaw raw = ord_fetch(bits, live, gi2, kk2, t + 2 < nk);
+      if (++kk2 == spg) {
+        kk2 = 0;
+        ++gi2;
+      }
+      const bool odd = t & 1;
+      compute(odd ? a1 : a0, odd ? b1 : b0, cur.fl, nxt, odd ? a0 : a1, odd ? b0 : b1, t + 1 < nk);
+      cur = nxt;
+      // Pin the raw words here: without this the compiler moves them to
+      // scalar registers right after the reads, waiting on them there.
+      OrdRaw late = raw;
+      asm volatile("" : "+v"(late.lo), "+v"(late.hi), "+v"(late.g));
+      nxt = ord_decode(late, a.G, wmu, wv);
+    }
+    WIDE_WAIT_VM_LGKM0(0);
+  }
+
+  if (part < nparts - 1) {
+    float *wt = a.ws + ((size_t)slot * (nparts - 1) + part) * (size_t)(eng::kBM * BN);
+#pragma unroll
+    for (int j = 0; j < S::FM; ++j) {
+      float *wrow = wt + (size_t)(wm * S::TM + j * 16 + lane % 16) * BN + wn * S::TN + 4 * (lane / 16);
+#pragma unroll
+      for (int i = 0; i < S::FN; ++i) *reinterpret_cast<f32x4 *>(wrow + i * 16) = acc[i][j];
+    }
+    return;
+  }
+#pragma unroll
+  for (int j = 0; j < S::FM; ++j) {
+    const int m = sRows[wm * S::TM + j * 16 + lane % 16];
+    if (m < 0) continue;
     float *crow = a.C + (size_t)m * a.ldc + n0 + wn * S::TN + 4 * (lane / 16);
 #pragma unroll
     for (int i = 0; i < S::FN; ++i) {
@@ -362,8 +657,10 @@ __global__ __launch_bounds__(256) void gemm_k_fixup_kernel(KArgs a) {
   const int MT = (a.M + eng::kBM - 1) / eng::kBM;
   int mt, tn;
   eng::tile_of<kKRasterM>(a.head + slot, MT, a.N / 256, mt, tn);
-  const int m = mt * eng::kBM + r;
-  if (m >= a.M) return;
+  const int pos = mt * eng::kBM + r;
+  if (pos >= a.M) return;
+  const int m = a.order ? a.order[pos] : pos;
+  if ((unsigned)m >= (unsigned)a.M) return;
   float *c = a.C + (size_t)m * a.ldc + tn * 256 + 4 * q;
   f32x4 v = *reinterpret_cast<const f32x4 *>(c);
   const float *w = a.ws + (size_t)slot * (a.ksplit - 1) * TILE + (size_t)r * 256 + 4 * q;
@@ -429,7 +726,20 @@ int launch_gemm_k(const KArgs &a0, hipStream_t s) {
       case 3: hipLaunchKernelGGL(gemv_k_kernel<3>, grid, block, 0, s, a); break;
       default: hipLaunchKernelGGL(gemv_k_kernel<4>, grid, block, 0, s, a); break;
     }
+  } else if (a.N % 256 == 0 && a.order != nullptr) {
+    // rows through the order; the leftover round split along K with a workspace
+    const KSplitPlan p = ksplit_plan(a.M, a.N, a.K);
+    if (p.ksplit > 1 && a.ws != nullptr && a.ws_bytes >= plan_bytes(p)) {
+      const int tail = p.tiles - p.head;
+      a.head = p.head;
+      a.ksplit = p.ksplit;
+      hipLaunchKernelGGL(gemm_k_ordered_kernel, dim3(p.head + tail * p.ksplit), dim3(512), 0, s, a);
+      hipLaunchKernelGGL(gemm_k_fixup_kernel, dim3(tail * (eng::kBM * 64 / 256)), dim3(256), 0, s, a);
+    } else {
+      hipLaunchKernelGGL(gemm_k_ordered_kernel, dim3(mt * (a.N / 256)), dim3(512), 0, s, a);
+    }
   } else if (a.N % 256 == 0) {
+    a.order = nullptr;
     const KSplitPlan p = ksplit_plan(a.M, a.N, a.K);
     if (p.ksplit > 1 && a.ws != nullptr && a.ws_bytes >= plan_bytes(p)) {
       const int tail = p.tiles - p.head;
@@ -449,6 +759,7 @@ int launch_gemm_k(const KArgs &a0, hipStream_t s) {
       }
     }
   } else {
+    a.order = nullptr;
     hipLaunchKernelGGL((gemm_k_kernel<128, 4>), dim3(mt * (a.N / 128)), dim3(256), 0, s, a);
   }
   return check_launch();

@@ -29,6 +29,9 @@ __device__ __forceinline__ int xcd_remap(int p, int total) {
 
 int launch_reorder(const uint8_t *mask, int batch, int rows, int groups, int32_t *perm,
                    int32_t *counts, hipStream_t stream);
+// Stable sort of the rows by the Gray-code rank of their pattern over the
+// first min(groups, 8) groups.
+int launch_pattern_order(const uint8_t *mask, int rows, int groups, int32_t *order, hipStream_t stream);
 
 struct MnArgs {
   const uint16_t *A;
@@ -64,6 +67,10 @@ struct KArgs {
   int beta;
   int M, N, K, G;
   const uint8_t *mask;
+  // Optional permutation of the token rows (rows with equal routing patterns
+  // adjacent); with it the tiles cover sorted positions and skip the work of
+  // groups their rows do not keep.
+  const int32_t *order;
   // Caller's workspace for the K-split tiles (may be null: then no K split).
   float *ws;
   size_t ws_bytes;

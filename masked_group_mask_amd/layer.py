@@ -29,8 +29,15 @@ def to_device(x: np.ndarray) -> torch.Tensor:
 class PrefillLayer:
     """One masked layer of shape `s` (workloads.LayerShape) on the GPU."""
 
-    def __init__(self, s, host: dict, with_dense: bool = True, scheduled_mn: dict | None = None):
+    def __init__(self, s, host: dict, with_dense: bool = True, scheduled_mn: dict | None = None,
+                 ordered_k: tuple = ()):
         self.s = s
+        # GEMM-K ops that run over rows sorted by routing pattern (their tiles
+        # skip the K-groups and 16-row fragments whose rows all skip a group).
+        # The sort looks at the first 8 groups, which is every attention group
+        # of these shapes; with the 68-272 FFN groups it would order rows for 8
+        # of them only, so down_proj keeps token order by default.
+        self.ordered_k = tuple(ordered_k)
         # GEMM-MN ops that take the workspace (tiles scheduled from counts on
         # the device, group by group, and a short last round split along K),
         # per mask set. Routed masks give every group its own row set, so
@@ -58,6 +65,8 @@ class PrefillLayer:
         self.cnt_a = torch.empty((B, s.Hk), dtype=i32, device=dev)
         self.perm_f = torch.empty((1, s.NG_ffn, M), dtype=i32, device=dev)
         self.cnt_f = torch.empty((1, s.NG_ffn), dtype=i32, device=dev)
+        self.order_a = torch.empty(M, dtype=i32, device=dev)
+        self.order_f = torch.empty(M, dtype=i32, device=dev)
         # Every consumer reads only the active entries of its input (GEMM-K
         # loads only the active (row, group) segments, attention gathers active
         # rows), so the intermediate buffers need no zero-initialisation.
@@ -85,6 +94,10 @@ class PrefillLayer:
         if op == "reorder":
             mg.reorder(ma, self.perm_a, self.cnt_a)
             mg.reorder(mf.view(1, s.M, s.NG_ffn), self.perm_f, self.cnt_f)
+            if "o_proj" in self.ordered_k:
+                mg.order_by_pattern(ma.view(s.M, s.Hk), self.order_a)
+            if "down_proj" in self.ordered_k:
+                mg.order_by_pattern(mf.view(s.M, s.NG_ffn), self.order_f)
         elif op == "q_proj":
             # B = 1: the attention reorder is also the flattened reorder of the GEMMs.
             mg.gemm_mn(self.x, self.wq, s.G_attn, perm=self.perm_a[0], counts=self.cnt_a[0],
@@ -94,13 +107,14 @@ class PrefillLayer:
                     counts=self.cnt_a, out=self.o)
         elif op == "o_proj":
             mg.gemm_k(self.o.view(s.M, s.Hq * s.d), self.wo, s.G_attn, ma.view(s.M, s.Hk),
-                      out=self.y_attn, workspace=self.ws)
+                      out=self.y_attn, workspace=self.ws,
+                      order=self.order_a if "o_proj" in self.ordered_k else None)
         elif op == "gate_up_swiglu":
             mg.gemm_mn_swiglu(self.x, self.wg, self.wu, s.G_ffn, perm=self.perm_f[0],
                               counts=self.cnt_f[0], out=self.h, workspace=self._mn_ws("gate_up_swiglu", which))
         elif op == "down_proj":
             mg.gemm_k(self.h, self.wd, s.G_ffn, mf.view(s.M, s.NG_ffn), out=self.y_ffn,
-                      workspace=self.ws)
+                      workspace=self.ws, order=self.order_f if "down_proj" in self.ordered_k else None)
         else:
             raise ValueError(f"unknown op {op!r}")
 

@@ -43,7 +43,7 @@ def test_status_strings(lib):
     assert _lib.status_string(INVALID) == "invalid argument"
     assert _lib.status_string(UNSUPPORTED) == "unsupported shape or mode"
     assert _lib.status_string(12345) == "unknown status"
-    assert lib.wide_abi_version() == 1
+    assert lib.wide_abi_version() == 2
 
 
 FAKE = 1 << 20      # a 16-byte aligned, non-null address that is never dereferenced
@@ -139,17 +139,17 @@ def test_gemm_mn_workspace_validation(lib):
 
 def gk(lib, **kw):
     a = dict(A=P(0), lda=256, B=P(1), ldb=256, C=P(2), ldc=128, beta=0, M=32, N=128, K=256,
-             G=128, mask=P(3))
+             G=128, order=None, mask=P(3))
     a.update(kw)
     return lib.wide_gemm_k(a["A"], a["lda"], a["B"], a["ldb"], a["C"], a["ldc"], a["beta"],
-                           a["M"], a["N"], a["K"], a["G"], a["mask"], None)
+                           a["M"], a["N"], a["K"], a["G"], a["order"], a["mask"], None)
 
 
-def gkw(lib, ws, wsb, M, N, K, G=128):
+def gkw(lib, ws, wsb, M, N, K, G=128, order=None):
     """wide_gemm_k_ws on fake pointers spaced far enough apart for these sizes."""
     base = 1 << 40
     A, B, C, mask = (ctypes.c_void_p(base + i * (1 << 34)) for i in range(4))
-    return lib.wide_gemm_k_ws(A, K, B, K, C, N, 0, M, N, K, G, mask, ws, wsb, None)
+    return lib.wide_gemm_k_ws(A, K, B, K, C, N, 0, M, N, K, G, order, mask, ws, wsb, None)
 
 
 def test_gemm_k_workspace_plan(lib):
@@ -172,6 +172,9 @@ def test_gemm_k_workspace_validation(lib):
     assert gkw(lib, ctypes.c_void_p(ws.value + 4), need, 256, 256, 4096) == INVALID  # misaligned
     alias = ctypes.c_void_p((1 << 40) + 2 * (1 << 34))                        # C's address
     assert gkw(lib, alias, need, 256, 256, 4096) == INVALID
+    # the workspace may not overlap the order either
+    order = ctypes.c_void_p((1 << 40) + 9 * (1 << 34))
+    assert gkw(lib, order, need, 256, 256, 4096, order=order) == INVALID
 
 
 def test_gemm_k_validation(lib):
@@ -182,6 +185,17 @@ def test_gemm_k_validation(lib):
     assert gk(lib, C=P(1)) == INVALID                       # C aliases B
     assert gk(lib, G=32, K=256) == UNSUPPORTED
     assert gk(lib, N=64, ldc=64) == UNSUPPORTED
+    assert gk(lib, order=P(2)) == INVALID                   # C overlaps the order
+
+
+def test_order_by_pattern_validation(lib):
+    f = lib.wide_order_by_pattern
+    assert f(None, 64, 8, P(1), None) == INVALID
+    assert f(P(0), 64, 8, None, None) == INVALID
+    assert f(P(0), 0, 8, P(1), None) == INVALID
+    assert f(P(0), 64, 0, P(1), None) == INVALID
+    assert f(P(0), 1 << 31, 8, P(1), None) == INVALID
+    assert f(P(0), 64, 8, P(0), None) == INVALID            # order overlaps the mask
 
 
 def at(lib, **kw):

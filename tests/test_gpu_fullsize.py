@@ -42,6 +42,13 @@ def check_reorder(mask, perm, counts):
     assert np.array_equal(perm, want)
 
 
+def active_only(bits, keep):
+    """The GPU's bf16 intermediate with the entries it never writes (inactive
+    groups: the buffers are not cleared) set to +0, which is all the next
+    operator may depend on."""
+    return np.where(keep, bits, np.uint16(0))
+
+
 def check_ffn(s, host, rows, h_gpu_bits, y_gpu):
     m2 = host["mask_ffn"].reshape(s.M, s.NG_ffn)
     X = host["x"][rows]
@@ -51,7 +58,7 @@ def check_ffn(s, host, rows, h_gpu_bits, y_gpu):
     want_h = ref.swiglu(gate, up)
     keep = ref.expand(mr, s.G_ffn)
     check_bf16_store(h_gpu_bits[keep], want_h[keep], f"{s.name} gate/up+SwiGLU")
-    want_y = ref.gemm_k(h_gpu_bits, host["w_down"], mr, s.G_ffn)
+    want_y = ref.gemm_k(active_only(h_gpu_bits, keep), host["w_down"], mr, s.G_ffn)
     check_gemm(y_gpu, want_y, f"{s.name} down_proj")
 
 
@@ -60,7 +67,9 @@ PREFILL = [
     ("qwen14b_prefill", {"p_attn": 0.5, "p_ffn": 0.5, "G_ffn": 128}),
     ("qwen14b_prefill", {"p_attn": 0.5, "p_ffn": 0.5, "G_ffn": 64}),
     ("qwen14b_prefill", {"p_attn": 0.5, "p_ffn": 0.5, "G_ffn": 256}),
+    ("qwen14b_prefill", {"p_attn": 0.75, "p_ffn": 0.75, "G_ffn": 64}),
     ("qwen14b_prefill", {"p_attn": 0.75, "p_ffn": 0.75, "G_ffn": 128}),
+    ("qwen14b_prefill", {"p_attn": 0.75, "p_ffn": 0.75, "G_ffn": 256}),
 ]
 
 
@@ -86,13 +95,15 @@ def test_prefill_layer_full_size(name, over):
     keep = ref.expand(mr, s.G_attn)
     check_bf16_store(q_bits[rows][keep], want_q[keep], f"{s.name} q_proj")
     # attention, on the GPU's own Q
-    want_o = ref.attention(q_bits.reshape(s.B, s.T, s.Hq, s.d), host["k"], host["v"],
+    q_in = active_only(q_bits, ref.expand(ma2, s.G_attn))
+    want_o = ref.attention(q_in.reshape(s.B, s.T, s.Hq, s.d), host["k"], host["v"],
                            host["mask_attn"], queries=[(0, int(t)) for t in rows])
     o_bits = bits_of(layer.o).reshape(s.M, s.Hq, s.d)[rows]
     keep_h = np.repeat(mr != 0, s.Hq // s.Hk, axis=1)
     check_attn_bf16(o_bits[keep_h], want_o[keep_h], f"{s.name} attention")
     # o_proj on the GPU's own O
-    want_y = ref.gemm_k(o_bits.reshape(len(rows), -1), host["w_o"], mr, s.G_attn)
+    o_in = active_only(o_bits, keep_h[..., None]).reshape(len(rows), -1)
+    want_y = ref.gemm_k(o_in, host["w_o"], mr, s.G_attn)
     check_gemm(layer.y_attn.cpu().numpy()[rows].astype(np.float64), want_y, f"{s.name} o_proj")
     # FFN
     check_ffn(s, host, rows, bits_of(layer.h)[rows], layer.y_ffn.cpu().numpy()[rows].astype(np.float64))
@@ -152,10 +163,11 @@ def test_decode_step_full_size(B):
     want_q = ref.gemm_mn(host["x"], host["w_q"], ma2, s.G_attn)
     keep = ref.expand(ma2, s.G_attn)
     check_bf16_store(q_bits[keep], want_q[keep], "decode q_proj")
-    want_o = ref.attention(q_bits.reshape(B, 1, s.Hq, s.d), host["k"], host["v"], host["mask_attn"])
+    want_o = ref.attention(active_only(q_bits, keep).reshape(B, 1, s.Hq, s.d), host["k"], host["v"],
+                           host["mask_attn"])
     o_bits = bits_of(layer.o).reshape(B, s.Hq, s.d)
     keep_h = np.repeat(ma2 != 0, s.Hq // s.Hk, axis=1)
     check_attn_bf16(o_bits[keep_h], want_o.reshape(B, s.Hq, s.d)[keep_h], "decode attention")
-    want_y = ref.gemm_k(o_bits.reshape(B, -1), host["w_o"], ma2, s.G_attn)
+    want_y = ref.gemm_k(active_only(o_bits, keep_h[..., None]).reshape(B, -1), host["w_o"], ma2, s.G_attn)
     check_gemm(layer.y_attn.cpu().numpy().astype(np.float64), want_y, "decode o_proj")
     check_ffn(s, host, np.arange(B), bits_of(layer.h), layer.y_ffn.cpu().numpy().astype(np.float64))

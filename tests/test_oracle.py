@@ -2,8 +2,9 @@
 
 Each oracle function is checked against something other than itself: hand-
 worked fixtures (tests/golden), a different library's routine (torch on the
-CPU, float64), the naive gather-scatter formulations of WIDE Appendix A, brute
-force on tiny inputs, closed forms and invariants. Non-square shapes are used
+CPU, float64), element-by-element brute force of the routed products (the
+meaning of WIDE Appendix A's naive N- and K-axis pruning), closed forms and
+invariants. Non-square shapes are used
 throughout so that a transposed operand or a swapped index fails.
 """
 import json
@@ -117,22 +118,21 @@ def test_reorder_special_cases():
 # GEMM-MN
 # ---------------------------------------------------------------------------
 
-def naive_n_axis(A, B, mask, G):
-    """WIDE Appendix A, naive N-axis pruning: per token, materialise the
-    selected weight rows, take token-wise dot products, scatter into zeros.
-    Written per token because the number of selected groups varies."""
+def brute_n_axis(A, B, mask, G):
+    """Element-by-element definition of N-axis routing (WIDE Appendix A, naive
+    N-axis pruning): output (m, n) is the full dot product over k when token m
+    keeps group n // G, and zero otherwise. Plain loops, no library routine."""
     M, K = A.shape
     N = B.shape[0]
     C = np.zeros((M, N))
-    offset = np.arange(G)
     for m in range(M):
-        groups = np.nonzero(mask[m])[0]
-        if len(groups) == 0:
-            continue
-        J = (groups[:, None] * G + offset).reshape(-1)      # selected columns
-        B_sub = B[J, :]                                      # [N'][K]
-        C_sub = np.einsum("k,nk->n", A[m], B_sub)
-        C[m, J] = C_sub
+        for n in range(N):
+            if mask[m][n // G] == 0:
+                continue
+            acc = 0.0
+            for k in range(K):
+                acc += A[m, k] * B[n, k]
+            C[m, n] = acc
     return C
 
 
@@ -149,8 +149,8 @@ def test_gemm_mn_pins(M, N, K, G):
     mask = wl.random_mask(3, (M, N // G))
     Af, Bf = ref.from_bf16(A), ref.from_bf16(B)
     C = ref.gemm_mn(A, B, mask, G)
-    # naive gather-scatter formulation (Appendix A)
-    np.testing.assert_allclose(C, naive_n_axis(Af, Bf, mask, G), rtol=1e-12, atol=1e-12)
+    # element-by-element brute force (Appendix A, naive N-axis pruning)
+    np.testing.assert_allclose(C, brute_n_axis(Af, Bf, mask, G), rtol=1e-12, atol=1e-12)
     # all-ones mask: the dense product, by another library
     dense = (torch.from_numpy(Af) @ torch.from_numpy(Bf).T).numpy()
     np.testing.assert_allclose(ref.gemm_mn(A, B, np.ones_like(mask), G), dense, rtol=1e-12, atol=1e-12)
@@ -181,21 +181,20 @@ def test_gemm_mn_bruteforce_tiny():
 # GEMM-K
 # ---------------------------------------------------------------------------
 
-def naive_k_axis(A, B, mask, G):
-    """WIDE Appendix A, naive K-axis pruning: per token, gather the selected
-    reduction indices of A and the matching columns of B, then dot."""
+def brute_k_axis(A, B, mask, G):
+    """Element-by-element definition of K-axis routing (WIDE Appendix A, naive
+    K-axis pruning): output (m, n) sums A[m, k] B[n, k] over the reduction
+    indices k whose group k // G token m keeps. Plain loops."""
     M, K = A.shape
     N = B.shape[0]
     C = np.zeros((M, N))
-    offset = np.arange(G)
     for m in range(M):
-        groups = np.nonzero(mask[m])[0]
-        if len(groups) == 0:
-            continue
-        J = (groups[:, None] * G + offset).reshape(-1)
-        A_sub = A[m, J]                      # [K']
-        B_sub = B[:, J]                      # [N][K']
-        C[m] = np.einsum("k,nk->n", A_sub, B_sub)
+        for n in range(N):
+            acc = 0.0
+            for k in range(K):
+                if mask[m][k // G] != 0:
+                    acc += A[m, k] * B[n, k]
+            C[m, n] = acc
     return C
 
 
@@ -212,7 +211,7 @@ def test_gemm_k_pins(M, N, K, G):
     mask = wl.random_mask(8, (M, K // G))
     Af, Bf = ref.from_bf16(A), ref.from_bf16(B)
     C = ref.gemm_k(A, B, mask, G)
-    np.testing.assert_allclose(C, naive_k_axis(Af, Bf, mask, G), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(C, brute_k_axis(Af, Bf, mask, G), rtol=1e-12, atol=1e-12)
     dense = (torch.from_numpy(Af) @ torch.from_numpy(Bf).T).numpy()
     np.testing.assert_allclose(ref.gemm_k(A, B, np.ones_like(mask), G), dense, rtol=1e-12, atol=1e-12)
     assert (ref.gemm_k(A, B, np.zeros_like(mask), G) == 0).all()
@@ -405,6 +404,68 @@ def test_attn_layer_empty_mask_is_zero():
     V = wl.random_bf16(64, (B, T, Hk, d))
     q, o, y = ref.attn_layer(X, Wq, K, V, Wo, np.zeros((B, T, Hk), np.uint8), Hq, Hk, d)
     assert (q == 0).all() and (o == 0).all() and (y == 0).all()
+
+
+def _attn_layer_inputs(seed, B=2, T=12, D=48, Hq=6, Hk=2, d=16):
+    X = wl.random_bf16(seed, (B * T, D))
+    Wq = wl.random_bf16(seed + 1, (Hq * d, D), 0.1)
+    Wo = wl.random_bf16(seed + 2, (D, Hq * d), 0.1)
+    K = wl.random_bf16(seed + 3, (B, T, Hk, d))
+    V = wl.random_bf16(seed + 4, (B, T, Hk, d))
+    return X, Wq, Wo, K, V
+
+
+def _within_one_bf16_step(got, want):
+    """got is a bf16 value within one rounding of the real number want."""
+    return np.all(np.abs(got - want) <= 2.0 ** -8 * np.abs(want) + 1e-300)
+
+
+def test_attn_layer_all_ones_is_the_dense_sublayer():
+    """Section 3.1, Eq. 1-2 with every group kept: the masked attention
+    sub-layer is the plain dense one. Each stage is checked against torch on
+    the CPU (float64 matmul, SDPA with grouped KV heads), fed the oracle's own
+    stored bf16 intermediate so a wrong group size, head mapping or reshape
+    shows up as a mismatch."""
+    B, T, D, Hq, Hk, d = 2, 12, 48, 6, 2, 16
+    X, Wq, Wo, K, V = _attn_layer_inputs(600, B, T, D, Hq, Hk, d)
+    ones = np.ones((B, T, Hk), np.uint8)
+    q, o, y = ref.attn_layer(X, Wq, K, V, Wo, ones, Hq, Hk, d)
+    tq = (torch.from_numpy(ref.from_bf16(X)) @ torch.from_numpy(ref.from_bf16(Wq)).T).numpy()
+    assert _within_one_bf16_step(q, tq)
+    q_bits = wl.f32_to_bf16_bits(q.astype(np.float32)).reshape(B, T, Hq, d)
+    to = sdpa(q_bits, K, V, True)
+    assert _within_one_bf16_step(o.reshape(B, T, Hq, d), to)
+    o_in = torch.from_numpy(o.reshape(B * T, Hq * d))
+    ty = (o_in @ torch.from_numpy(ref.from_bf16(Wo)).T).numpy()
+    np.testing.assert_allclose(y, ty, rtol=1e-12, atol=1e-12)
+
+
+def test_attn_layer_switched_off_group():
+    """Switching one group off for some tokens zeroes exactly that group's
+    heads in q and o for those tokens, leaves every other entry unchanged, and
+    removes exactly that group's o_proj term from y (Eq. 2 and Eq. 21)."""
+    B, T, D, Hq, Hk, d = 1, 10, 40, 6, 3, 16
+    X, Wq, Wo, K, V = _attn_layer_inputs(610, B, T, D, Hq, Hk, d)
+    ones = np.ones((B, T, Hk), np.uint8)
+    q1, o1, y1 = ref.attn_layer(X, Wq, K, V, Wo, ones, Hq, Hk, d)
+    g, toks = 1, [0, 3, 9]
+    m = ones.copy()
+    m[0, toks, g] = 0
+    q, o, y = ref.attn_layer(X, Wq, K, V, Wo, m, Hq, Hk, d)
+    G = (Hq // Hk) * d
+    cols = np.zeros(Hq * d, bool)
+    cols[g * G:(g + 1) * G] = True
+    off = np.zeros((B * T, Hq * d), bool)
+    off[np.ix_(toks, cols)] = True
+    o2, o12 = o.reshape(B * T, -1), o1.reshape(B * T, -1)
+    assert (q[off] == 0).all() and (o2[off] == 0).all()
+    assert np.array_equal(q[~off], q1[~off]) and np.array_equal(o2[~off], o12[~off])
+    wo = ref.from_bf16(Wo)
+    removed = np.zeros_like(y1)
+    removed[toks] = o12[toks][:, cols] @ wo[:, cols].T
+    np.testing.assert_allclose(y, y1 - removed, rtol=1e-12, atol=1e-12)
+    others = np.setdiff1d(np.arange(T), toks)
+    assert np.array_equal(y[others], y1[others])
 
 
 def test_work_counts():
