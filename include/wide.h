@@ -51,7 +51,8 @@ typedef enum {
   WIDE_ERR_INVALID_ARG = -1,   /* null pointer, bad size, misalignment, aliasing */
   WIDE_ERR_UNSUPPORTED = -2,   /* valid request this build does not implement */
   WIDE_ERR_NO_DEVICE = -3,     /* no usable HIP device */
-  WIDE_ERR_LAUNCH = -4         /* the HIP runtime rejected a kernel launch */
+  WIDE_ERR_LAUNCH = -4,        /* the HIP runtime rejected a kernel launch */
+  WIDE_ERR_TOO_LARGE = -5      /* needs more scratch than wide_attn_noalloc's built-in buffer */
 } wide_status;
 
 typedef enum { WIDE_DTYPE_BF16 = 0, WIDE_DTYPE_F32 = 1 } wide_dtype;
@@ -320,6 +321,28 @@ int wide_attn_grouped(const wide_bf16 *Q, const wide_bf16 *K, const wide_bf16 *V
                       int64_t groups, int64_t d, int causal, float scale,
                       const int32_t *leftpad, const int32_t *perm, const int32_t *counts,
                       const uint8_t *mask, void *workspace, size_t workspace_bytes,
+                      wide_stream_t stream);
+
+/*
+ * wide_attn_noalloc -- wide_attn for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same computation, arguments and results as
+ * wide_attn, minus the workspace. Decoding (Tq = 1) keeps its split-KV
+ * partials in a scratch array built into the library, 32 MiB per device,
+ * held from the first call on a device until the process ends; prefill
+ * needs no scratch. Nothing is allocated or freed by the call. The partials
+ * a call reads are always written earlier in the same call, so the array
+ * needs no clearing, but every call on one device shares it: calls that
+ * overlap on one device (two streams) race and must be serialised by the
+ * caller.
+ * Errors: as wide_attn, plus WIDE_ERR_TOO_LARGE when
+ * wide_attn_workspace_bytes(B, Tq, Tk, Hq, Hk, d) exceeds 32 MiB (for
+ * decoding: B * Hq * ceil(Tk / 64) > 63550).
+ */
+int wide_attn_noalloc(const wide_bf16 *Q, const wide_bf16 *K, const wide_bf16 *V, void *O,
+                      int o_dtype, int64_t B, int64_t Tq, int64_t Tk, int64_t Hq, int64_t Hk,
+                      int64_t d, int causal, float scale, const int32_t *leftpad,
+                      const int32_t *perm, const int32_t *counts, const uint8_t *mask,
                       wide_stream_t stream);
 
 /* Bytes of device workspace wide_attn needs for these sizes (0 if none). */

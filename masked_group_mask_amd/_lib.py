@@ -47,6 +47,8 @@ _SIGS = {
                     _ptr],
     "wide_attn_grouped": [_ptr, _ptr, _ptr, _ptr, _int, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _int,
                           _f32, _ptr, _ptr, _ptr, _ptr, _ptr, _size, _ptr],
+    "wide_attn_noalloc": [_ptr, _ptr, _ptr, _ptr, _int, _i64, _i64, _i64, _i64, _i64, _i64, _int, _f32,
+                          _ptr, _ptr, _ptr, _ptr, _ptr],
     "wide_attn_workspace_bytes": [_i64] * 6,
     "wide_status_string": [_int],
     "wide_abi_version": [],
@@ -355,10 +357,13 @@ def attn(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, perm: Optional[torch
          counts: Optional[torch.Tensor] = None, mask: Optional[torch.Tensor] = None,
          causal: bool = True, scale: float = 0.0, leftpad: Optional[torch.Tensor] = None,
          out: Optional[torch.Tensor] = None, out_dtype=torch.bfloat16,
-         workspace: Optional[torch.Tensor] = None, groups: Optional[int] = None) -> torch.Tensor:
+         workspace: Optional[torch.Tensor] = None, groups: Optional[int] = None,
+         noalloc: bool = False) -> torch.Tensor:
     """Head-group-masked GQA attention; Q [B][Tq][Hq][d], K/V [B][Tk][Hk][d].
     groups: routing groups (default Hk); finer groups gate fewer query heads
-    each (mask [B][Tq][groups], perm/counts from reorder of that mask)."""
+    each (mask [B][Tq][groups], perm/counts from reorder of that mask).
+    noalloc: call wide_attn_noalloc (the library's built-in decode scratch;
+    no workspace is allocated here; `out` must then be given)."""
     for t, n in ((Q, "Q"), (K, "K"), (V, "V")):
         _need(t, n, torch.bfloat16, 4)
         if not t.is_contiguous():
@@ -376,6 +381,8 @@ def attn(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, perm: Optional[torch
     _sized(counts, "counts", torch.int32, B * NG, NG)
     _sized(mask, "mask", torch.uint8, B * Tq * NG, NG)
     _sized(leftpad, "leftpad", torch.int32, B, B)
+    if noalloc and out is None:
+        raise ValueError("noalloc needs the output tensor: the call allocates nothing")
     if out is None:
         out = torch.zeros((B, Tq, Hq, d), dtype=out_dtype, device=Q.device)
     _need(out, "out", out.dtype, 4)
@@ -383,6 +390,12 @@ def attn(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, perm: Optional[torch
         raise ValueError("out must be a contiguous [B][Tq][Hq][d] tensor")
     _on_device(Q, K=K, V=V, out=out, perm=perm, counts=counts, mask=mask, leftpad=leftpad,
                workspace=workspace)
+    if noalloc:
+        if workspace is not None or (groups is not None and groups != Hk):
+            raise ValueError("noalloc takes no workspace and only one routing group per KV head")
+        _call("wide_attn_noalloc", _p(Q), _p(K), _p(V), _p(out), _dt(out.dtype), B, Tq, Tk, Hq, Hk, d,
+              int(bool(causal)), float(scale), _p(leftpad), _p(perm), _p(counts), _p(mask), _stream())
+        return out
     need = attn_workspace_bytes(B, Tq, Tk, Hq, Hk, d)
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=Q.device)

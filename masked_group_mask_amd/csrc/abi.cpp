@@ -124,6 +124,7 @@ const char *wide_status_string(int status) {
     case WIDE_ERR_UNSUPPORTED: return "unsupported shape or mode";
     case WIDE_ERR_NO_DEVICE: return "no HIP device";
     case WIDE_ERR_LAUNCH: return "kernel launch failed";
+    case WIDE_ERR_TOO_LARGE: return "needs more scratch than the built-in buffer holds";
     default: return "unknown status";
   }
 }
@@ -276,11 +277,17 @@ size_t wide_attn_workspace_bytes(int64_t B, int64_t Tq, int64_t Tk, int64_t Hq, 
   return wide::attn_workspace_bytes(B, Tq, Tk, Hq, Hk, d);
 }
 
-int wide_attn_grouped(const wide_bf16 *Q, const wide_bf16 *K, const wide_bf16 *V, void *O, int o_dtype,
-                      int64_t B, int64_t Tq, int64_t Tk, int64_t Hq, int64_t Hk, int64_t groups, int64_t d,
-                      int causal, float scale, const int32_t *leftpad, const int32_t *perm,
-                      const int32_t *counts, const uint8_t *mask, void *workspace, size_t workspace_bytes,
-                      wide_stream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Validates and launches attention. builtin: the decode scratch is this
+// device's built-in array (workspace arguments ignored); sizes that need more
+// than it holds are refused.
+int attn_impl(const wide_bf16 *Q, const wide_bf16 *K, const wide_bf16 *V, void *O, int o_dtype, int64_t B,
+              int64_t Tq, int64_t Tk, int64_t Hq, int64_t Hk, int64_t groups, int64_t d, int causal, float scale,
+              const int32_t *leftpad, const int32_t *perm, const int32_t *counts, const uint8_t *mask,
+              void *workspace, size_t workspace_bytes, bool builtin, wide_stream_t stream) {
   if (!Q || !K || !V || !O) return WIDE_ERR_INVALID_ARG;
   if (B < 1 || Tq < 1 || Tk < 1 || Hq < 1 || Hk < 1 || d < 1) return WIDE_ERR_INVALID_ARG;
   if (B > 65535 || Hq > 65535 || Tq > kI32Max || Tk > kI32Max) return WIDE_ERR_INVALID_ARG;
@@ -293,13 +300,19 @@ int wide_attn_grouped(const wide_bf16 *Q, const wide_bf16 *K, const wide_bf16 *V
   if (Tq == 1 && !perm && !mask) return WIDE_ERR_INVALID_ARG;
   if (Tq == 1 && perm && !counts) return WIDE_ERR_INVALID_ARG;
   const size_t need = wide::attn_workspace_bytes(B, Tq, Tk, Hq, Hk, d);
-  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return WIDE_ERR_INVALID_ARG;
+  if (builtin) {
+    if (need > wide::kAttnScratchBytes) return WIDE_ERR_TOO_LARGE;
+    workspace = nullptr;  // taken below, once every other argument has passed
+  } else if (need > 0 && (workspace == nullptr || workspace_bytes < need)) {
+    return WIDE_ERR_INVALID_ARG;
+  }
   const size_t ob = (size_t)B * Tq * Hq * d * (o_dtype == WIDE_DTYPE_F32 ? 4 : 2);
   const size_t qb = (size_t)B * Tq * Hq * d * 2, kb = (size_t)B * Tk * Hk * d * 2;
   if (overlap(O, ob, Q, qb) || overlap(O, ob, K, kb) || overlap(O, ob, V, kb))
     return WIDE_ERR_INVALID_ARG;
-  if (need > 0 && (overlap(workspace, need, O, ob) || overlap(workspace, need, Q, qb) ||
-                   overlap(workspace, need, K, kb) || overlap(workspace, need, V, kb)))
+  if (!builtin && need > 0 &&
+      (overlap(workspace, need, O, ob) || overlap(workspace, need, Q, qb) || overlap(workspace, need, K, kb) ||
+       overlap(workspace, need, V, kb)))
     return WIDE_ERR_INVALID_ARG;
   if (d != 128) return WIDE_ERR_UNSUPPORTED;
   // Per-sequence Q/K/V are addressed with 32-bit byte offsets.
@@ -308,6 +321,11 @@ int wide_attn_grouped(const wide_bf16 *Q, const wide_bf16 *K, const wide_bf16 *V
   // Decoding merges at most 4096 splits of 64 keys.
   if (Tq == 1 && (Hq / Hk > 16 || Tk > 4096 * 64)) return WIDE_ERR_UNSUPPORTED;
   if (!device_ok()) return WIDE_ERR_NO_DEVICE;
+  if (builtin && need > 0) {
+    int st = WIDE_OK;
+    workspace = wide::attn_scratch(&st);
+    if (st != WIDE_OK) return st;
+  }
   wide::AttnArgs a{};
   a.Q = Q;
   a.K = K;
@@ -329,6 +347,27 @@ int wide_attn_grouped(const wide_bf16 *Q, const wide_bf16 *K, const wide_bf16 *V
   a.mask = perm ? nullptr : mask;
   a.workspace = workspace;
   return wide::launch_attn(a, reinterpret_cast<hipStream_t>(stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+int wide_attn_grouped(const wide_bf16 *Q, const wide_bf16 *K, const wide_bf16 *V, void *O, int o_dtype,
+                      int64_t B, int64_t Tq, int64_t Tk, int64_t Hq, int64_t Hk, int64_t groups, int64_t d,
+                      int causal, float scale, const int32_t *leftpad, const int32_t *perm,
+                      const int32_t *counts, const uint8_t *mask, void *workspace, size_t workspace_bytes,
+                      wide_stream_t stream) {
+  return attn_impl(Q, K, V, O, o_dtype, B, Tq, Tk, Hq, Hk, groups, d, causal, scale, leftpad, perm, counts, mask,
+                   workspace, workspace_bytes, false, stream);
+}
+
+int wide_attn_noalloc(const wide_bf16 *Q, const wide_bf16 *K, const wide_bf16 *V, void *O, int o_dtype,
+                      int64_t B, int64_t Tq, int64_t Tk, int64_t Hq, int64_t Hk, int64_t d, int causal,
+                      float scale, const int32_t *leftpad, const int32_t *perm, const int32_t *counts,
+                      const uint8_t *mask, wide_stream_t stream) {
+  return attn_impl(Q, K, V, O, o_dtype, B, Tq, Tk, Hq, Hk, Hk, d, causal, scale, leftpad, perm, counts, mask,
+                   nullptr, 0, true, stream);
 }
 
 int wide_attn(const wide_bf16 *Q, const wide_bf16 *K, const wide_bf16 *V, void *O, int o_dtype,

@@ -30,6 +30,8 @@
 // splits of each active head with log-sum-exp weights.
 #include <math.h>
 
+#include <mutex>
+
 #include "common.hpp"
 #include "launch.hpp"
 #include "mma_engine.hpp"
@@ -547,6 +549,36 @@ __global__ __launch_bounds__(kMergeThreads) void attn_decode_merge_kernel(AttnAr
     else
       reinterpret_cast<uint16_t *>(a.O)[idx] = f2bf(out);
   }
+}
+
+// ---------------------------------------------------------------------------
+// Built-in scratch for callers that cannot allocate (wide_attn_noalloc).
+// ---------------------------------------------------------------------------
+
+// One array per device, alive until the process ends. In host code its name
+// only stands for the symbol: the device address comes from
+// hipGetSymbolAddress, queried once per device with that device current.
+static __device__ __align__(256) unsigned char scratch[kAttnScratchBytes];
+
+void *attn_scratch(int *status) {
+  static std::mutex mu;
+  static void *ptr[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    *status = WIDE_ERR_NO_DEVICE;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (ptr[dev] == nullptr) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) {
+      *status = WIDE_ERR_LAUNCH;
+      return nullptr;
+    }
+    ptr[dev] = p;
+  }
+  *status = WIDE_OK;
+  return ptr[dev];
 }
 
 size_t attn_workspace_bytes(int64_t B, int64_t Tq, int64_t Tk, int64_t Hq, int64_t Hk, int64_t d) {

@@ -103,6 +103,11 @@ struct AttnArgs {
   void *workspace;
 };
 int launch_attn(const AttnArgs &a, hipStream_t stream);
+// Size of the built-in decode scratch of wide_attn_noalloc (one per device).
+constexpr size_t kAttnScratchBytes = size_t(32) << 20;
+// Device address of this device's built-in scratch (queried once per device);
+// null with *status set on failure.
+void *attn_scratch(int *status);
 
 struct RouterArgs {
   const uint16_t *X;   // [M][ldx] bf16

@@ -222,6 +222,26 @@ def test_attn_validation(lib):
     assert at(lib, Tq=1, Tk=4096, perm=None, counts=None, mask=P(6), ws=P(7), wsb=need - 4) == INVALID
 
 
+def test_attn_noalloc_validation(lib):
+    def na(**kw):
+        a = dict(Q=P(0), K=P(1), V=P(2), O=P(3), dt=0, B=1, Tq=1, Tk=16, Hq=8, Hk=2, d=128, causal=1,
+                 scale=0.0, leftpad=None, perm=None, counts=None, mask=P(5))
+        a.update(kw)
+        return lib.wide_attn_noalloc(a["Q"], a["K"], a["V"], a["O"], a["dt"], a["B"], a["Tq"], a["Tk"],
+                                     a["Hq"], a["Hk"], a["d"], a["causal"], a["scale"], a["leftpad"],
+                                     a["perm"], a["counts"], a["mask"], None)
+    TOO_LARGE = -5
+    assert na(Q=None) == INVALID
+    assert na(Hq=6, Hk=4) == INVALID
+    # 16 x 64 heads x 1024 splits of 132 floats: 69 MB > 32 MiB of built-in scratch
+    big = dict(B=16, Tk=65536, Hq=64, Hk=8)
+    assert na(**big) == TOO_LARGE
+    assert _lib.status_string(TOO_LARGE).startswith("needs more scratch")
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        assert na() == NO_DEVICE
+
+
 def test_attn_grouped_validation(lib):
     def call(groups, Hq=8, Hk=2):
         return lib.wide_attn_grouped(P(0), P(1), P(2), P(3), 1, 1, 16, 16, Hq, Hk, groups, 128, 1,
