@@ -286,6 +286,9 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-router", action="store_true")
     ap.add_argument("--no-torch-dense", action="store_true")
+    ap.add_argument("--ordered-k", default="", metavar="OPS",
+                    help="comma-separated GEMM-K ops (o_proj, down_proj) to run over rows sorted by "
+                         "routing pattern")
     ap.add_argument("--only", metavar="OP", default=None,
                     help="profiling aid: after one full masked step, run only this op --steps times")
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -331,7 +334,8 @@ def main():
     host = wl.make_layer(s, seed=0)
     log(f"inputs ready in {time.perf_counter() - t0:.1f} s")
     from masked_group_mask_amd.layer import PrefillLayer
-    layer = PrefillLayer(s, host, with_dense=not args.no_dense)
+    ordered = tuple(o for o in args.ordered_k.split(",") if o)
+    layer = PrefillLayer(s, host, with_dense=not args.no_dense, ordered_k=ordered)
     flops = metrics.layer_flops(s, host["mask_attn"], host["mask_ffn"])
     ones_a = np.ones_like(host["mask_attn"])
     ones_f = np.ones_like(host["mask_ffn"])
