@@ -205,6 +205,155 @@ def bench_torch_dense(torch, s, ours_dense_ms: dict, steps=10, warmup=3):
     }
 
 
+def bench_app_a(torch, mg, sizes=(2048, 4096, 8192), G=128, reps=3, naive_limit_gb=80.0):
+    """The page's GEMM pruning comparison (Appendix A, Fig. 11) on MI355X: for
+    M-, N- and K-axis routing of C = A B^T with M = N = K = S and half of the
+    routing units on, the time, active TFLOP/s and peak extra device memory of
+
+      dense    -- torch F.linear (hipBLASLt) over the whole problem;
+      naive    -- gather-scatter in torch ops: the selected rows (M axis) or
+                  every token's own weight subset (N and K axes, a
+                  [tokens][units][K] tensor) are materialised, multiplied
+                  (batched matrix-vector products) and scattered back;
+      grouped  -- after this library's reorder, one torch GEMM per group over
+                  that group's active rows (the counts are read on the host,
+                  a device-to-host synchronisation per call);
+      fused    -- this library's kernels: reorder + GEMM-MN (M and N axes,
+                  the M axis being the one-group case) or GEMM-K (K axis).
+
+    Every token keeps exactly half of the groups (a random half per token),
+    so the naive per-token gather has a fixed width. Peak memory excludes
+    the dense output C (pre-allocated for every variant). A naive run whose
+    gathered tensor would pass naive_limit_gb is skipped and reported so."""
+    import torch.nn.functional as F
+    dev = "cuda"
+    out = {"what": "C = A B^T, bf16, half of the routing units on per token, G = %d; "
+                   "time = median of %d runs (ms), peak = extra device memory beyond A, B and C (GB)" % (G, reps),
+           "rows": []}
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        base = torch.cuda.memory_allocated()
+        torch.cuda.reset_peak_memory_stats()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return float(np.median(ts)), (torch.cuda.max_memory_allocated() - base) / 1e9
+
+    for S in sizes:
+        M = N = K = S
+        gen = torch.Generator(device="cpu").manual_seed(S)
+        A = torch.randn(M, K, generator=gen).to(torch.bfloat16).to(dev)
+        B = (torch.randn(N, K, generator=gen) * 0.02).to(torch.bfloat16).to(dev)
+        C = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+        C32 = torch.empty(M, N, dtype=torch.float32, device=dev)
+        NG = S // G
+        R = NG // 2
+        # every token keeps R random groups: sorted indices [M][R] and the mask [M][NG]
+        pick = torch.rand(M, NG, generator=gen).argsort(dim=1)[:, :R].sort(dim=1).values
+        mask = torch.zeros(M, NG, dtype=torch.uint8)
+        mask.scatter_(1, pick, 1)
+        pick, mask = pick.to(dev), mask.to(dev)
+        rows = torch.randperm(M, generator=gen)[: M // 2].sort().values.to(dev)   # M axis: half the tokens
+        mrow = torch.zeros(M, 1, dtype=torch.uint8, device=dev)
+        mrow[rows] = 1
+        units = (torch.arange(G, device=dev)[None, None, :] + pick[:, :, None] * G).reshape(M, R * G)
+        dense_flops = 2.0 * M * N * K
+
+        def add(axis, variant, ms, peak, note=""):
+            out["rows"].append({"axis": axis, "S": S, "variant": variant, "ms": ms,
+                                "active_tflops": dense_flops / 2 / (ms * 1e-3) / 1e12 if ms else None,
+                                "peak_extra_gb": peak, "note": note})
+            shown = "skipped" if ms is None else f"{ms:.3f} ms"
+            pk_s = "n/a" if peak is None else f"+{peak:.2f} GB"
+            log(f"app-A {axis} S={S} {variant}: {shown}, peak {pk_s} {note}")
+
+        ms, pk = timed(lambda: torch.matmul(A, B.T, out=C))
+        add("dense", "dense", ms, pk, "torch matmul, all units")
+
+        # ---- M axis (depth routing: half of the token rows) ----
+        def naive_m():
+            Cm = torch.zeros(M, N, dtype=torch.bfloat16, device=dev)
+            Cm[rows] = F.linear(A.index_select(0, rows), B)
+            return Cm
+        ms, pk = timed(naive_m)
+        add("M", "naive", ms, pk - M * N * 2 / 1e9)
+        pm = torch.empty(1, 1, M, dtype=torch.int32, device=dev)
+        cm = torch.empty(1, 1, dtype=torch.int32, device=dev)
+
+        def fused_m():
+            mg.reorder(mrow.view(1, M, 1), pm, cm)
+            mg.gemm_mn(A, B, N, perm=pm[0], counts=cm[0], out=C)
+        ms, pk = timed(fused_m)
+        add("M", "fused", ms, pk, "reorder + GEMM-MN with one group")
+
+        # ---- N axis ----
+        gathered_gb = M * R * G * K * 2 / 1e9
+        if gathered_gb <= naive_limit_gb:
+            def naive_n():
+                Bsub = B.index_select(0, units.reshape(-1)).view(M, R * G, K)       # every token's rows of B
+                Csub = torch.bmm(Bsub, A.unsqueeze(2)).squeeze(2)                    # [M][R G]
+                Cn = torch.zeros(M, N, dtype=torch.bfloat16, device=dev)
+                Cn.scatter_(1, units, Csub)
+                return Cn
+            ms, pk = timed(naive_n)
+            add("N", "naive", ms, pk - M * N * 2 / 1e9)
+        else:
+            add("N", "naive", None, None, "skipped: the gathered weight tensor alone needs %.0f GB" % gathered_gb)
+        perm, counts = mg.reorder(mask.view(1, M, NG))
+        Bg = [B[g * G:(g + 1) * G].contiguous() for g in range(NG)]
+
+        def grouped_n():
+            cnt = counts[0].tolist()                       # device-to-host synchronisation
+            for g in range(NG):
+                r = perm[0, g, : cnt[g]].long()
+                C[r, g * G:(g + 1) * G] = F.linear(A.index_select(0, r), Bg[g])
+        ms, pk = timed(grouped_n)
+        add("N", "grouped", ms, pk, "one torch GEMM per group after the reorder")
+
+        def fused_n():
+            mg.reorder(mask.view(1, M, NG), perm, counts)
+            mg.gemm_mn(A, B, G, perm=perm[0], counts=counts[0], out=C)
+        ms, pk = timed(fused_n)
+        add("N", "fused", ms, pk, "reorder + GEMM-MN")
+
+        # ---- K axis ----
+        if gathered_gb <= naive_limit_gb:
+            def naive_k():
+                Asub = torch.gather(A, 1, units)                                     # [M][R G]
+                Bsub = B.index_select(1, units.reshape(-1)).view(N, M, R * G).permute(1, 0, 2).contiguous()
+                return torch.bmm(Bsub, Asub.unsqueeze(2)).squeeze(2)                 # [M][N]
+            ms, pk = timed(naive_k)
+            add("K", "naive", ms, pk - M * N * 2 / 1e9)
+        else:
+            add("K", "naive", None, None, "skipped: the gathered weight tensor alone needs %.0f GB" % gathered_gb)
+        BgK = [B[:, g * G:(g + 1) * G].contiguous() for g in range(NG)]
+
+        def grouped_k():
+            cnt = counts[0].tolist()
+            C32.zero_()
+            for g in range(NG):
+                r = perm[0, g, : cnt[g]].long()
+                part = F.linear(A.index_select(0, r)[:, g * G:(g + 1) * G].contiguous(), BgK[g])
+                C32.index_add_(0, r, part.float())
+        ms, pk = timed(grouped_k)
+        add("K", "grouped", ms, pk, "one torch GEMM per group after the reorder, index_add into fp32 C")
+
+        def fused_k():
+            mg.gemm_k(A, B, G, mask, out=C32)
+        ms, pk = timed(fused_k)
+        add("K", "fused", ms, pk, "GEMM-K (fp32 output)")
+        del A, B, C, C32, Bg, BgK
+        torch.cuda.empty_cache()
+    return out
+
+
 def measured_traffic(op: str):
     """Bytes per launch of `op` from profiles/traffic.json (two rocprofv3
     counter passes, scaled by the same counters on a copy of known size), or
@@ -286,6 +435,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-router", action="store_true")
     ap.add_argument("--no-torch-dense", action="store_true")
+    ap.add_argument("--no-app-a", action="store_true",
+                    help="skip the naive / grouped / fused GEMM pruning comparison (the page's Appendix A)")
     ap.add_argument("--ordered-k", default="", metavar="OPS",
                     help="comma-separated GEMM-K ops (o_proj, down_proj) to run over rows sorted by "
                          "routing pattern")
@@ -389,6 +540,9 @@ def main():
     if not args.no_dense and not args.no_torch_dense and s.Hq:
         out["torch_dense"] = bench_torch_dense(torch, s, out["dense_per_op_ms"])
         log("torch dense GEMMs (ms): " + ", ".join(f"{k} {v:.3f}" for k, v in out["torch_dense"]["per_op_ms"].items()))
+    if not args.no_app_a:
+        log("timing the naive / grouped / fused GEMM pruning comparison")
+        out["app_a_gemm_pruning"] = bench_app_a(torch, mg)
     if not args.no_router:
         out["router"] = bench_router(torch, wl, s)
         log("routers (+reorder): " + ", ".join(f"{k} {v * 1e3:.1f} us"
