@@ -75,34 +75,20 @@ def hold_gpu(torch, ms: float) -> None:
     sleep(int(ms * hold_gpu.cycles_per_ms))
 
 
-def bench_decode(torch, wl, metrics, B=1, steps=50, sets=3):
-    """Decode step of the Llama3.1-8B shape: B sequences with one new token
-    each, KV cache of 16384 per sequence, half of the attention and FFN groups
-    off for every token. Weight/KV sets rotate so the 256 MB
-    Infinity Cache cannot hold the active set across steps.
-
-    Timed two ways: as individual launches (HIP events around each op, the
-    GPU held busy first so the host has queued every timed launch), and as a
-    captured HIP graph of the step replayed back to back (whole step, gaps
-    between kernels included). The headline rate is the graph replay's."""
-    from masked_group_mask_amd.layer import DECODE_OPS, DecodeLayer
-    s = wl.shape("llama8b_decode", B=B)
-    host = wl.make_layer(s, seed=1)
-    nbytes = metrics.decode_bytes(s, host["mask_attn"], host["mask_ffn"])
-    total = sum(nbytes.values())
-    layer = DecodeLayer(s, host, sets=sets)
+def _time_decode(torch, layer, ops, steps, sets):
+    """(per-op medians, whole step as individual launches, whole step as a
+    replayed HIP graph), all in ms."""
     for i in range(5):
         layer.step(i)
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(DECODE_OPS) + 1)] for _ in range(steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(ops) + 1)] for _ in range(steps)]
     hold_gpu(torch, 20.0)
     for i in range(steps):
         layer.step(i, evs[i])
     torch.cuda.synchronize()
     per_op = {op: float(np.median([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(steps)]))
-              for j, op in enumerate(DECODE_OPS)}
+              for j, op in enumerate(ops)}
     launch_ms = float(np.median([evs[i][0].elapsed_time(evs[i][-1]) for i in range(steps)]))
-
     graphs = []
     for k in range(sets):
         g = torch.cuda.CUDAGraph()
@@ -119,7 +105,35 @@ def bench_decode(torch, wl, metrics, B=1, steps=50, sets=3):
         graphs[i % sets].replay()
     e1.record()
     torch.cuda.synchronize()
-    graph_ms = e0.elapsed_time(e1) / steps
+    return per_op, launch_ms, e0.elapsed_time(e1) / steps
+
+
+def bench_decode(torch, wl, metrics, B=1, steps=50, sets=3):
+    """Decode step of the Llama3.1-8B shape: B sequences with one new token
+    each, KV cache of 16384 per sequence, half of the attention and FFN groups
+    off for every token. Weight/KV sets rotate so the 256 MB
+    Infinity Cache cannot hold the active set across steps.
+
+    Timed two ways: as individual launches (HIP events around each op, the
+    GPU held busy first so the host has queued every timed launch), and as a
+    captured HIP graph of the step replayed back to back (whole step, gaps
+    between kernels included). The headline rate is the graph replay's. The
+    same kernels on all-ones masks (every weight and KV byte read) give the
+    decode speedup."""
+    from masked_group_mask_amd.layer import DECODE_OPS, DecodeLayer
+    s = wl.shape("llama8b_decode", B=B)
+    host = wl.make_layer(s, seed=1)
+    nbytes = metrics.decode_bytes(s, host["mask_attn"], host["mask_ffn"])
+    total = sum(nbytes.values())
+    layer = DecodeLayer(s, host, sets=sets)
+    per_op, launch_ms, graph_ms = _time_decode(torch, layer, DECODE_OPS, steps, sets)
+    del layer
+    ones = dict(host, mask_attn=np.ones_like(host["mask_attn"]), mask_ffn=np.ones_like(host["mask_ffn"]))
+    dense_bytes = sum(metrics.decode_bytes(s, ones["mask_attn"], ones["mask_ffn"]).values())
+    dense = DecodeLayer(s, ones, sets=sets)
+    d_per_op, _, d_graph_ms = _time_decode(torch, dense, DECODE_OPS, steps, sets)
+    del dense
+    torch.cuda.empty_cache()
     return {
         "workload": ("llama8b_decode (B=%d, KV 16384 per sequence, 4/8 attention and 56/112 FFN groups "
                      "on per token)" % B),
@@ -130,8 +144,14 @@ def bench_decode(torch, wl, metrics, B=1, steps=50, sets=3):
         "frac_of_hbm_peak": total / (graph_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
         "per_op_ms": per_op,
         "per_op_GB_per_s": {op: nbytes[op] / (per_op[op] * 1e-3) / 1e9 for op in DECODE_OPS},
+        "dense_graph_ms_per_step": d_graph_ms,
+        "dense_GB_per_s": dense_bytes / (d_graph_ms * 1e-3) / 1e9,
+        "dense_per_op_ms": d_per_op,
+        "speedup_vs_dense": d_graph_ms / graph_ms,
+        "ideal_speedup": dense_bytes / total,
         "timing": ("graph: %d back-to-back replays of the captured step; per op: median over %d steps "
-                   "of HIP events around each launch; %d rotated weight/KV sets" % (steps, steps, sets)),
+                   "of HIP events around each launch; %d rotated weight/KV sets; dense = the same "
+                   "kernels on all-ones masks" % (steps, steps, sets)),
     }
 
 
@@ -354,6 +374,24 @@ def bench_app_a(torch, mg, sizes=(2048, 4096, 8192), G=128, reps=3, naive_limit_
     return out
 
 
+def bench_batched_leftpad(torch, wl, metrics, steps=5, warmup=5, T=4096, leftpad=(0, 1024)):
+    """Two left-padded sequences through the same layer driver (the bench
+    shape with B = 2, T = 4096: the same 8192 tokens, the keys before each
+    sequence's padding excluded): masked and all-ones steps."""
+    from masked_group_mask_amd.layer import PrefillLayer
+    s = wl.shape("qwen14b_prefill", B=2, T=T)
+    host = wl.make_layer(s, seed=5)
+    layer = PrefillLayer(s, host, leftpad=leftpad)
+    flops = sum(metrics.layer_flops(s, host["mask_attn"], host["mask_ffn"], leftpad=leftpad).values())
+    ms, per_op, _ = time_steps(layer, "masked", steps, warmup, torch)
+    dense_ms, _, _ = time_steps(layer, "dense", steps, warmup, torch)
+    del layer
+    torch.cuda.empty_cache()
+    return {"workload": "qwen14b_prefill, B=2 x T=%d, leftpad %s, 50%% of the groups off" % (T, list(leftpad)),
+            "ms_per_step": ms, "active_tflops": flops / (ms * 1e-3) / 1e12, "dense_ms_per_step": dense_ms,
+            "speedup_vs_dense": dense_ms / ms, "per_op_ms": per_op}
+
+
 def measured_traffic(op: str):
     """Bytes per launch of `op` from profiles/traffic.json (two rocprofv3
     counter passes, scaled by the same counters on a copy of known size), or
@@ -540,6 +578,11 @@ def main():
     if not args.no_dense and not args.no_torch_dense and s.Hq:
         out["torch_dense"] = bench_torch_dense(torch, s, out["dense_per_op_ms"])
         log("torch dense GEMMs (ms): " + ", ".join(f"{k} {v:.3f}" for k, v in out["torch_dense"]["per_op_ms"].items()))
+    if not args.no_dense:
+        log("timing two left-padded sequences")
+        out["prefill_b2_leftpad"] = bench_batched_leftpad(torch, wl, metrics)
+        log(f"B=2 leftpad: {out['prefill_b2_leftpad']['ms_per_step']:.3f} ms/step, "
+            f"{out['prefill_b2_leftpad']['speedup_vs_dense']:.2f}x all-ones")
     if not args.no_app_a:
         log("timing the naive / grouped / fused GEMM pruning comparison")
         out["app_a_gemm_pruning"] = bench_app_a(torch, mg)
@@ -551,7 +594,8 @@ def main():
         log("timing decode step")
         out["decode"] = bench_decode(torch, wl, metrics, B=1)
         log(f"decode: {out['decode']['graph_ms_per_step'] * 1e3:.1f} us, "
-            f"{out['decode']['GB_per_s']:.0f} GB/s")
+            f"{out['decode']['GB_per_s']:.0f} GB/s, {out['decode']['speedup_vs_dense']:.2f}x all-ones "
+            f"({out['decode']['dense_GB_per_s']:.0f} GB/s)")
         out["decode_b4"] = bench_decode(torch, wl, metrics, B=4)
         log(f"decode B=4: {out['decode_b4']['graph_ms_per_step'] * 1e3:.1f} us, "
             f"{out['decode_b4']['GB_per_s']:.0f} GB/s")

@@ -30,7 +30,7 @@ class PrefillLayer:
     """One masked layer of shape `s` (workloads.LayerShape) on the GPU."""
 
     def __init__(self, s, host: dict, with_dense: bool = True, scheduled_mn: dict | None = None,
-                 ordered_k: tuple = ()):
+                 ordered_k: tuple = (), leftpad=None):
         self.s = s
         # GEMM-K ops that run over rows sorted by routing pattern (their tiles
         # skip the K-groups and 16-row fragments whose rows all skip a group).
@@ -62,8 +62,18 @@ class PrefillLayer:
         dev = self.x.device
         M, B, T = s.M, s.B, s.T
         i32 = torch.int32
+        # Attention reorders each sequence's routing columns (batch B, rows
+        # T); the GEMMs reorder the flattened tokens (batch 1, rows B*T). With
+        # B = 1 the two coincide and one reorder serves both.
         self.perm_a = torch.empty((B, s.Hk, T), dtype=i32, device=dev)
         self.cnt_a = torch.empty((B, s.Hk), dtype=i32, device=dev)
+        if B > 1:
+            self.perm_q = torch.empty((1, s.Hk, M), dtype=i32, device=dev)
+            self.cnt_q = torch.empty((1, s.Hk), dtype=i32, device=dev)
+        else:
+            self.perm_q, self.cnt_q = self.perm_a, self.cnt_a
+        # left padding of each sequence: keys before it are not attended
+        self.leftpad = None if leftpad is None else torch.tensor(list(leftpad), dtype=i32, device=dev)
         self.perm_f = torch.empty((1, s.NG_ffn, M), dtype=i32, device=dev)
         self.cnt_f = torch.empty((1, s.NG_ffn), dtype=i32, device=dev)
         self.order_a = torch.empty(M, dtype=i32, device=dev)
@@ -81,8 +91,6 @@ class PrefillLayer:
                   mg.gemm_mn_workspace_bytes(M, s.Hq * s.d, s.D, s.G_attn, False),
                   mg.gemm_mn_workspace_bytes(M, s.Dff, s.D, s.G_ffn, True))
         self.ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
-        if B != 1:
-            raise ValueError("the prefill layer driver flattens tokens with B = 1")
 
     def _mn_ws(self, op: str, which: str):
         return self.ws if op in self.scheduled_mn.get(which, ()) else None
@@ -94,18 +102,19 @@ class PrefillLayer:
         ma, mf = self.masks[which]
         if op == "reorder":
             mg.reorder(ma, self.perm_a, self.cnt_a)
+            if s.B > 1:
+                mg.reorder(ma.view(1, s.M, s.Hk), self.perm_q, self.cnt_q)
             mg.reorder(mf.view(1, s.M, s.NG_ffn), self.perm_f, self.cnt_f)
             if "o_proj" in self.ordered_k:
                 mg.order_by_pattern(ma.view(s.M, s.Hk), self.order_a)
             if "down_proj" in self.ordered_k:
                 mg.order_by_pattern(mf.view(s.M, s.NG_ffn), self.order_f)
         elif op == "q_proj":
-            # B = 1: the attention reorder is also the flattened reorder of the GEMMs.
-            mg.gemm_mn(self.x, self.wq, s.G_attn, perm=self.perm_a[0], counts=self.cnt_a[0],
+            mg.gemm_mn(self.x, self.wq, s.G_attn, perm=self.perm_q[0], counts=self.cnt_q[0],
                        out=self.q, workspace=self._mn_ws("q_proj", which))
         elif op == "attention":
             mg.attn(self.q.view(s.B, s.T, s.Hq, s.d), self.k, self.v, perm=self.perm_a,
-                    counts=self.cnt_a, out=self.o)
+                    counts=self.cnt_a, out=self.o, leftpad=self.leftpad)
         elif op == "o_proj":
             mg.gemm_k(self.o.view(s.M, s.Hq * s.d), self.wo, s.G_attn, ma.view(s.M, s.Hk),
                       out=self.y_attn, workspace=self.ws,

@@ -22,25 +22,30 @@ def gemm_k_flops(mask2d, N: int, G: int) -> int:
     return 2 * N * G * active_pairs(mask2d)
 
 
-def attention_flops(mask, Tk: int, Hq: int, d: int, causal: bool = True) -> int:
-    """QK^T and PV: 4*d FLOPs per valid key for every head of an active group."""
+def attention_flops(mask, Tk: int, Hq: int, d: int, causal: bool = True, leftpad=None) -> int:
+    """QK^T and PV: 4*d FLOPs per valid key for every head of an active group
+    (keys before a sequence's left padding are not valid)."""
     mask = np.asarray(mask) != 0
     B, Tq, Hk = mask.shape
     rep = Hq // Hk
     t = np.arange(Tq)
-    nkeys = np.minimum(t + (Tk - Tq) + 1, Tk) if causal else np.full(Tq, Tk)
-    per_t = mask.sum(axis=(0, 2))          # active groups per query position
-    return int(4 * d * rep * int(np.dot(per_t.astype(np.int64), nkeys.astype(np.int64))))
+    end = np.minimum(t + (Tk - Tq) + 1, Tk) if causal else np.full(Tq, Tk)
+    total = 0
+    for b in range(B):
+        start = int(leftpad[b]) if leftpad is not None else 0
+        nkeys = np.maximum(end - start, 0).astype(np.int64)
+        total += int(np.dot(mask[b].sum(axis=1).astype(np.int64), nkeys))
+    return int(4 * d * rep * total)
 
 
-def layer_flops(s, mask_attn, mask_ffn) -> dict:
+def layer_flops(s, mask_attn, mask_ffn, leftpad=None) -> dict:
     """Active FLOPs of each routed operator of one masked layer."""
     out = {}
     M = s.M
     if mask_attn is not None:
         ma = np.asarray(mask_attn).reshape(M, s.Hk)
         out["q_proj"] = gemm_mn_flops(ma, s.D, s.G_attn)
-        out["attention"] = attention_flops(mask_attn, s.Tkv, s.Hq, s.d)
+        out["attention"] = attention_flops(mask_attn, s.Tkv, s.Hq, s.d, leftpad=leftpad)
         out["o_proj"] = gemm_k_flops(ma, s.D, s.G_attn)
     if mask_ffn is not None:
         mf = np.asarray(mask_ffn).reshape(M, s.NG_ffn)

@@ -109,6 +109,46 @@ def test_prefill_layer_full_size(name, over):
     check_ffn(s, host, rows, bits_of(layer.h)[rows], layer.y_ffn.cpu().numpy()[rows].astype(np.float64))
 
 
+def test_prefill_layer_batched_leftpad():
+    """Two left-padded sequences of 4096 tokens through the layer driver
+    (Qwen3-14B shape, 50% of the groups off): per-sequence attention reorder,
+    flattened GEMM reorder, keys before each sequence's padding excluded
+    (Appendix B, Algorithm 4 with leftpad)."""
+    from masked_group_mask_amd.layer import PrefillLayer
+    s = wl.shape("qwen14b_prefill", B=2, T=4096)
+    leftpad = [0, 777]
+    say("batched left-padded prefill", s.B, s.T, leftpad)
+    host = wl.make_layer(s, seed=3)
+    layer = PrefillLayer(s, host, with_dense=False, leftpad=leftpad)
+    layer.step("masked")
+    torch.cuda.synchronize()
+    pa, ca = layer.perm_a.cpu().numpy(), layer.cnt_a.cpu().numpy()
+    for b in range(s.B):
+        check_reorder(host["mask_attn"][b], pa[b], ca[b])
+    check_reorder(host["mask_attn"].reshape(s.M, s.Hk), layer.perm_q.cpu().numpy()[0], layer.cnt_q.cpu().numpy()[0])
+    rows = np.array(sorted(set(sample_rows(s.M, 21).tolist()) | {s.T, s.T + 5, s.T + 776, s.T + 777}))
+    ma2 = host["mask_attn"].reshape(s.M, s.Hk)
+    mr = ma2[rows]
+    q_bits = bits_of(layer.q)
+    want_q = ref.gemm_mn(host["x"][rows], host["w_q"], mr, s.G_attn)
+    keep = ref.expand(mr, s.G_attn)
+    check_bf16_store(q_bits[rows][keep], want_q[keep], "batched q_proj")
+    q_in = active_only(q_bits, ref.expand(ma2, s.G_attn))
+    queries = [(int(r) // s.T, int(r) % s.T) for r in rows]
+    want_o = ref.attention(q_in.reshape(s.B, s.T, s.Hq, s.d), host["k"], host["v"], host["mask_attn"],
+                           leftpad=leftpad, queries=queries)
+    o_bits = bits_of(layer.o).reshape(s.M, s.Hq, s.d)[rows]
+    keep_h = np.repeat(mr != 0, s.Hq // s.Hk, axis=1)
+    check_attn_bf16(o_bits[keep_h], want_o[keep_h], "batched left-padded attention")
+    # padded queries of sequence 1 see no key: exact zeros where active
+    pad = np.array([r // s.T == 1 and r % s.T < leftpad[1] for r in rows])
+    assert (o_bits[pad][keep_h[pad]] == 0).all()
+    o_in = active_only(o_bits, keep_h[..., None]).reshape(len(rows), -1)
+    check_gemm(layer.y_attn.cpu().numpy()[rows].astype(np.float64), ref.gemm_k(o_in, host["w_o"], mr, s.G_attn),
+               "batched o_proj")
+    check_ffn(s, host, rows, bits_of(layer.h)[rows], layer.y_ffn.cpu().numpy()[rows].astype(np.float64))
+
+
 def test_llama3b_ffn_full_size():
     """Llama3.2-3B-shaped FFN, T=4096, per-group Beta(2,2) activation rates."""
     import masked_group_mask_amd as mg

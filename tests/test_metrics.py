@@ -43,3 +43,10 @@ def test_decode_bytes_batched_match_oracle():
     assert got == ref.decode_bytes(ma.reshape(4, s.Hk), mf.reshape(4, s.NG_ffn), s.D, s.Hq, s.Hk, s.d,
                                    s.G_ffn, s.Tk)
     assert int(ma.sum()) == 4 * s.Hk // 2     # "half" rule: every token keeps exactly half
+
+
+def test_attention_flops_with_leftpad_match_oracle():
+    m = wl.random_mask(4, (3, 11, 2), 0.6)
+    for lp in ([0, 4, 11], [2, 0, 7]):
+        assert metrics.attention_flops(m, 11, 6, 16, leftpad=lp) == ref.flops_attention(m, 11, 6, 16, leftpad=lp)
+        assert metrics.attention_flops(m, 15, 6, 16, leftpad=lp) == ref.flops_attention(m, 15, 6, 16, leftpad=lp)
