@@ -101,8 +101,11 @@ int wide_reorder(const uint8_t *mask, int64_t batch, int64_t rows, int64_t group
  * zero-initialised C).
  * Requirements: K % 8 == 0; lda, ldb >= K and multiples of 8; ldc >= N;
  * A, B, C 16-byte aligned; C must not overlap A or B. WIDE_ERR_UNSUPPORTED
- * unless G % 64 == 0, M * lda * 2 < 2^31 (rows are gathered with 32-bit byte
- * offsets) and ldb < 2^22.
+ * unless G % 16 == 0, M * lda * 2 < 2^31 (rows are gathered with 32-bit byte
+ * offsets) and ldb < 2^22. A group narrower than the output tile (G < 64, or
+ * a group size that is not a multiple of the tile width) is covered by tiles
+ * of its own whose columns past the group are computed but not stored: still
+ * exact, at G / 64 of the tile's MFMA work for G < 64.
  */
 int wide_gemm_mn(const wide_bf16 *A, int64_t lda, const wide_bf16 *B, int64_t ldb,
                  void *C, int64_t ldc, int c_dtype, int64_t M, int64_t N, int64_t K,
@@ -214,8 +217,10 @@ int wide_order_by_pattern(const uint8_t *mask, int64_t rows, int64_t groups, int
  * results are bitwise reproducible run to run.
  * Requirements: K % G == 0; lda, ldb >= K and multiples of 8; ldc >= N and a
  * multiple of 4; 16-byte aligned A, B, C; C must not overlap A, B, mask or
- * order. WIDE_ERR_UNSUPPORTED unless G % 64 == 0, K / G <= 512,
- * N % 128 == 0, lda < 2^22 and ldb < 2^22.
+ * order. WIDE_ERR_UNSUPPORTED unless G % 16 == 0, K / G <= 512,
+ * N % 128 == 0, lda < 2^22 and ldb < 2^22. When G is not a multiple of 64 a
+ * 64-deep stage spans several groups and each 16-byte chunk of an A row is
+ * predicated by its own (row, group) bit; the order is then ignored.
  */
 int wide_gemm_k(const wide_bf16 *A, int64_t lda, const wide_bf16 *B, int64_t ldb,
                 float *C, int64_t ldc, int beta, int64_t M, int64_t N, int64_t K,

@@ -60,7 +60,7 @@ int check_mn(const wide_bf16 *A, int64_t lda, const wide_bf16 *B0, const wide_bf
   if (overlap(C, cb, A, span_bytes(M, K, lda, 2)) || overlap(C, cb, B0, span_bytes(N, K, ldb, 2)) ||
       (B1 && overlap(C, cb, B1, span_bytes(N, K, ldb, 2))))
     return WIDE_ERR_INVALID_ARG;
-  if (G % 64 != 0) return WIDE_ERR_UNSUPPORTED;
+  if (G % 16 != 0) return WIDE_ERR_UNSUPPORTED;
   // Gathered rows are addressed with 32-bit byte offsets into A, a tile's
   // (at most 256) weight rows with 32-bit offsets into B.
   if ((uint64_t)M * (uint64_t)lda * 2u > 0x7fffffffull || (uint64_t)ldb * 512u > 0x7fffffffull)
@@ -217,7 +217,7 @@ int wide_gemm_k_ws(const wide_bf16 *A, int64_t lda, const wide_bf16 *B, int64_t 
   if (overlap(C, cb, A, span_bytes(M, K, lda, 2)) || overlap(C, cb, B, span_bytes(N, K, ldb, 2)) ||
       overlap(C, cb, mask, (size_t)M * (K / G)) || (order && overlap(C, cb, order, (size_t)M * 4)))
     return WIDE_ERR_INVALID_ARG;
-  if (G % 64 != 0 || K / G > 512 || N % 128 != 0) return WIDE_ERR_UNSUPPORTED;
+  if (G % 16 != 0 || K / G > 512 || N % 128 != 0) return WIDE_ERR_UNSUPPORTED;
   // A tile of 256 rows and a B tile of 128 rows are addressed with 32-bit byte offsets.
   if ((uint64_t)lda * 512u > 0x7fffffffull || (uint64_t)ldb * 512u > 0x7fffffffull)
     return WIDE_ERR_UNSUPPORTED;

@@ -105,34 +105,50 @@ __device__ __forceinline__ bool build_bits(const KArgs &a, int m, WIDE_LDS uint3
 // dense. The bit words of a stage's group are read from LDS a step before the
 // stage is issued, among the fragment reads, and unpacked only when it is, so
 // the LDS latency never sits in front of the loads.
-template <class S>
+// SMALLG: groups narrower than a 64-deep stage (G = 16 or 32): a stage then
+// spans 64 / G groups and each lane's 16-byte chunk of a row (8 reduction
+// elements) lies in one of them, so the predicate is taken per lane from the
+// bit of (row, group of its chunk), read from the table when the stage is
+// issued.
+template <class S, bool SMALLG>
 struct KLoader {
-  static constexpr int kDsReads = 2;
+  static constexpr int kDsReads = SMALLG ? 0 : 2;
   static constexpr int kLoadGap = 0;
   static constexpr int AHEAD = S::STAGES - 1;  // stages in flight ahead of the one multiplied
   rsrc_t ar, br, none;
   uint32_t aoff[S::AI], boff[S::BI];
   const WIDE_LDS uint32_t *bits;
-  int nk, kb, steps_per_group, NG, wave, lane;  // steps kb .. kb + nk - 1 of K
+  int nk, kb, steps_per_group, NG, G, wave, lane;  // steps kb .. kb + nk - 1 of K
   u32x4 wlo, whi;  // bit words (rows 0..127, 128..255) of the group of the next stage
 
   __device__ __forceinline__ void fetch(int t) {
+    if (SMALLG) return;
     const int g = min((t + kb) / steps_per_group, NG - 1);
     wlo = *(const WIDE_LDS u32x4 *)(bits + g * 8);
     whi = *(const WIDE_LDS u32x4 *)(bits + g * 8 + 4);
   }
 
   __device__ __forceinline__ void operator()(int t, eng::lds_u16 *sa, eng::lds_u16 *sb) {
-    // Load instruction i covers tile row 8 (wave + W i) + lane / 8: word
-    // (W / 4) i + wave / 4 of the table, bit (8 wave + lane / 8) % 32.
-    const int sh = (wave * 8 + lane / 8) % 32;
-    const bool hiw = S::WAVES == 8 && wave >= 4;
     uint32_t p = 0;
+    if (SMALLG) {
 #pragma unroll
-    for (int i = 0; i < S::AI; ++i) {
-      const int w = (S::WAVES / 4) * i;  // word index for waves 0..3
-      const uint32_t x = w < 4 ? (hiw ? wlo[(w + 1) % 4] : wlo[w % 4]) : (hiw ? whi[(w + 1) % 4] : whi[w % 4]);
-      p |= ((x >> sh) & 1u) << i;
+      for (int i = 0; i < S::AI; ++i) {
+        const int r = eng::load_row<S::WAVES>(wave, i, lane);
+        const int c = (lane % 8) ^ eng::swz(r);  // chunk of the row this lane loads
+        const int g = min(((t + kb) * eng::kBK + 8 * c) / G, NG - 1);
+        p |= ((bits[g * 8 + (r >> 5)] >> (r & 31)) & 1u) << i;
+      }
+    } else {
+      // Load instruction i covers tile row 8 (wave + W i) + lane / 8: word
+      // (W / 4) i + wave / 4 of the table, bit (8 wave + lane / 8) % 32.
+      const int sh = (wave * 8 + lane / 8) % 32;
+      const bool hiw = S::WAVES == 8 && wave >= 4;
+#pragma unroll
+      for (int i = 0; i < S::AI; ++i) {
+        const int w = (S::WAVES / 4) * i;  // word index for waves 0..3
+        const uint32_t x = w < 4 ? (hiw ? wlo[(w + 1) % 4] : wlo[w % 4]) : (hiw ? whi[(w + 1) % 4] : whi[w % 4]);
+        p |= ((x >> sh) & 1u) << i;
+      }
     }
     const bool live = t < nk;
     const rsrc_t ra = live ? ar : none, rb = live ? br : none;
@@ -148,7 +164,7 @@ struct KLoader {
   __device__ __forceinline__ void prefetch(int t) { fetch(t + AHEAD + 1); }
 };
 
-template <int BN, int W>
+template <int BN, int W, bool SMALLG>
 __global__ __launch_bounds__(64 * W) void gemm_k_kernel(KArgs a) {
   using S = eng::Shape<BN, W>;
   constexpr int A3 = S::STAGES == 3 ? S::A_ELEMS : 8, B3 = S::STAGES == 3 ? S::B_ELEMS : 8;
@@ -191,7 +207,7 @@ __global__ __launch_bounds__(64 * W) void gemm_k_kernel(KArgs a) {
     for (int j = 0; j < S::FM; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   if (any) {  // level 0: otherwise the tile's product is exactly zero
-    KLoader<S> ld;
+    KLoader<S, SMALLG> ld;
     const int rows = min(eng::kBM, a.M - m0);
     ld.ar = make_rsrc(a.A + (size_t)m0 * a.lda, (uint64_t)rows * a.lda * 2);  // rows past M: out of range
     ld.br = make_rsrc(a.B + (size_t)n0 * a.ldb, (uint64_t)BN * a.ldb * 2);
@@ -210,8 +226,9 @@ __global__ __launch_bounds__(64 * W) void gemm_k_kernel(KArgs a) {
     const int nk_all = a.K / eng::kBK;
     ld.kb = part * nk_all / nparts;
     ld.nk = (part + 1) * nk_all / nparts - ld.kb;
-    ld.steps_per_group = a.G / eng::kBK;
+    ld.steps_per_group = max(1, a.G / eng::kBK);
     ld.NG = a.K / a.G;
+    ld.G = a.G;
     ld.wave = wave;
     ld.lane = lane;
     ld.fetch(0);
@@ -701,6 +718,14 @@ size_t plan_bytes(const KSplitPlan &p) {
 
 size_t gemm_k_workspace_bytes(int M, int N, int K) { return plan_bytes(ksplit_plan(M, N, K)); }
 
+template <int BN, int W>
+static void launch_k_tiles(const KArgs &a, dim3 grid, hipStream_t s) {
+  if (a.G % eng::kBK == 0)
+    hipLaunchKernelGGL((gemm_k_kernel<BN, W, false>), grid, dim3(64 * W), 0, s, a);
+  else
+    hipLaunchKernelGGL((gemm_k_kernel<BN, W, true>), grid, dim3(64 * W), 0, s, a);
+}
+
 // Tiled launches. With N a multiple of 256 the 8-wave 256 x 256 kernel runs.
 // When its tiles leave a last round at most half full (640 tiles on 256 CUs
 // run as 3 rounds, 2.5 of work) and the caller gave the workspace, each
@@ -726,7 +751,7 @@ int launch_gemm_k(const KArgs &a0, hipStream_t s) {
       case 3: hipLaunchKernelGGL(gemv_k_kernel<3>, grid, block, 0, s, a); break;
       default: hipLaunchKernelGGL(gemv_k_kernel<4>, grid, block, 0, s, a); break;
     }
-  } else if (a.N % 256 == 0 && a.order != nullptr) {
+  } else if (a.N % 256 == 0 && a.order != nullptr && a.G % eng::kBK == 0) {
     // rows through the order; the leftover round split along K with a workspace
     const KSplitPlan p = ksplit_plan(a.M, a.N, a.K);
     if (p.ksplit > 1 && a.ws != nullptr && a.ws_bytes >= plan_bytes(p)) {
@@ -745,22 +770,22 @@ int launch_gemm_k(const KArgs &a0, hipStream_t s) {
       const int tail = p.tiles - p.head;
       a.head = p.head;
       a.ksplit = p.ksplit;
-      hipLaunchKernelGGL((gemm_k_kernel<256, 8>), dim3(p.head + tail * p.ksplit), dim3(512), 0, s, a);
+      launch_k_tiles<256, 8>(a, dim3(p.head + tail * p.ksplit), s);
       hipLaunchKernelGGL(gemm_k_fixup_kernel, dim3(tail * (eng::kBM * 64 / 256)), dim3(256), 0, s, a);
     } else {
       const int tiles = mt * (a.N / 256), cus = cu_count();
       const int tail = tiles % cus;
       const int head = tiles > cus && tail > 0 && 2 * tail <= cus ? tiles - tail : tiles;
-      hipLaunchKernelGGL((gemm_k_kernel<256, 8>), dim3(head), dim3(512), 0, s, a);
+      launch_k_tiles<256, 8>(a, dim3(head), s);
       if (head < tiles) {
         a.tile_base = head;
         a.split_tail = 1;
-        hipLaunchKernelGGL((gemm_k_kernel<128, 4>), dim3(2 * (tiles - head)), dim3(256), 0, s, a);
+        launch_k_tiles<128, 4>(a, dim3(2 * (tiles - head)), s);
       }
     }
   } else {
     a.order = nullptr;
-    hipLaunchKernelGGL((gemm_k_kernel<128, 4>), dim3(mt * (a.N / 128)), dim3(256), 0, s, a);
+    launch_k_tiles<128, 4>(a, dim3(mt * (a.N / 128)), s);
   }
   return check_launch();
 }

@@ -94,7 +94,7 @@ struct MnLoader {
 //
 // The active tiles are known only on the device (counts are never read on the
 // host), so every workgroup derives the same schedule from counts: group g
-// has ceil(counts[g] / 256) row tiles times G / BN_OUT column tiles, numbered
+// has ceil(counts[g] / 256) row tiles times ceil(G / BN_OUT) column tiles, numbered
 // group by group (row tile major, column tile minor, so the column tiles of
 // one row tile, which gather the same rows, are neighbours). With A active
 // tiles on C compute units (one tile workgroup per CU), the A mod C tiles of
@@ -203,7 +203,7 @@ __global__ __launch_bounds__(64 * W) void gemm_mn_kernel(MnArgs a) {
   int part = 0, nparts = 1, slot = 0;  // K slice of this workgroup; slot: split tile index
   if constexpr (SCHED) {
     __shared__ int sTmp[W + 2];
-    const int ntg = a.G / BN_OUT;
+    const int ntg = (a.G + BN_OUT - 1) / BN_OUT;
     int first, mine;
     const MnPlan p = mn_plan<S::THREADS>(a, ntg, nk_all, sTmp, first, mine);
     int *hdr = static_cast<int *>(a.ws);
@@ -227,12 +227,17 @@ __global__ __launch_bounds__(64 * W) void gemm_mn_kernel(MnArgs a) {
     if (nparts > 1 && part == 0 && threadIdx.x == 0)
       reinterpret_cast<int4 *>(hdr)[1 + slot] = int4{g, mt * eng::kBM, n0, a.counts[g]};
   } else {
-    const int MT = (a.M + eng::kBM - 1) / eng::kBM, NT = a.N / BN_OUT;
+    // column tiles: ntg per group (a group narrower than a tile gets one)
+    const int ntg = (a.G + BN_OUT - 1) / BN_OUT;
+    const int MT = (a.M + eng::kBM - 1) / eng::kBM, NT = (a.N / a.G) * ntg;
     int tn;
     eng::tile_of<8>(blockIdx.x, MT, NT, mt, tn);  // 8 m-tiles per raster group
-    n0 = tn * BN_OUT;
-    g = n0 / a.G;
+    g = tn / ntg;
+    n0 = g * a.G + (tn % ntg) * BN_OUT;
   }
+  // outputs of this tile that belong to its group (fewer than BN_OUT when
+  // the group is narrower than the tile, or in a group's last column tile)
+  const int ncols = min(BN_OUT, (g + 1) * a.G - n0);
   const int cnt = a.counts[g];
   const int s0 = mt * eng::kBM;
   if (s0 >= cnt) return;  // level 0 (never taken by a scheduled tile)
@@ -244,8 +249,10 @@ __global__ __launch_bounds__(64 * W) void gemm_mn_kernel(MnArgs a) {
   MnLoader<S, SWIGLU> ld;
   ld.ar = make_rsrc(a.A, (uint64_t)a.M * a.lda * 2);
   const int brows = SWIGLU ? BN / 2 : BN;
-  ld.br0 = make_rsrc(a.B0 + (size_t)n0 * a.ldb, (uint64_t)brows * a.ldb * 2);
-  ld.br1 = make_rsrc((SWIGLU ? a.B1 : a.B0) + (size_t)n0 * a.ldb, (uint64_t)brows * a.ldb * 2);
+  // weight rows past N (a narrow last group) read as zeros
+  const uint64_t brange = (uint64_t)min(brows, a.N - n0) * a.ldb * 2;
+  ld.br0 = make_rsrc(a.B0 + (size_t)n0 * a.ldb, brange);
+  ld.br1 = make_rsrc((SWIGLU ? a.B1 : a.B0) + (size_t)n0 * a.ldb, brange);
   ld.none = make_rsrc(a.A, 0);
 #pragma unroll
   for (int i = 0; i < S::AI; ++i) {
@@ -299,14 +306,19 @@ __global__ __launch_bounds__(64 * W) void gemm_mn_kernel(MnArgs a) {
     if (SWIGLU) {
 #pragma unroll
       for (int i = 0; i < S::FN / 2; ++i) {
+        const int col = wn * (S::TN / 2) + i * 16 + 4 * (lane / 16);
+        if (col >= ncols) continue;
         const f32x4 gt = acc[i][j], up = acc[i + S::FN / 2][j];
         const f32x4 h = {silu(gt[0]) * up[0], silu(gt[1]) * up[1], silu(gt[2]) * up[2], silu(gt[3]) * up[3]};
-        store_out4<OUT_F32>(a.C, rowoff + n0 + wn * (S::TN / 2) + i * 16 + 4 * (lane / 16), h, vec);
+        store_out4<OUT_F32>(a.C, rowoff + n0 + col, h, vec);
       }
     } else {
 #pragma unroll
-      for (int i = 0; i < S::FN; ++i)
-        store_out4<OUT_F32>(a.C, rowoff + n0 + wn * S::TN + i * 16 + 4 * (lane / 16), acc[i][j], vec);
+      for (int i = 0; i < S::FN; ++i) {
+        const int col = wn * S::TN + i * 16 + 4 * (lane / 16);
+        if (col >= ncols) continue;
+        store_out4<OUT_F32>(a.C, rowoff + n0 + col, acc[i][j], vec);
+      }
     }
   }
 }
@@ -327,12 +339,13 @@ __global__ __launch_bounds__(256) void gemm_mn_fixup_kernel(MnArgs a) {
   if (slot >= L) return;
   const int4 info = reinterpret_cast<const int4 *>(hdr)[1 + slot];
   const int g = info.x, s0 = info.y, n0 = info.z, cnt = info.w;
+  const int ncols = min(BN_OUT, (g + 1) * a.G - n0);
   const float *base = reinterpret_cast<const float *>(static_cast<const char *>(a.ws) + kMnHdrBytes) +
                       (size_t)slot * S * TILE;
   const bool vec = a.ldc % 4 == 0 && reinterpret_cast<uintptr_t>(a.C) % 16 == 0;
   for (int e = threadIdx.x; e < kFixRows * Q; e += 256) {
     const int r = rb * kFixRows + e / Q, q = e % Q;
-    if (s0 + r >= cnt) continue;
+    if (s0 + r >= cnt || 4 * q >= ncols) continue;
     const int phys = a.perm[(size_t)g * a.M + s0 + r];
     const float *src = base + (size_t)r * BN + 4 * q;
     f32x4 pv[kMaxSlices], pu[kMaxSlices];
@@ -437,7 +450,8 @@ __global__ __launch_bounds__(256) void gemv_mn_kernel(MnArgs a) {
 template <int BN, int W, bool SWIGLU, bool F32>
 static void launch_tiled(const MnArgs &a, hipStream_t s) {
   constexpr int BN_OUT = SWIGLU ? BN / 2 : BN;
-  const int tiles = (a.N / BN_OUT) * ((a.M + eng::kBM - 1) / eng::kBM);
+  const int ntg = (a.G + BN_OUT - 1) / BN_OUT;
+  const int tiles = (a.N / a.G) * ntg * ((a.M + eng::kBM - 1) / eng::kBM);
   if (a.ws != nullptr) {
     // every schedule has at most tiles - L + C <= tiles + C work items, and
     // at most C / 2 split tiles

@@ -81,7 +81,8 @@ def test_gemm_mn_validation(lib):
     assert mn(lib, perm=None, mask=P(5), M=5) == INVALID          # mask path needs M <= 4
     assert mn(lib, counts=None) == INVALID
     assert mn(lib, C=P(0)) == INVALID                             # C aliases A
-    assert mn(lib, G=32, N=256) == UNSUPPORTED
+    assert mn(lib, G=8, N=256) == UNSUPPORTED        # groups narrower than 16
+    assert mn(lib, G=24, N=264, ldc=264) == UNSUPPORTED
 
 
 def test_gemm_mn_swiglu_validation(lib):
@@ -183,7 +184,10 @@ def test_gemm_k_validation(lib):
     assert gk(lib, beta=2) == INVALID
     assert gk(lib, ldc=130) == INVALID                      # ldc % 4
     assert gk(lib, C=P(1)) == INVALID                       # C aliases B
-    assert gk(lib, G=32, K=256) == UNSUPPORTED
+    assert gk(lib, G=8, K=256) == UNSUPPORTED
+    far = {k: ctypes.c_void_p((i + 1) << 40) for i, k in enumerate(("A", "B", "C", "mask"))}
+    K513 = 16 * 513                                         # more than 512 groups
+    assert gk(lib, G=16, K=K513, lda=K513, ldb=K513, **far) == UNSUPPORTED
     assert gk(lib, N=64, ldc=64) == UNSUPPORTED
     assert gk(lib, order=P(2)) == INVALID                   # C overlaps the order
 
