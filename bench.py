@@ -155,6 +155,66 @@ def bench_decode(torch, wl, metrics, B=1, steps=50, sets=3):
     }
 
 
+def bench_decode_groups(torch, wl, steps=50, sets=3, group_counts=(8, 16, 32)):
+    """Decode of the attention sub-layer (q_proj, attention, o_proj) of the
+    Llama3.1-8B shape (KV 16384) with routing groups of G_attn = (Hq / NG) d:
+    NG = 8 (one group per KV head), 16 and 32 (one query head per group),
+    half of the groups on, against the same kernels with every group on (the
+    page's decode sweep over the attention group size, Appendix C, Fig. 13).
+    A replayed HIP graph of the three ops, 3 rotated weight/KV sets."""
+    import masked_group_mask_amd as mg
+    s = wl.shape("llama8b_decode")
+    host = wl.make_layer(s, seed=11, parts=("attn",))
+    rng = np.random.default_rng(13)
+    dev = "cuda"
+    to = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)  # noqa: E731
+    base = {k: to(host[k]) for k in ("w_q", "w_o", "k", "v")}
+    wsets = [base] + [{k: t.clone() for k, t in base.items()} for _ in range(sets - 1)]
+    x = to(host["x"])
+    q = torch.empty((1, s.Hq * s.d), dtype=torch.bfloat16, device=dev)
+    o = torch.empty((1, 1, s.Hq, s.d), dtype=torch.bfloat16, device=dev)
+    y = torch.empty((1, s.D), dtype=torch.float32, device=dev)
+    ws = torch.empty(mg.attn_workspace_bytes(1, 1, s.Tkv, s.Hq, s.Hk, s.d), dtype=torch.uint8, device=dev)
+    rows = []
+    for NG in group_counts:
+        G = s.Hq * s.d // NG
+        half = np.zeros((1, 1, NG), np.uint8)
+        half[0, 0, rng.permutation(NG)[: NG // 2]] = 1
+        res = {}
+        for name, m in (("masked", half), ("all_ones", np.ones_like(half))):
+            md = torch.from_numpy(m).to(dev)
+
+            def step(w, md=md):
+                mg.gemm_mn(x, w["w_q"], G, mask=md.view(1, NG), out=q)
+                mg.attn(q.view(1, 1, s.Hq, s.d), w["k"], w["v"], mask=md, out=o, workspace=ws, groups=NG)
+                mg.gemm_k(o.view(1, -1), w["w_o"], G, md.view(1, NG), out=y)
+            for i in range(3):
+                step(wsets[i % sets])
+            graphs = []
+            for k in range(sets):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    step(wsets[k])
+                graphs.append(g)
+            for k in range(2 * sets):
+                graphs[k % sets].replay()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            hold_gpu(torch, 5.0)
+            e0.record()
+            for i in range(steps):
+                graphs[i % sets].replay()
+            e1.record()
+            torch.cuda.synchronize()
+            res[name] = e0.elapsed_time(e1) / steps
+        rows.append({"groups": NG, "G_attn": G, "masked_us": res["masked"] * 1e3,
+                     "all_ones_us": res["all_ones"] * 1e3, "speedup": res["all_ones"] / res["masked"]})
+        log(f"decode attention sub-layer NG={NG} (G_attn={G}): {res['masked'] * 1e3:.1f} us masked, "
+            f"{res['all_ones'] * 1e3:.1f} us all-ones, {res['all_ones'] / res['masked']:.2f}x")
+    return {"workload": "llama8b_decode attention sub-layer (q_proj, attention, o_proj), KV 16384, "
+                        "half of the routing groups on", "rows": rows}
+
+
 def bench_router(torch, wl, s, steps=50, rank=32):
     """The two routers of the bench layer (attention: Hk groups, FFN: NG_ffn
     groups; rank 32, seeded weights) on the same X, each followed by its
@@ -392,6 +452,42 @@ def bench_batched_leftpad(torch, wl, metrics, steps=5, warmup=5, T=4096, leftpad
             "speedup_vs_dense": dense_ms / ms, "per_op_ms": per_op}
 
 
+def measured_peaks(torch, mg, copy_bytes=1 << 30, reps=10):
+    """Rates this device sustains, beside the vendor figures: the bf16 MFMA
+    rate of the library's probe kernel (independent MFMA chains from
+    registers, 8 workgroups of 4 waves per compute unit) and a plain device
+    copy (read + write of copy_bytes)."""
+    props = torch.cuda.get_device_properties(0)
+    blocks, iters = 8 * props.multi_processor_count, 4096
+    sink = torch.empty(blocks * 4, dtype=torch.float32, device="cuda")
+    mg.mfma_probe(blocks, 64, sink)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        mg.mfma_probe(blocks, iters, sink)
+    e1.record()
+    torch.cuda.synchronize()
+    mfma = blocks * 4 * iters * 8 * 16384 / (e0.elapsed_time(e1) / reps * 1e-3) / 1e12
+    n = copy_bytes // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        torch.mul(src, 1.0, out=dst)
+    e1.record()
+    torch.cuda.synchronize()
+    copy = 2 * n * 4 / (e0.elapsed_time(e1) / reps * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"mfma_bf16_tflops": mfma, "copy_read_write_GB_per_s": copy,
+            "how": ("MFMA: wide_mfma_probe, %d workgroups x 4 waves x %d rounds of 8 independent "
+                    "16x16x32 bf16 MFMAs; copy: torch elementwise copy of %d MiB, read + write"
+                    % (blocks, iters, copy_bytes >> 20))}
+
+
 def measured_traffic(op: str):
     """Bytes per launch of `op` from profiles/traffic.json (two rocprofv3
     counter passes, scaled by the same counters on a copy of known size), or
@@ -419,12 +515,14 @@ def cpu_baseline(s, host, rows: int):
     """The CPU oracle on `rows` token rows of the same layer (all routed ops)."""
     from oracle import wide_ref as ref
     from masked_group_mask_amd import metrics
+    # the oracle's BLAS runs on every core this process may use, and that is
+    # the core count reported
+    cores = len(os.sched_getaffinity(0))
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()
-                       if i.get("user_api") == "blas"] or [1])
+        from threadpoolctl import threadpool_limits
+        limiter = threadpool_limits(limits=cores, user_api="blas")
     except Exception:  # pragma: no cover - threadpoolctl missing
-        threads = os.cpu_count() or 1
+        limiter = None
     rng = np.random.default_rng(123)
     sel = np.sort(rng.choice(s.M, size=min(rows, s.M), replace=False))
     ma = host["mask_attn"].reshape(s.M, s.Hk)[sel]
@@ -442,6 +540,8 @@ def cpu_baseline(s, host, rows: int):
                                    ref.gemm_mn(X, host["w_up"], mf, s.G_ffn)))
     ref.gemm_k(ref.to_bf16_bits(hh), host["w_down"], mf, s.G_ffn)
     dt = time.perf_counter() - t0
+    if limiter is not None:
+        limiter.unregister()
     # active FLOPs of exactly the sampled rows
     fl = (metrics.gemm_mn_flops(ma, s.D, s.G_attn) + metrics.gemm_k_flops(ma, s.D, s.G_attn)
           + 2 * metrics.gemm_mn_flops(mf, s.D, s.G_ffn) + metrics.gemm_k_flops(mf, s.D, s.G_ffn))
@@ -453,7 +553,7 @@ def cpu_baseline(s, host, rows: int):
             cpu = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), cpu)
     except OSError:
         pass
-    return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+    return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
             "cpu": cpu, "blas": np.show_config(mode="dicts").get("Build Dependencies", {}).get("blas", {}).get("name", "?"),
             "sample": f"{len(sel)} of {s.M} token rows of the same layer (all routed ops, float64), {dt:.1f} s",
             "seconds": dt}
@@ -575,6 +675,11 @@ def main():
         "dense_per_op_ms": dense_per_op,
         "roofline": roof,
     }
+    out["measured_peaks"] = measured_peaks(torch, mg)
+    log(f"measured peaks: MFMA bf16 {out['measured_peaks']['mfma_bf16_tflops']:.0f} TFLOP/s, "
+        f"copy {out['measured_peaks']['copy_read_write_GB_per_s']:.0f} GB/s")
+    out["roofline"]["measured_peak"] = out["measured_peaks"]["mfma_bf16_tflops"]
+    out["roofline"]["frac_of_measured_peak"] = achieved / out["measured_peaks"]["mfma_bf16_tflops"]
     if not args.no_dense and not args.no_torch_dense and s.Hq:
         out["torch_dense"] = bench_torch_dense(torch, s, out["dense_per_op_ms"])
         log("torch dense GEMMs (ms): " + ", ".join(f"{k} {v:.3f}" for k, v in out["torch_dense"]["per_op_ms"].items()))
@@ -596,6 +701,7 @@ def main():
         log(f"decode: {out['decode']['graph_ms_per_step'] * 1e3:.1f} us, "
             f"{out['decode']['GB_per_s']:.0f} GB/s, {out['decode']['speedup_vs_dense']:.2f}x all-ones "
             f"({out['decode']['dense_GB_per_s']:.0f} GB/s)")
+        out["decode_groups"] = bench_decode_groups(torch, wl)
         out["decode_b4"] = bench_decode(torch, wl, metrics, B=4)
         log(f"decode B=4: {out['decode_b4']['graph_ms_per_step'] * 1e3:.1f} us, "
             f"{out['decode_b4']['GB_per_s']:.0f} GB/s")

@@ -354,6 +354,17 @@ int wide_attn_noalloc(const wide_bf16 *Q, const wide_bf16 *K, const wide_bf16 *V
 size_t wide_attn_workspace_bytes(int64_t B, int64_t Tq, int64_t Tk, int64_t Hq,
                                  int64_t Hk, int64_t d);
 
+/*
+ * wide_mfma_probe -- a measurement, not part of the routed layer: `blocks`
+ * workgroups of 4 waves each run `iters` rounds of 8 independent bf16 MFMAs
+ * (16 x 16 x 32, 16384 FLOPs each) from register operands, so the elapsed
+ * time gives the matrix-core rate the device sustains:
+ * blocks * 4 * iters * 8 * 16384 FLOPs. sink: device float [blocks * 4],
+ * written (one value per wave). Errors: WIDE_ERR_INVALID_ARG for a null sink,
+ * blocks outside [1, 65535] or iters outside [1, 2^24].
+ */
+int wide_mfma_probe(int64_t blocks, int64_t iters, float *sink, wide_stream_t stream);
+
 /* Static, human-readable text for a wide_status value. */
 const char *wide_status_string(int status);
 

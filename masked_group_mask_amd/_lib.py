@@ -50,6 +50,7 @@ _SIGS = {
     "wide_attn_noalloc": [_ptr, _ptr, _ptr, _ptr, _int, _i64, _i64, _i64, _i64, _i64, _i64, _int, _f32,
                           _ptr, _ptr, _ptr, _ptr, _ptr],
     "wide_attn_workspace_bytes": [_i64] * 6,
+    "wide_mfma_probe": [_i64, _i64, _ptr, _ptr],
     "wide_status_string": [_int],
     "wide_abi_version": [],
 }
@@ -411,3 +412,13 @@ def attn(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, perm: Optional[torch
               int(groups), d, int(bool(causal)), float(scale), _p(leftpad), _p(perm), _p(counts),
               _p(mask), _p(workspace), ws_bytes, _stream())
     return out
+
+
+def mfma_probe(blocks: int, iters: int, sink: torch.Tensor) -> None:
+    """Launch the MFMA rate probe (blocks * 4 * iters * 8 * 16384 bf16 FLOPs);
+    sink is a device float tensor of at least blocks * 4 elements."""
+    _need(sink, "sink", torch.float32)
+    if sink.numel() < blocks * 4 or not sink.is_contiguous():
+        raise ValueError("sink needs blocks * 4 contiguous floats")
+    _on_device(sink)
+    _call("wide_mfma_probe", blocks, iters, _p(sink), _stream())

@@ -271,6 +271,12 @@ int wide_router(const wide_bf16 *X, int64_t ldx, const wide_bf16 *W1, const wide
   return wide::launch_router(a, reinterpret_cast<hipStream_t>(stream));
 }
 
+int wide_mfma_probe(int64_t blocks, int64_t iters, float *sink, wide_stream_t stream) {
+  if (!sink || blocks < 1 || iters < 1 || blocks > 65535 || iters > (1 << 24)) return WIDE_ERR_INVALID_ARG;
+  if (!device_ok()) return WIDE_ERR_NO_DEVICE;
+  return wide::launch_mfma_probe((int)blocks, (int)iters, sink, reinterpret_cast<hipStream_t>(stream));
+}
+
 size_t wide_attn_workspace_bytes(int64_t B, int64_t Tq, int64_t Tk, int64_t Hq, int64_t Hk,
                                  int64_t d) {
   if (B < 1 || Tq < 1 || Tk < 1 || Hq < 1 || Hk < 1 || d < 1) return 0;

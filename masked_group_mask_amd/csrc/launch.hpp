@@ -125,4 +125,8 @@ int launch_router(const RouterArgs &a, hipStream_t stream);
 size_t attn_workspace_bytes(int64_t B, int64_t Tq, int64_t Tk, int64_t Hq, int64_t Hk,
                             int64_t d);
 
+// MFMA rate probe: `blocks` workgroups of 4 waves, `iters` rounds of 8 MFMAs
+// per wave; one float per wave to sink[blocks * 4].
+int launch_mfma_probe(int blocks, int iters, float *sink, hipStream_t stream);
+
 }  // namespace wide
