@@ -254,6 +254,39 @@ int wide_gemm_k_ws(const wide_bf16 *A, int64_t lda, const wide_bf16 *B, int64_t 
 size_t wide_gemm_k_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /*
+ * wide_gemm_k_grouped -- GEMM-K computed group by group from the reorder
+ * (Appendix B, Eq. 21 and Algorithm 3): the same product as wide_gemm_k,
+ *
+ *   C[m][n] = beta * C[m][n]
+ *           + sum_g [m among the first counts[g] rows of perm[g]]
+ *                   * sum_{k in [gG, (g+1)G)} A[m][k] * B[n][k],
+ *
+ * with the rows that keep group g read from wide_reorder's output instead of
+ * a mask. Every (group, 256 sorted rows, 256 or 128 features) tile that has
+ * rows multiplies them over the group's G columns only, and adds its partial
+ * tile into C with fp32 atomic adds at the gathered rows; a tile past
+ * counts[g] does nothing. Work and A traffic are those of the active pairs
+ * only; the cost is K/G partial writes per output row, which suits large
+ * groups (the page's observation that GEMM-K needs G > 128).
+ *   A [M][K] bf16 (lda), B [N][K] bf16 (ldb), C [M][N] fp32 (ldc).
+ *   perm [K/G][M], counts [K/G]: wide_reorder(mask, 1, M, K/G, ...) of the
+ *     [M][K/G] mask. perm entries outside [0, M) are dropped (never
+ *     dereferenced); counts are clamped to M.
+ *   beta 0: C is zeroed first (rows in no group end at exact 0); 1: added to.
+ * Results: the partials of different groups reach an entry of C in no fixed
+ * order, so fp32 rounding can differ run to run (the sum is the same up to
+ * reassociation of K/G terms).
+ * Requirements: K % G == 0; lda, ldb >= K and multiples of 8; ldc >= N and a
+ * multiple of 4; 16-byte aligned A, B, C; C must not overlap A, B, perm or
+ * counts (WIDE_ERR_INVALID_ARG). WIDE_ERR_UNSUPPORTED unless G % 64 == 0,
+ * N % 128 == 0, M * lda * 2 < 2^31 and ldb < 2^22.
+ */
+int wide_gemm_k_grouped(const wide_bf16 *A, int64_t lda, const wide_bf16 *B, int64_t ldb,
+                        float *C, int64_t ldc, int beta, int64_t M, int64_t N, int64_t K,
+                        int64_t G, const int32_t *perm, const int32_t *counts,
+                        wide_stream_t stream);
+
+/*
  * wide_attn -- head-group-masked causal GQA attention (section 3.1, Eq. 2;
  * Appendix B, Algorithm 4 and its decoding paragraph).
  *

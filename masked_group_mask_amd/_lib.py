@@ -41,6 +41,8 @@ _SIGS = {
     "wide_gemm_k_ws": [_ptr, _i64, _ptr, _i64, _ptr, _i64, _int, _i64, _i64, _i64, _i64, _ptr, _ptr, _ptr,
                        _size, _ptr],
     "wide_gemm_k_workspace_bytes": [_i64] * 3,
+    "wide_gemm_k_grouped": [_ptr, _i64, _ptr, _i64, _ptr, _i64, _int, _i64, _i64, _i64, _i64, _ptr, _ptr,
+                            _ptr],
     "wide_attn": [_ptr, _ptr, _ptr, _ptr, _int, _i64, _i64, _i64, _i64, _i64, _i64, _int, _f32,
                   _ptr, _ptr, _ptr, _ptr, _ptr, _size, _ptr],
     "wide_router": [_ptr, _i64, _ptr, _ptr, _i64, _i64, _i64, _i64, _i64, _ptr, _ptr, _ptr, _ptr,
@@ -347,6 +349,35 @@ def gemm_k(A: torch.Tensor, B: torch.Tensor, G: int, mask: torch.Tensor,
     ws, wsb = _ws(workspace, A)
     _call("wide_gemm_k_ws", _p(A), _rowmajor(A, "A"), _p(B), _rowmajor(B, "B"), _p(out),
           _rowmajor(out, "out"), int(beta), M, N, K, G, _p(order), _p(mask), ws, wsb, _stream())
+    return out
+
+
+def gemm_k_grouped(A: torch.Tensor, B: torch.Tensor, G: int, perm: torch.Tensor, counts: torch.Tensor,
+                   out: Optional[torch.Tensor] = None, beta: int = 0) -> torch.Tensor:
+    """GEMM-K group by group from the reorder of the [M][K/G] mask: every
+    active (group, row tile) multiplies over the group's columns and adds its
+    partial into C (fp32) with atomics. perm [K/G][M] (or [1][K/G][M]) and
+    counts [K/G] (or [1][K/G]) from reorder."""
+    _need(A, "A", torch.bfloat16, 2)
+    _need(B, "B", torch.bfloat16, 2)
+    M, K = A.shape
+    N = B.shape[0]
+    if B.shape[1] != K:
+        raise ValueError("A and B disagree on K")
+    if G < 1 or K % G:
+        raise ValueError(f"K = {K} is not a multiple of the group size {G}")
+    if perm is None or counts is None:
+        raise ValueError("gemm_k_grouped needs perm and counts")
+    _routing(M, K // G, perm, counts, None)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=A.device)
+        beta = 0
+    _need(out, "out", torch.float32, 2)
+    if tuple(out.shape) != (M, N):
+        raise ValueError("out shape mismatch")
+    _on_device(A, B=B, out=out, perm=perm, counts=counts)
+    _call("wide_gemm_k_grouped", _p(A), _rowmajor(A, "A"), _p(B), _rowmajor(B, "B"), _p(out),
+          _rowmajor(out, "out"), int(beta), M, N, K, G, _p(perm), _p(counts), _stream())
     return out
 
 

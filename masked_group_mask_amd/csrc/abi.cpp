@@ -237,6 +237,33 @@ int wide_gemm_k_ws(const wide_bf16 *A, int64_t lda, const wide_bf16 *B, int64_t 
   return wide::launch_gemm_k(a, reinterpret_cast<hipStream_t>(stream));
 }
 
+int wide_gemm_k_grouped(const wide_bf16 *A, int64_t lda, const wide_bf16 *B, int64_t ldb, float *C,
+                        int64_t ldc, int beta, int64_t M, int64_t N, int64_t K, int64_t G,
+                        const int32_t *perm, const int32_t *counts, wide_stream_t stream) {
+  if (!A || !B || !C || !perm || !counts) return WIDE_ERR_INVALID_ARG;
+  if (M < 1 || N < 1 || K < 1 || G < 1) return WIDE_ERR_INVALID_ARG;
+  if (M > kI32Max || N > kI32Max || K > kI32Max) return WIDE_ERR_INVALID_ARG;
+  if (K % G != 0 || lda < K || ldb < K || lda % 8 != 0 || ldb % 8 != 0) return WIDE_ERR_INVALID_ARG;
+  if (ldc < N || ldc % 4 != 0 || (beta != 0 && beta != 1)) return WIDE_ERR_INVALID_ARG;
+  if (!aligned16(A) || !aligned16(B) || !aligned16(C)) return WIDE_ERR_INVALID_ARG;
+  const int64_t NG = K / G;
+  const size_t cb = span_bytes(M, N, ldc, 4);
+  if (overlap(C, cb, A, span_bytes(M, K, lda, 2)) || overlap(C, cb, B, span_bytes(N, K, ldb, 2)) ||
+      overlap(C, cb, perm, (size_t)NG * M * 4) || overlap(C, cb, counts, (size_t)NG * 4))
+    return WIDE_ERR_INVALID_ARG;
+  if (G % 64 != 0 || N % 128 != 0) return WIDE_ERR_UNSUPPORTED;
+  // Gathered rows are addressed with 32-bit byte offsets into A, a tile's
+  // (at most 256) weight rows with 32-bit offsets into B; one workgroup per
+  // (group, row tile, column tile).
+  if ((uint64_t)M * (uint64_t)lda * 2u > 0x7fffffffull || (uint64_t)ldb * 512u > 0x7fffffffull)
+    return WIDE_ERR_UNSUPPORTED;
+  if ((uint64_t)NG * (uint64_t)((M + 255) / 256) * (uint64_t)(N / 128) > 0x7fffffffull)
+    return WIDE_ERR_UNSUPPORTED;
+  if (!device_ok()) return WIDE_ERR_NO_DEVICE;
+  wide::KgArgs a{A, lda, B, ldb, C, ldc, beta, (int)M, (int)N, (int)K, (int)G, perm, counts};
+  return wide::launch_gemm_kg(a, reinterpret_cast<hipStream_t>(stream));
+}
+
 int wide_router(const wide_bf16 *X, int64_t ldx, const wide_bf16 *W1, const wide_bf16 *W2,
                 int64_t batch, int64_t rows, int64_t D, int64_t r, int64_t groups, uint8_t *mask,
                 float *logits, int32_t *perm, int32_t *counts, wide_stream_t stream) {

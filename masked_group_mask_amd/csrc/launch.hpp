@@ -89,6 +89,23 @@ int launch_gemm_k(const KArgs &a, hipStream_t stream);
 // current device (0 when the plan splits nothing).
 size_t gemm_k_workspace_bytes(int M, int N, int K);
 
+// GEMM-K by K-groups: every active (group, sorted row tile) pair multiplies
+// its rows over the group's G columns and adds the partial into C with
+// atomics (C zeroed first when beta = 0). Needs G % 64 == 0, N % 128 == 0.
+struct KgArgs {
+  const uint16_t *A;
+  int64_t lda;
+  const uint16_t *B;
+  int64_t ldb;
+  float *C;
+  int64_t ldc;
+  int beta;
+  int M, N, K, G;
+  const int32_t *perm;    // [K/G][M]
+  const int32_t *counts;  // [K/G]
+};
+int launch_gemm_kg(const KgArgs &a, hipStream_t stream);
+
 struct AttnArgs {
   const uint16_t *Q, *K, *V;
   void *O;

@@ -192,6 +192,32 @@ def test_gemm_k_validation(lib):
     assert gk(lib, order=P(2)) == INVALID                   # C overlaps the order
 
 
+def gkg(lib, **kw):
+    """wide_gemm_k_grouped on fake pointers spaced far apart."""
+    far = {k: ctypes.c_void_p((i + 1) << 40) for i, k in enumerate(("A", "B", "C", "perm", "counts"))}
+    a = dict(lda=256, ldb=256, ldc=256, beta=0, M=32, N=256, K=256, G=64, **far)
+    a.update(kw)
+    return lib.wide_gemm_k_grouped(a["A"], a["lda"], a["B"], a["ldb"], a["C"], a["ldc"], a["beta"],
+                                   a["M"], a["N"], a["K"], a["G"], a["perm"], a["counts"], None)
+
+
+def test_gemm_k_grouped_validation(lib):
+    assert gkg(lib, perm=None) == INVALID
+    assert gkg(lib, counts=None) == INVALID
+    assert gkg(lib, K=200) == INVALID                       # K % G
+    assert gkg(lib, beta=2) == INVALID
+    assert gkg(lib, ldc=258) == INVALID                     # ldc % 4
+    assert gkg(lib, lda=128) == INVALID                     # lda < K
+    assert gkg(lib, C=ctypes.c_void_p((4 << 40) + 64)) == INVALID   # C overlaps perm
+    assert gkg(lib, C=ctypes.c_void_p(((5 << 40) - 64))) == INVALID  # C overlaps counts
+    assert gkg(lib, G=32, K=256) == UNSUPPORTED             # groups narrower than a 64-deep stage
+    assert gkg(lib, N=64, ldc=64) == UNSUPPORTED            # N % 128
+    assert gkg(lib, M=1 << 20, lda=2048, K=2048, ldb=2048) == UNSUPPORTED  # 32-bit offsets into A
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        assert gkg(lib) == NO_DEVICE
+
+
 def test_order_by_pattern_validation(lib):
     f = lib.wide_order_by_pattern
     assert f(None, 64, 8, P(1), None) == INVALID

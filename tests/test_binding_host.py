@@ -49,6 +49,19 @@ def test_gemm_mn_swiglu_routing_sizes_and_output():
     raises("device", mg.gemm_mn_swiglu, A, W, W, G, perm=perm, counts=counts, out=z(M, N))
 
 
+def test_gemm_k_grouped_routing_sizes():
+    A, B = z(M, K), z(N, K)
+    perm, counts = z(K // G, M, dtype=i32), z(K // G, dtype=i32)
+    raises("device", mg.gemm_k_grouped, A, B, G, perm, counts)
+    raises("device", mg.gemm_k_grouped, A, B, G, perm[None], counts[None])   # reorder's batch-1 shapes
+    # the FFN reorder handed to a smaller GEMM-K
+    raises("perm", mg.gemm_k_grouped, A, B, G, z(4 * K // G, M, dtype=i32), counts)
+    raises("counts", mg.gemm_k_grouped, A, B, G, perm, z(K // G + 1, dtype=i32))
+    raises("needs perm", mg.gemm_k_grouped, A, B, G, None, counts)
+    raises("multiple", mg.gemm_k_grouped, A, B, 96, perm, counts)
+    raises("out", mg.gemm_k_grouped, A, B, G, perm, counts, out=z(M, N - 4, dtype=torch.float32))
+
+
 def test_gemm_k_mask_size():
     A, B = z(M, K), z(N, K)
     raises("device", mg.gemm_k, A, B, G, z(M, K // G, dtype=u8))
