@@ -47,6 +47,7 @@ constexpr int kAk = 64;    // keys per K/V stage
 constexpr int kAd = 128;   // head size
 constexpr int kAStage = kAk * kAd;  // bf16 elements of one K (or V) stage
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLazy = 8.f;  // log2 of the largest p the prefill softmax lets through unrescaled
 
 template <bool OUT_F32>
 __device__ __forceinline__ void store4(void *O, size_t idx, float a, float b, float c, float d) {
@@ -65,6 +66,43 @@ __device__ __forceinline__ void store4(void *O, size_t idx, float a, float b, fl
 //      a 32-byte chunk pair from 8 rows per half wave, on distinct positions.
 __device__ __forceinline__ int k_swz(int r) { return r & 15; }
 __device__ __forceinline__ int v_swz(int r) { return (r & 7) << 1; }
+
+// Max and sum over the lanes l, l ^ 16, l ^ 32 and l ^ 48 (the four lanes
+// that hold keys of one query) with gfx950's lane-swap instructions instead of
+// LDS permutes: swapping a register with itself across lane halves (16 within
+// each 32, or 32) leaves, in the two results, lane l's own value and its
+// partner's, in some order, so one max or add finishes each step.
+__device__ __forceinline__ void swap16(float x, float &u, float &v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  u = __uint_as_float(r[0]);
+  v = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void swap32(float x, float &u, float &v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  u = __uint_as_float(r[0]);
+  v = __uint_as_float(r[1]);
+}
+// max(a, b, c) as one instruction. Written out because the compiler's own
+// fmaxf first quiets each operand that does not come from an arithmetic op
+// (here the MFMA results), one extra instruction per operand; the scores are
+// never signalling NaNs.
+__device__ __forceinline__ float max3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+__device__ __forceinline__ float quad_max(float x) {
+  float u, v;
+  swap16(x, u, v);
+  swap32(max3(u, v, v), u, v);
+  return max3(u, v, v);
+}
+__device__ __forceinline__ float quad_sum(float x) {
+  float u, v;
+  swap16(x, u, v);
+  swap32(u + v, u, v);
+  return u + v;
+}
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 
@@ -208,21 +246,29 @@ __global__ __launch_bounds__(kAThreads) void attn_prefill_kernel(AttnArgs a) {
             sc[kb][qb][v] = ok ? sc[kb][qb][v] : -INFINITY;
           }
     }
-    // Online softmax in the log2 domain: m is the running max of scale*log2e*s.
+    // Online softmax in the log2 domain. m is a row's reference: the running
+    // max of scale*log2e*s, moved only when a tile's max exceeds it by more
+    // than kLazy. Until then the tile's p = 2^(t - m) stay below 2^kLazy (no
+    // overflow in fp32 sums or bf16 P) and the output needs no rescale; p, the
+    // row sum l and the output share the reference, so the normalised result
+    // is the same up to rounding. The rescale of the output, 64 multiplies per
+    // lane, then runs only when some row of the wave moved its reference,
+    // which after the first tiles is rare.
     float alpha[kAQB];
     u32x4 pf[2][kAQB];
 #pragma unroll
     for (int qb = 0; qb < kAQB; ++qb) {
-      float mx = -INFINITY;
+      // max of the lane's 16 scores: a chain of 8 three-way maxima
+      float mx = max3(sc[0][qb][0], sc[0][qb][1], sc[0][qb][2]);
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-        mx = fmaxf(mx, fmaxf(fmaxf(sc[kb][qb][0], sc[kb][qb][1]), fmaxf(sc[kb][qb][2], sc[kb][qb][3])));
-      mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-      const float mnew = fmaxf(m[qb], mx * sl2);
-      const float muse = mnew == -INFINITY ? 0.f : mnew;
-      alpha[qb] = exp2_fast(m[qb] - muse);
-      m[qb] = mnew;
+      for (int e = 3; e < 15; e += 2) mx = max3(mx, sc[e / 4][qb][e % 4], sc[(e + 1) / 4][qb][(e + 1) % 4]);
+      mx = quad_max(max3(mx, sc[3][qb][3], sc[3][qb][3]));
+      const float cand = mx * sl2;
+      const bool up = cand > m[qb] + kLazy;  // m = -inf: any finite max moves it
+      const float mref = up ? cand : m[qb];
+      const float muse = mref == -INFINITY ? 0.f : mref;  // a row with no valid key yet: p = 0
+      alpha[qb] = up ? exp2_fast(m[qb] - muse) : 1.f;
+      m[qb] = mref;
       float ls = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
@@ -304,8 +350,7 @@ __global__ __launch_bounds__(kAThreads) void attn_prefill_kernel(AttnArgs a) {
 #pragma unroll
   for (int qb = 0; qb < kAQB; ++qb) {
     float z = l[qb];
-    z += __shfl_xor(z, 16, kWave);
-    z += __shfl_xor(z, 32, kWave);
+    z = quad_sum(z);
     if (qpos[qb] < 0) continue;
     const float inv = z > 0.f ? 1.f / z : 0.f;
     const size_t obase = ((size_t)b * a.Tq + qpos[qb]) * q_row + (size_t)h * kAd + 4 * q;
@@ -422,8 +467,7 @@ __global__ __launch_bounds__(kWave) void attn_decode_split_kernel(AttnArgs a, in
     }
     sc[t] = acc;
   }
-  m = fmaxf(m, __shfl_xor(m, 16, kWave));
-  m = fmaxf(m, __shfl_xor(m, 32, kWave));  // finite: the split has a valid key
+  m = quad_max(m);  // finite: the split has a valid key
   float z = 0.f;
 #pragma unroll
   for (int t = 0; t < 4; ++t)
@@ -433,8 +477,7 @@ __global__ __launch_bounds__(kWave) void attn_decode_split_kernel(AttnArgs a, in
       sc[t][i] = pv;
       z += pv;
     }
-  z += __shfl_xor(z, 16, kWave);
-  z += __shfl_xor(z, 32, kWave);
+  z = quad_sum(z);
   // P^T fragments: keys 32 ks + 4 q + i, then 32 ks + 16 + 4 q + i.
   u32x4 pf[2];
 #pragma unroll
