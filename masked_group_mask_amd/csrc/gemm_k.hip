@@ -33,6 +33,20 @@ namespace wide {
 constexpr int kKMaxGroups = 512;
 constexpr int kKRasterM = 32;  // m-tiles per raster group (eng::tile_of)
 
+// Tile order of the kernel over pattern-sorted rows. Sorted row tiles differ
+// in cost (the number of groups their rows keep), and the plain raster gives
+// each XCD the same few m-tiles for every n-tile, so the XCDs ended far apart
+// (measured: compute units busy 70% of the span). Here logical tile j is
+// (m-tile j % MT, n-tile j / MT), and the whole tiles are dealt so that each
+// XCD owns a contiguous range of j (xcd_remap): it walks one or two n-tiles
+// over every m-tile, the same mix of costs on every XCD, with its weight
+// columns shared in its L2. Tiles of the K-split tail keep j = L.
+__device__ __forceinline__ void ord_tile_of(int L, int whole, int MT, int &mt, int &tn) {
+  const int j = L < whole ? xcd_remap(L, whole) : L;
+  mt = j % MT;
+  tn = j / MT;
+}
+
 // Builds the tile's bit table: bit r of word i of group g says whether tile
 // row 32 i + r keeps group g. Thread t reads the mask row of tile row t % 256
 // (for the groups g = t / 256 mod THREADS / 256) and each wave turns one
@@ -374,7 +388,7 @@ __global__ __launch_bounds__(512) void gemm_k_ordered_kernel(KArgs a) {
       nparts = a.ksplit;
       L = a.head + slot;
     }
-    eng::tile_of<kKRasterM>(a.tile_base + L, MT, a.N / BN, mt, tn);
+    ord_tile_of(L, a.ksplit > 1 ? a.head : (int)gridDim.x, MT, mt, tn);
   }
   const int m0 = mt * eng::kBM, n0 = tn * BN;
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
@@ -673,7 +687,10 @@ __global__ __launch_bounds__(256) void gemm_k_fixup_kernel(KArgs a) {
   const int r = e / Q, q = e % Q;
   const int MT = (a.M + eng::kBM - 1) / eng::kBM;
   int mt, tn;
-  eng::tile_of<kKRasterM>(a.head + slot, MT, a.N / 256, mt, tn);
+  if (a.order)
+    ord_tile_of(a.head + slot, a.head, MT, mt, tn);
+  else
+    eng::tile_of<kKRasterM>(a.head + slot, MT, a.N / 256, mt, tn);
   const int pos = mt * eng::kBM + r;
   if (pos >= a.M) return;
   const int m = a.order ? a.order[pos] : pos;
