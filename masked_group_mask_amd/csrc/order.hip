@@ -24,31 +24,52 @@ namespace wide {
 constexpr int kOrdThreads = 1024;
 constexpr int kOrdWaves = kOrdThreads / kWave;
 constexpr int kOrdBins = 256;
-constexpr int kOrdKeyRegs = 16;  // 64-row rounds per wave whose keys stay in registers
+// 64-row rounds per wave whose keys stay in registers (fewer with byte loads,
+// whose eight loads per row would otherwise spill at 128 registers a thread)
+template <int WIDE>
+constexpr int ord_key_regs() { return WIDE == 1 ? 4 : 16; }
 
 // Key of row m from the first min(NG, 8) bytes of its mask row: one 8-byte
 // load (WIDE = 8), two 4-byte loads (WIDE = 4) or byte loads (WIDE = 1), all
 // unconditional so a thread's loads are in flight together (the caller
 // clamps m to a valid row).
+// The first min(NG, 8) mask bytes of row m, as loaded (split from the key so
+// that a thread can issue all its loads before it uses any).
+struct RowBytes {
+  uint32_t lo, hi;
+};
+
 template <int WIDE>
-__device__ __forceinline__ int pattern_key(const uint8_t *mask, int m, int NG, int nb) {
+__device__ __forceinline__ RowBytes load_row_bytes(const uint8_t *mask, int m, int NG, int nb) {
   const uint8_t *row = mask + (size_t)m * NG;
-  uint8_t v[8];
+  RowBytes r;
   if (WIDE == 8) {
     const uint64_t w = *reinterpret_cast<const uint64_t *>(row);
-#pragma unroll
-    for (int g = 0; g < 8; ++g) v[g] = (uint8_t)(w >> (8 * g));
+    r.lo = (uint32_t)w;
+    r.hi = (uint32_t)(w >> 32);
   } else if (WIDE == 4) {
-    const uint32_t w0 = *reinterpret_cast<const uint32_t *>(row);
-    const uint32_t w1 = *reinterpret_cast<const uint32_t *>(row + (nb > 4 ? 4 : 0));
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      v[g] = (uint8_t)(w0 >> (8 * g));
-      v[g + 4] = (uint8_t)(w1 >> (8 * g));
-    }
+    r.lo = *reinterpret_cast<const uint32_t *>(row);
+    r.hi = *reinterpret_cast<const uint32_t *>(row + (nb > 4 ? 4 : 0));
   } else {
+    r.lo = r.hi = 0u;
 #pragma unroll
-    for (int g = 0; g < 8; ++g) v[g] = row[g < nb ? g : 0];
+    for (int g = 0; g < 8; ++g) {
+      const uint32_t b = row[g < nb ? g : 0];
+      if (g < 4)
+        r.lo |= b << (8 * g);
+      else
+        r.hi |= b << (8 * (g - 4));
+    }
+  }
+  return r;
+}
+
+__device__ __forceinline__ int row_key(RowBytes r, int nb) {
+  uint8_t v[8];
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    v[g] = (uint8_t)(r.lo >> (8 * g));
+    v[g + 4] = (uint8_t)(r.hi >> (8 * g));
   }
   int p = 0;
 #pragma unroll
@@ -59,6 +80,11 @@ __device__ __forceinline__ int pattern_key(const uint8_t *mask, int m, int NG, i
   k ^= k >> 2;
   k ^= k >> 4;
   return k;
+}
+
+template <int WIDE>
+__device__ __forceinline__ int pattern_key(const uint8_t *mask, int m, int NG, int nb) {
+  return row_key(load_row_bytes<WIDE>(mask, m, NG, nb), nb);
 }
 
 // Lanes of the wave holding the same key as this lane (8 ballots over the
@@ -80,6 +106,9 @@ __device__ __forceinline__ uint64_t key_peers(int key, bool valid) {
 // plus the rows of that key owned by earlier waves; pass 2 places every row
 // at its wave's running offset for its key plus its rank among the equal
 // keys of its round, which keeps equal keys in ascending row order.
+// One compute unit does it all, so the kernel is bound by latency (~17 us
+// at 8192 rows on MI355X, most of it the first pass's mask loads and its
+// dependent LDS updates).
 template <int WIDE>
 __global__ __launch_bounds__(kOrdThreads) void pattern_order_kernel(const uint8_t *mask, int M, int NG,
                                                                     int32_t *order) {
@@ -91,19 +120,28 @@ __global__ __launch_bounds__(kOrdThreads) void pattern_order_kernel(const uint8_
   const int r0 = wave * R, rounds = R / kWave;
   for (int i = tid; i < kOrdWaves * kOrdBins; i += kOrdThreads) (&sH[0][0])[i] = 0;
   __syncthreads();
-  int keep[kOrdKeyRegs];
-  // pass 1: count (keys of the first kOrdKeyRegs rounds kept for pass 2)
-  for (int c = 0; c < rounds; c += kOrdKeyRegs) {
-    int key[kOrdKeyRegs];
+  constexpr int KR = ord_key_regs<WIDE>();
+  int keep[KR];
+  // pass 1: count (keys of the first KR rounds kept for pass 2)
+  for (int c = 0; c < rounds; c += KR) {
+    // every load of the chunk in flight before the first is used
+    RowBytes raw[KR];
 #pragma unroll
-    for (int u = 0; u < kOrdKeyRegs; ++u) {
+    for (int u = 0; u < KR; ++u) {
       const int m = r0 + (c + u) * kWave + lane;
       const bool ok = c + u < rounds && m < M;
-      const int kk = pattern_key<WIDE>(mask, ok ? m : M - 1, NG, nb);
-      key[u] = ok ? kk : -1;
+      raw[u] = load_row_bytes<WIDE>(mask, ok ? m : M - 1, NG, nb);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    int key[KR];
+#pragma unroll
+    for (int u = 0; u < KR; ++u) {
+      const int m = r0 + (c + u) * kWave + lane;
+      const bool ok = c + u < rounds && m < M;
+      key[u] = ok ? row_key(raw[u], nb) : -1;
     }
 #pragma unroll
-    for (int u = 0; u < kOrdKeyRegs; ++u) {
+    for (int u = 0; u < KR; ++u) {
       const uint64_t peers = key_peers(key[u], key[u] >= 0);
       if (key[u] >= 0 && rank_below(peers) == 0) sH[wave][key[u]] += __popcll(peers);
       if (c == 0) keep[u] = key[u];
@@ -142,9 +180,9 @@ __global__ __launch_bounds__(kOrdThreads) void pattern_order_kernel(const uint8_
     const bool valid = m < M;
     int key = -1;
     if (valid) {
-      if (c < kOrdKeyRegs) {
+      if (c < KR) {
 #pragma unroll
-        for (int u = 0; u < kOrdKeyRegs; ++u)
+        for (int u = 0; u < KR; ++u)
           if (u == c) key = keep[u];
       } else {
         key = pattern_key<WIDE>(mask, m, NG, nb);
@@ -163,12 +201,14 @@ __global__ __launch_bounds__(kOrdThreads) void pattern_order_kernel(const uint8_
 int launch_pattern_order(const uint8_t *mask, int M, int NG, int32_t *order, hipStream_t s) {
   // widest load every row start allows (only bytes of the row itself are read)
   const uintptr_t base = reinterpret_cast<uintptr_t>(mask);
-  if (NG >= 8 && NG % 8 == 0 && base % 8 == 0)
-    hipLaunchKernelGGL(pattern_order_kernel<8>, dim3(1), dim3(kOrdThreads), 0, s, mask, M, NG, order);
-  else if (NG >= 4 && NG % 4 == 0 && base % 4 == 0)
-    hipLaunchKernelGGL(pattern_order_kernel<4>, dim3(1), dim3(kOrdThreads), 0, s, mask, M, NG, order);
+  const int wide = NG >= 8 && NG % 8 == 0 && base % 8 == 0 ? 8 : NG >= 4 && NG % 4 == 0 && base % 4 == 0 ? 4 : 1;
+  const dim3 g(1), b(kOrdThreads);
+  if (wide == 8)
+    hipLaunchKernelGGL(pattern_order_kernel<8>, g, b, 0, s, mask, M, NG, order);
+  else if (wide == 4)
+    hipLaunchKernelGGL(pattern_order_kernel<4>, g, b, 0, s, mask, M, NG, order);
   else
-    hipLaunchKernelGGL(pattern_order_kernel<1>, dim3(1), dim3(kOrdThreads), 0, s, mask, M, NG, order);
+    hipLaunchKernelGGL(pattern_order_kernel<1>, g, b, 0, s, mask, M, NG, order);
   return check_launch();
 }
 

@@ -32,12 +32,14 @@ class PrefillLayer:
     def __init__(self, s, host: dict, with_dense: bool = True, scheduled_mn: dict | None = None,
                  ordered_k: tuple = (), leftpad=None):
         self.s = s
-        # GEMM-K ops that run over rows sorted by routing pattern (their tiles
-        # skip the K-groups and 16-row fragments whose rows all skip a group).
+        # GEMM-K ops that run over rows sorted by routing pattern in the
+        # masked step (their tiles skip the K-groups and 16-row fragments
+        # whose rows all skip a group). All-ones masks have nothing to skip,
+        # so the dense reference keeps token order there.
         # Off by default: measured on MI355X at the Qwen3-14B shape, the
-        # ordered o_proj runs 377 us against ~360 us in token order, plus
-        # 21 us for the sort (the main loop is bound by its stage loads, and
-        # the tiles whose rows keep every group set the end of the kernel).
+        # ordered o_proj runs 0.35 against 0.37 ms in token order but its
+        # sort adds ~0.02 ms (one workgroup, latency-bound), inline or on a
+        # side stream, so the step gains nothing.
         self.ordered_k = tuple(ordered_k)
         # GEMM-MN ops that take the workspace (tiles scheduled from counts on
         # the device, group by group, and a short last round split along K),
@@ -92,6 +94,9 @@ class PrefillLayer:
                   mg.gemm_mn_workspace_bytes(M, s.Dff, s.D, s.G_ffn, True))
         self.ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
 
+    def _ordered(self, op: str, which: str) -> bool:
+        return which == "masked" and op in self.ordered_k
+
     def _mn_ws(self, op: str, which: str):
         return self.ws if op in self.scheduled_mn.get(which, ()) else None
 
@@ -105,10 +110,11 @@ class PrefillLayer:
             if s.B > 1:
                 mg.reorder(ma.view(1, s.M, s.Hk), self.perm_q, self.cnt_q)
             mg.reorder(mf.view(1, s.M, s.NG_ffn), self.perm_f, self.cnt_f)
-            if "o_proj" in self.ordered_k:
-                mg.order_by_pattern(ma.view(s.M, s.Hk), self.order_a)
-            if "down_proj" in self.ordered_k:
-                mg.order_by_pattern(mf.view(s.M, s.NG_ffn), self.order_f)
+            sorts = [(op, m, o) for op, m, o in (("o_proj", ma.view(s.M, s.Hk), self.order_a),
+                                                 ("down_proj", mf.view(s.M, s.NG_ffn), self.order_f))
+                     if self._ordered(op, which)]
+            for _, m, o in sorts:
+                mg.order_by_pattern(m, o)
         elif op == "q_proj":
             mg.gemm_mn(self.x, self.wq, s.G_attn, perm=self.perm_q[0], counts=self.cnt_q[0],
                        out=self.q, workspace=self._mn_ws("q_proj", which))
@@ -118,13 +124,13 @@ class PrefillLayer:
         elif op == "o_proj":
             mg.gemm_k(self.o.view(s.M, s.Hq * s.d), self.wo, s.G_attn, ma.view(s.M, s.Hk),
                       out=self.y_attn, workspace=self.ws,
-                      order=self.order_a if "o_proj" in self.ordered_k else None)
+                      order=self.order_a if self._ordered("o_proj", which) else None)
         elif op == "gate_up_swiglu":
             mg.gemm_mn_swiglu(self.x, self.wg, self.wu, s.G_ffn, perm=self.perm_f[0],
                               counts=self.cnt_f[0], out=self.h, workspace=self._mn_ws("gate_up_swiglu", which))
         elif op == "down_proj":
             mg.gemm_k(self.h, self.wd, s.G_ffn, mf.view(s.M, s.NG_ffn), out=self.y_ffn,
-                      workspace=self.ws, order=self.order_f if "down_proj" in self.ordered_k else None)
+                      workspace=self.ws, order=self.order_f if self._ordered("down_proj", which) else None)
         else:
             raise ValueError(f"unknown op {op!r}")
 

@@ -62,7 +62,8 @@ def test_gray_rank_hand_worked():
 
 
 ORDER_CASES = [(1, 8, 0.5), (64, 8, 0.5), (1000, 3, 0.5), (1025, 8, 0.34), (8192, 8, 0.5),
-               (5000, 136, 0.5), (3000, 1, 0.5), (700, 12, 0.9), (300, 8, 0.0), (300, 8, 1.0)]
+               (5000, 136, 0.5), (3000, 1, 0.5), (700, 12, 0.9), (300, 8, 0.0), (300, 8, 1.0),
+               (16384, 8, 0.5), (20000, 8, 0.5), (17000, 5, 0.5)]  # more rounds than keys kept in registers
 
 
 @pytest.mark.parametrize("M,NG,p", ORDER_CASES)
@@ -186,3 +187,29 @@ def test_gemm_k_order_entry_out_of_range_is_dropped():
     assert (got[lost] == -5.0).all()
     keep = np.arange(M) != lost
     check_gemm(got[keep], ref.gemm_k(A, B, mask, G)[keep], "rows with valid order entries")
+
+
+def test_prefill_layer_ordered_o_proj_matches_token_order():
+    """The layer with o_proj over pattern-sorted rows: every output but
+    y_attn is bitwise that of the token-order layer,
+    y_attn agrees at the GEMM bar (a K-split tile groups different rows), and
+    the all-ones reference step still runs in token order."""
+    from masked_group_mask_amd import workloads as wl2
+    from masked_group_mask_amd.layer import PrefillLayer
+    s = wl2.shape("qwen14b_prefill", T=2048, p_attn=0.5, p_ffn=0.5, G_ffn=128)
+    host = wl2.make_layer(s, seed=9)
+    say("layer, ordered o_proj vs token order", s.T)
+    outs = {}
+    for ordered in ((), ("o_proj",)):
+        layer = PrefillLayer(s, host, with_dense=True, ordered_k=ordered)
+        for t in (layer.q, layer.o, layer.h):
+            t.zero_()  # inactive entries are never written
+        layer.step("masked")
+        torch.cuda.synchronize()
+        outs[ordered] = {k: getattr(layer, k).detach().clone() for k in ("q", "o", "h", "y_attn", "y_ffn")}
+        assert not layer._ordered("o_proj", "dense")
+        del layer
+    a, b = outs[()], outs[("o_proj",)]
+    for k in ("q", "o", "h", "y_ffn"):
+        assert torch.equal(a[k], b[k]), k
+    check_gemm(f32_of(b["y_attn"]), f32_of(a["y_attn"]), "ordered o_proj in the layer")

@@ -70,21 +70,26 @@ def prefill_outputs(layer):
             layer.h, layer.y_ffn]
 
 
-def test_prefill_graph_replays_match_eager():
+@pytest.mark.parametrize("ordered", [(), ("o_proj",)], ids=["token_order", "ordered_o_proj"])
+def test_prefill_graph_replays_match_eager(ordered):
     """The masked prefill step (reorders, scheduled GEMM-MN with K-split last
     rounds and their fixups, attention, K-split GEMM-K) captured as a HIP
     graph: the workspace header the fixups read is rewritten by every replay,
-    and every replay reproduces the eager step bit for bit."""
+    and every replay reproduces the eager step bit for bit, also with o_proj
+    over pattern-sorted rows (the sort kernel and the ordered GEMM-K)."""
     from masked_group_mask_amd.layer import PrefillLayer
     s = wl.shape("qwen14b_prefill", T=1024, p_attn=0.5, p_ffn=0.5, G_ffn=128)
-    say("prefill graph replay", s.T, s.D, s.Dff)
-    layer = PrefillLayer(s, wl.make_layer(s, seed=6), with_dense=False)
+    say("prefill graph replay", s.T, s.D, s.Dff, ordered)
+    layer = PrefillLayer(s, wl.make_layer(s, seed=6), with_dense=False, ordered_k=ordered)
     names = ["perm_a", "cnt_a", "perm_f", "cnt_f", "q", "o", "y_attn", "h", "y_ffn"]
+    if ordered:
+        names.append("order_a")
 
     def snap():
-        return [t.detach().view(torch.uint8).cpu().numpy().copy() for t in prefill_outputs(layer)]
+        outs = prefill_outputs(layer) + ([layer.order_a] if ordered else [])
+        return [t.detach().view(torch.uint8).cpu().numpy().copy() for t in outs]
 
-    for t in prefill_outputs(layer):
+    for t in prefill_outputs(layer) + ([layer.order_a] if ordered else []):
         t.zero_()
     layer.step("masked")
     torch.cuda.synchronize()
@@ -94,7 +99,7 @@ def test_prefill_graph_replays_match_eager():
         layer.step("masked")
     torch.cuda.synchronize()
     for r in range(3):
-        for t in prefill_outputs(layer):
+        for t in prefill_outputs(layer) + ([layer.order_a] if ordered else []):
             t.zero_()
         layer.ws.fill_(255)                              # stale workspace between replays
         junk = torch.randn(512, 512, device="cuda") @ torch.randn(512, 512, device="cuda")
