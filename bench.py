@@ -587,7 +587,7 @@ def main():
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the masked layer runs on a single MI355X and "
-              "this build has no multi-GPU path (--gpus must be 1).", file=sys.stderr)
+              "this library has no multi-GPU path (--gpus must be 1).", file=sys.stderr)
         sys.exit(2)
 
     import torch

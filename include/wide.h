@@ -49,7 +49,7 @@ typedef void *wide_stream_t;    /* hipStream_t */
 typedef enum {
   WIDE_OK = 0,
   WIDE_ERR_INVALID_ARG = -1,   /* null pointer, bad size, misalignment, aliasing */
-  WIDE_ERR_UNSUPPORTED = -2,   /* valid request this build does not implement */
+  WIDE_ERR_UNSUPPORTED = -2,   /* valid request this library does not implement */
   WIDE_ERR_NO_DEVICE = -3,     /* no usable HIP device */
   WIDE_ERR_LAUNCH = -4,        /* the HIP runtime rejected a kernel launch */
   WIDE_ERR_TOO_LARGE = -5      /* needs more scratch than wide_attn_noalloc's built-in buffer */
@@ -273,6 +273,8 @@ size_t wide_gemm_k_workspace_bytes(int64_t M, int64_t N, int64_t K);
  *     [M][K/G] mask. perm entries outside [0, M) are dropped (never
  *     dereferenced); counts are clamped to M.
  *   beta 0: C is zeroed first (rows in no group end at exact 0); 1: added to.
+ *   C must be ordinary device memory (hipMalloc, torch): the adds are
+ *   device-scope fp32 atomics, which host-coherent memory does not take.
  * Results: the partials of different groups reach an entry of C in no fixed
  * order, so fp32 rounding can differ run to run (the sum is the same up to
  * reassociation of K/G terms).
