@@ -163,3 +163,48 @@ def test_gemm_k_grouped_full_size_sampled(name, M, N, K, G):
     g, pl = got.cpu().numpy().astype(np.float64), plain.cpu().numpy().astype(np.float64)
     check_gemm(g, pl, f"{name} vs token-order kernel")
     del Ad, Bd, got, plain
+
+
+def _random_k_cases(n=16, seed=2025):
+    """Seeded random shapes for the three GEMM-K forms: group sizes 64 to 640
+    (multiples of 64, so every form applies), N a multiple of 256 or only of
+    128, M from 5 to 2500, activity from none to all, beta 0 or 1."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < n:
+        G = int(rng.choice([64, 128, 192, 256, 640]))
+        NG = int(rng.integers(1, 9))
+        N = int(rng.choice([128, 256, 384, 512, 768]))
+        M = int(rng.choice([5, 77, 256, 300, 1000, 2500]))
+        if M * N * NG * G > 2.5e9:     # keep the fp64 oracle quick
+            continue
+        cases.append((M, N, NG * G, G, float(rng.choice([0.0, 0.1, 0.5, 0.9, 1.0])), int(rng.integers(0, 2))))
+    return cases
+
+
+@pytest.mark.parametrize("M,N,K,G,p,beta", _random_k_cases())
+def test_gemm_k_three_forms_random_shapes(M, N, K, G, p, beta):
+    """Token order, pattern order (where N % 256 == 0 makes it apply) and the
+    per-group form agree with the oracle on the same inputs."""
+    A = wl.random_bf16(M + 600, (M, K))
+    B = wl.random_bf16(N + 601, (N, K), 0.05)
+    mask = wl.random_mask(M + N + K + 602, (M, K // G), p)
+    C0 = ref.from_bf16(wl.random_bf16(603, (M, N)).view(np.uint16)).astype(np.float32)
+    say("gemm_k three forms random", M, N, K, G, p, beta)
+    Ad, Bd, md = to_dev(A, torch), to_dev(B, torch), to_dev(mask, torch)
+    need = W().gemm_k_workspace_bytes(M, N, K)
+    ws = torch.full((max(need, 16) // 4,), float("nan"), dtype=torch.float32, device="cuda")
+
+    def fresh():
+        return to_dev(C0, torch) if beta else torch.full((M, N), float("nan"), device="cuda")
+
+    outs = {"token": W().gemm_k(Ad, Bd, G, md, out=fresh(), beta=beta, workspace=ws if need else None)}
+    torch.cuda.synchronize()
+    outs["ordered"] = W().gemm_k(Ad, Bd, G, md, out=fresh(), beta=beta, workspace=ws if need else None,
+                                 order=W().order_by_pattern(md))
+    perm, counts = routed(md)
+    outs["grouped"] = W().gemm_k_grouped(Ad, Bd, G, perm, counts, out=fresh(), beta=beta)
+    torch.cuda.synchronize()
+    want = ref.gemm_k(A, B, mask, G) + (C0 if beta else 0)
+    for name, o in outs.items():
+        check_gemm(f32_of(o), want, f"gemm_k {name} {M}x{N}x{K} G{G} p{p} beta{beta}")
