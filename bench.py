@@ -578,6 +578,9 @@ def main():
     ap.add_argument("--ordered-k", default="", metavar="OPS",
                     help="comma-separated GEMM-K ops (o_proj, down_proj) to run over rows sorted by "
                          "routing pattern")
+    ap.add_argument("--grouped-k", default="", metavar="OPS",
+                    help="comma-separated GEMM-K ops (o_proj, down_proj) to compute group by group from the "
+                         "reorder with atomic partial writes (the page's Algorithm 3)")
     ap.add_argument("--only", metavar="OP", default=None,
                     help="profiling aid: after one full masked step, run only this op --steps times")
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -624,7 +627,8 @@ def main():
     log(f"inputs ready in {time.perf_counter() - t0:.1f} s")
     from masked_group_mask_amd.layer import PrefillLayer
     ordered = tuple(o for o in args.ordered_k.split(",") if o)
-    layer = PrefillLayer(s, host, with_dense=not args.no_dense, ordered_k=ordered)
+    grouped = tuple(o for o in args.grouped_k.split(",") if o)
+    layer = PrefillLayer(s, host, with_dense=not args.no_dense, ordered_k=ordered, grouped_k=grouped)
     flops = metrics.layer_flops(s, host["mask_attn"], host["mask_ffn"])
     ones_a = np.ones_like(host["mask_attn"])
     ones_f = np.ones_like(host["mask_ffn"])
@@ -664,7 +668,10 @@ def main():
         "config": {"workload": s.name, "B": s.B, "T": s.T, "hidden": s.D, "ffn": s.Dff,
                    "q_heads": s.Hq, "kv_heads": s.Hk, "head_dim": s.d, "G_attn": s.G_attn,
                    "G_ffn": s.G_ffn, "sparsity_attn": args.sparsity, "sparsity_ffn": args.sparsity,
-                   "seed": 0},
+                   "seed": 0,
+                   # GEMM-K form of o_proj / down_proj in the masked step (all-ones: token order)
+                   "gemm_k": {op: ("pattern_order" if op in ordered else "per_group" if op in grouped
+                                   else "token_order") for op in ("o_proj", "down_proj")}},
         "speedup_vs_dense": (dense_ms / ms) if dense_ms else None,
         "ideal_speedup": sum(dense_flops.values()) / total_flops,
         "dense_ms_per_step": dense_ms,

@@ -30,7 +30,7 @@ class PrefillLayer:
     """One masked layer of shape `s` (workloads.LayerShape) on the GPU."""
 
     def __init__(self, s, host: dict, with_dense: bool = True, scheduled_mn: dict | None = None,
-                 ordered_k: tuple = (), leftpad=None):
+                 ordered_k: tuple = (), leftpad=None, grouped_k: tuple = ()):
         self.s = s
         # GEMM-K ops that run over rows sorted by routing pattern in the
         # masked step (their tiles skip the K-groups and 16-row fragments
@@ -41,6 +41,14 @@ class PrefillLayer:
         # sort adds ~0.02 ms (one workgroup, latency-bound), inline or on a
         # side stream, so the step gains nothing.
         self.ordered_k = tuple(ordered_k)
+        # GEMM-K ops computed group by group from the reorder with atomic
+        # partial writes (the page's Algorithm 3) in the masked step. Off by
+        # default: measured on MI355X at the Qwen3-14B shape the atomic adds
+        # bound it (o_proj 0.6 against 0.37 ms, down_proj at G = 256 4.3
+        # against 1.16 ms).
+        self.grouped_k = tuple(grouped_k)
+        if set(self.ordered_k) & set(self.grouped_k):
+            raise ValueError("an op runs either over pattern-sorted rows or group by group")
         # GEMM-MN ops that take the workspace (tiles scheduled from counts on
         # the device, group by group, and a short last round split along K),
         # per mask set. Routed masks give every group its own row set, so
@@ -97,6 +105,9 @@ class PrefillLayer:
     def _ordered(self, op: str, which: str) -> bool:
         return which == "masked" and op in self.ordered_k
 
+    def _grouped(self, op: str, which: str) -> bool:
+        return which == "masked" and op in self.grouped_k
+
     def _mn_ws(self, op: str, which: str):
         return self.ws if op in self.scheduled_mn.get(which, ()) else None
 
@@ -121,6 +132,9 @@ class PrefillLayer:
         elif op == "attention":
             mg.attn(self.q.view(s.B, s.T, s.Hq, s.d), self.k, self.v, perm=self.perm_a,
                     counts=self.cnt_a, out=self.o, leftpad=self.leftpad)
+        elif op == "o_proj" and self._grouped("o_proj", which):
+            mg.gemm_k_grouped(self.o.view(s.M, s.Hq * s.d), self.wo, s.G_attn, self.perm_q[0], self.cnt_q[0],
+                              out=self.y_attn)
         elif op == "o_proj":
             mg.gemm_k(self.o.view(s.M, s.Hq * s.d), self.wo, s.G_attn, ma.view(s.M, s.Hk),
                       out=self.y_attn, workspace=self.ws,
@@ -128,6 +142,8 @@ class PrefillLayer:
         elif op == "gate_up_swiglu":
             mg.gemm_mn_swiglu(self.x, self.wg, self.wu, s.G_ffn, perm=self.perm_f[0],
                               counts=self.cnt_f[0], out=self.h, workspace=self._mn_ws("gate_up_swiglu", which))
+        elif op == "down_proj" and self._grouped("down_proj", which):
+            mg.gemm_k_grouped(self.h, self.wd, s.G_ffn, self.perm_f[0], self.cnt_f[0], out=self.y_ffn)
         elif op == "down_proj":
             mg.gemm_k(self.h, self.wd, s.G_ffn, mf.view(s.M, s.NG_ffn), out=self.y_ffn,
                       workspace=self.ws, order=self.order_f if self._ordered("down_proj", which) else None)
