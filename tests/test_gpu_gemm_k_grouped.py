@@ -208,3 +208,30 @@ def test_gemm_k_three_forms_random_shapes(M, N, K, G, p, beta):
     want = ref.gemm_k(A, B, mask, G) + (C0 if beta else 0)
     for name, o in outs.items():
         check_gemm(f32_of(o), want, f"gemm_k {name} {M}x{N}x{K} G{G} p{p} beta{beta}")
+
+
+def test_prefill_layer_grouped_gemm_k_matches_token_order():
+    """The layer with o_proj and down_proj computed group by group: q, o and
+    h are bitwise those of the token-order layer, y_attn and y_ffn agree at
+    the GEMM bar, and the all-ones reference keeps token order."""
+    from masked_group_mask_amd.layer import PrefillLayer
+    s = wl.shape("qwen14b_prefill", T=2048, p_attn=0.5, p_ffn=0.5, G_ffn=256)
+    host = wl.make_layer(s, seed=11)
+    say("layer, per-group GEMM-K vs token order", s.T)
+    outs = {}
+    for grouped in ((), ("o_proj", "down_proj")):
+        layer = PrefillLayer(s, host, with_dense=True, grouped_k=grouped)
+        for t in (layer.q, layer.o, layer.h):
+            t.zero_()  # inactive entries are never written
+        layer.step("masked")
+        torch.cuda.synchronize()
+        outs[grouped] = {k: getattr(layer, k).detach().clone() for k in ("q", "o", "h", "y_attn", "y_ffn")}
+        assert not layer._grouped("o_proj", "dense")
+        del layer
+    a, b = outs[()], outs[("o_proj", "down_proj")]
+    for k in ("q", "o", "h"):
+        assert torch.equal(a[k], b[k]), k
+    for k in ("y_attn", "y_ffn"):
+        check_gemm(f32_of(b[k]), f32_of(a[k]), f"per-group {k} in the layer")
+    with pytest.raises(ValueError):
+        PrefillLayer(s, host, with_dense=False, ordered_k=("o_proj",), grouped_k=("o_proj",))
