@@ -31,6 +31,7 @@
 namespace wide {
 
 constexpr int kKMaxGroups = 512;
+constexpr int kKMaxGroups320 = 256;  // K-groups the 256 x 320 tile takes
 constexpr int kKRasterM = 32;  // m-tiles per raster group (eng::tile_of)
 
 // Tile order of the kernel over pattern-sorted rows. Sorted row tiles differ
@@ -124,13 +125,22 @@ __device__ __forceinline__ bool build_bits(const KArgs &a, int m, WIDE_LDS uint3
 // elements) lies in one of them, so the predicate is taken per lane from the
 // bit of (row, group of its chunk), read from the table when the stage is
 // issued.
+// Every load instruction of a wave moves rows 8 W apart from the previous
+// one's at the same swizzle, so one per-lane byte offset (that of instruction
+// 0) serves them all and instruction i adds i times the row stride to the
+// wave-uniform offset. A rows past M or skipping the group take the out-of-
+// range offset instead, so only rows below M are ever addressed.
 template <class S, bool SMALLG>
 struct KLoader {
   static constexpr int kDsReads = SMALLG ? 0 : 2;
   static constexpr int kLoadGap = 0;
+  // the bit words kept across the step leave room for fewer fragments (no
+  // spills at BN = 320 with 4 A-fragment groups; measured faster than 2)
+  static constexpr int kWideAGroups = 4;
   static constexpr int AHEAD = S::STAGES - 1;  // stages in flight ahead of the one multiplied
   rsrc_t ar, br, none;
-  uint32_t aoff[S::AI], boff[S::BI];
+  uint32_t aoff, boff;        // lane's byte offset in load instruction 0 (A, B)
+  uint32_t astride, bstride;  // bytes from one load instruction's rows to the next's
   const WIDE_LDS uint32_t *bits;
   int nk, kb, steps_per_group, NG, G, wave, lane;  // steps kb .. kb + nk - 1 of K
   u32x4 wlo, whi;  // bit words (rows 0..127, 128..255) of the group of the next stage
@@ -169,9 +179,10 @@ struct KLoader {
     const uint32_t k0 = (uint32_t)(t + kb) * eng::kBK * 2u;
 #pragma unroll
     for (int i = 0; i < S::AI; ++i)
-      eng::load_lds(ra, eng::load_dst<S::WAVES>(sa, wave, i), ((p >> i) & 1u) ? aoff[i] : kOffNone, k0);
+      eng::load_lds(ra, eng::load_dst<S::WAVES>(sa, wave, i), ((p >> i) & 1u) ? aoff : kOffNone, k0 + i * astride);
 #pragma unroll
-    for (int i = 0; i < S::BI; ++i) eng::load_lds(rb, eng::load_dst<S::WAVES>(sb, wave, i), boff[i], k0);
+    for (int i = 0; i < S::BI; ++i)
+      eng::load_lds(rb, eng::load_dst<S::WAVES>(sb, wave, i), boff, k0 + i * bstride);
     if (t < AHEAD) fetch(t + 1);  // prologue: these stages are issued before any is multiplied
   }
   // while stage t is multiplied, stage t + AHEAD has just been issued
@@ -182,13 +193,15 @@ template <int BN, int W, bool SMALLG>
 __global__ __launch_bounds__(64 * W) void gemm_k_kernel(KArgs a) {
   using S = eng::Shape<BN, W>;
   constexpr int A3 = S::STAGES == 3 ? S::A_ELEMS : 8, B3 = S::STAGES == 3 ? S::B_ELEMS : 8;
+  // the 320-wide tile's two stages take 144 KB of LDS: its table holds 256 groups
+  constexpr int KG = BN == 320 ? kKMaxGroups320 : kKMaxGroups;
   __shared__ __attribute__((aligned(1024))) uint16_t sA0[S::A_ELEMS];
   __shared__ __attribute__((aligned(1024))) uint16_t sB0[S::B_ELEMS];
   __shared__ __attribute__((aligned(1024))) uint16_t sA1[S::A_ELEMS];
   __shared__ __attribute__((aligned(1024))) uint16_t sB1[S::B_ELEMS];
   __shared__ __attribute__((aligned(1024))) uint16_t sA2[A3];
   __shared__ __attribute__((aligned(1024))) uint16_t sB2[B3];
-  __shared__ __attribute__((aligned(16))) uint32_t sBits[kKMaxGroups][8];
+  __shared__ __attribute__((aligned(16))) uint32_t sBits[KG][8];
 
   const int MT = (a.M + eng::kBM - 1) / eng::kBM;
   int mt, tn, n0;
@@ -226,16 +239,11 @@ __global__ __launch_bounds__(64 * W) void gemm_k_kernel(KArgs a) {
     ld.ar = make_rsrc(a.A + (size_t)m0 * a.lda, (uint64_t)rows * a.lda * 2);  // rows past M: out of range
     ld.br = make_rsrc(a.B + (size_t)n0 * a.ldb, (uint64_t)BN * a.ldb * 2);
     ld.none = make_rsrc(a.A, 0);
-#pragma unroll
-    for (int i = 0; i < S::AI; ++i) {
-      const int r = eng::load_row<W>(wave, i, lane);
-      ld.aoff[i] = (uint32_t)r * (uint32_t)a.lda * 2u + eng::load_chunk_bytes(r, lane);
-    }
-#pragma unroll
-    for (int i = 0; i < S::BI; ++i) {
-      const int r = eng::load_row<W>(wave, i, lane);
-      ld.boff[i] = (uint32_t)r * (uint32_t)a.ldb * 2u + eng::load_chunk_bytes(r, lane);
-    }
+    const int r0 = eng::load_row<W>(wave, 0, lane);
+    ld.aoff = (uint32_t)r0 * (uint32_t)a.lda * 2u + eng::load_chunk_bytes(r0, lane);
+    ld.boff = (uint32_t)r0 * (uint32_t)a.ldb * 2u + eng::load_chunk_bytes(r0, lane);
+    ld.astride = 8u * W * (uint32_t)a.lda * 2u;
+    ld.bstride = 8u * W * (uint32_t)a.ldb * 2u;
     ld.bits = (const WIDE_LDS uint32_t *)&sBits[0][0];
     const int nk_all = a.K / eng::kBK;
     ld.kb = part * nk_all / nparts;
@@ -743,7 +751,12 @@ static void launch_k_tiles(const KArgs &a, dim3 grid, hipStream_t s) {
     hipLaunchKernelGGL((gemm_k_kernel<BN, W, true>), grid, dim3(64 * W), 0, s, a);
 }
 
-// Tiled launches. With N a multiple of 256 the 8-wave 256 x 256 kernel runs.
+// Tiled launches. When 256 x 320 tiles fill whole rounds of the compute
+// units (N = 5120 at M = 8192: 512 tiles, where 256 x 256 tiles make 640)
+// and G is a multiple of 64 over at most 256 groups, the 8-wave 320-wide
+// kernel runs alone (measured on MI355X at 50% activity: o_proj, K = 5120,
+// 0.39 ms against 0.41, down_proj, K = 17408, 1.07 against 1.16).
+// Otherwise, with N a multiple of 256, the 8-wave 256 x 256 kernel runs.
 // When its tiles leave a last round at most half full (640 tiles on 256 CUs
 // run as 3 rounds, 2.5 of work) and the caller gave the workspace, each
 // leftover tile is split along K over S workgroups of the same launch, which
@@ -780,6 +793,10 @@ int launch_gemm_k(const KArgs &a0, hipStream_t s) {
     } else {
       hipLaunchKernelGGL(gemm_k_ordered_kernel, dim3(mt * (a.N / 256)), dim3(512), 0, s, a);
     }
+  } else if (a.N % 320 == 0 && a.G % eng::kBK == 0 && a.K / a.G <= kKMaxGroups320 &&
+             (mt * (a.N / 320)) % cu_count() == 0) {
+    a.order = nullptr;
+    hipLaunchKernelGGL((gemm_k_kernel<320, 8, false>), dim3(mt * (a.N / 320)), dim3(512), 0, s, a);
   } else if (a.N % 256 == 0) {
     a.order = nullptr;
     const KSplitPlan p = ksplit_plan(a.M, a.N, a.K);

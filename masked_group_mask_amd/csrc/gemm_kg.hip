@@ -54,6 +54,7 @@ template <class S>
 struct KgLoader {
   static constexpr int kDsReads = 0;
   static constexpr int kLoadGap = 0;
+  static constexpr int kWideAGroups = 2;
   rsrc_t ar, br, none;
   uint32_t aoff[S::AI], boff[S::BI];
   uint32_t kbyte0;  // byte offset of the group's first column

@@ -66,6 +66,7 @@ struct MnLoader {
   // SwiGLU tiles run faster with the next stage's loads packed at the start
   // of the step; plain tiles with them spread (both measured)
   static constexpr int kLoadGap = SPLIT ? 1 : 0;
+  static constexpr int kWideAGroups = 2;
   rsrc_t ar, br0, br1, none;
   uint32_t aoff[S::AI], boff[S::BI];
   int nk, kb, K, wave;  // steps kb .. kb + nk - 1 of K

@@ -100,16 +100,17 @@ __device__ __forceinline__ int b_frag_row(int wn, int i) {
 
 // One stage: two 32-deep halves, each reading its fragments then issuing the
 // MFMAs. With more than 4 B fragments per wave (BN = 320) the A fragments are
-// read and used in AG = 2 groups, so fewer fragment registers are live at
-// once. `issue.prefetch(t)` runs after the first half's first reads (the
-// loader's own LDS reads, consumed at the next step).
-template <class S>
-constexpr int a_groups() { return S::FN > 4 ? 2 : 1; }
+// read and used in AG groups (Issue::kWideAGroups: 2 or 4), so fewer fragment
+// registers are live at once; a loader that keeps more registers of its own
+// across the step takes 4. `issue.prefetch(t)` runs after the first half's
+// first reads (the loader's own LDS reads, consumed at the next step).
+template <class S, class Issue>
+constexpr int a_groups() { return S::FN > 4 ? Issue::kWideAGroups : 1; }
 
 template <class S, int BN, bool SPLIT, class Issue>
 __device__ __forceinline__ void compute_stage(const lds_u16 *sa, const lds_u16 *sb, Acc<S> &acc, int wm, int wn,
                                               int lane, Issue &issue, int t) {
-  constexpr int AG = a_groups<S>(), FMG = S::FM / AG;
+  constexpr int AG = a_groups<S, Issue>(), FMG = S::FM / AG;
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
     u32x4 fb[S::FN];
@@ -160,10 +161,10 @@ __device__ __forceinline__ void interleave_half() {
 // Order of one step. 3 stages: the stage loads are spread over both halves.
 // 2 stages: the next stage is needed at the next step, so its loads all go in
 // the first half, at most QMAX MFMAs apart when QMAX > 0. The loader's own LDS
-// reads come first in program order.
-template <class S, int EXTRA_DS, int QMAX>
+// reads come first in program order. With A-fragment groups, the loads are
+// spread over the first half's groups (the first group takes the remainder).
+template <class S, int AG, int EXTRA_DS, int QMAX>
 __device__ __forceinline__ void interleave() {
-  constexpr int AG = a_groups<S>();
   constexpr int NRB = S::FN, NRA = S::FM / AG, NMG = S::FN * S::FM / AG;
   if constexpr (AG == 1) {
     constexpr int NR = NRA + NRB, NM = NMG;
@@ -175,14 +176,25 @@ __device__ __forceinline__ void interleave() {
       interleave_half<NR + EXTRA_DS, NM, S::NLOAD, QMAX>();
       interleave_half<NR, NM, 0>();
     }
-  } else {
-    static_assert(AG == 2 && S::STAGES == 2, "A-fragment groups only with the 2-stage tile");
+  } else if constexpr (AG == 2) {
+    static_assert(S::STAGES == 2, "A-fragment groups only with the 2-stage tile");
     // first half: B + A group 0 (and the loader's reads), A group 1; loads
     // spread over the first half; second half without loads
     constexpr int NV0 = S::NLOAD / 2, NV1 = S::NLOAD - NV0;
     interleave_half<NRB + NRA + EXTRA_DS, NMG, NV0, QMAX>();
     interleave_half<NRA, NMG, NV1, QMAX>();
     interleave_half<NRB + NRA, NMG, 0>();
+    interleave_half<NRA, NMG, 0>();
+  } else {
+    static_assert(AG == 4 && S::STAGES == 2, "A-fragment groups only with the 2-stage tile");
+    constexpr int NV = S::NLOAD / 4, NV0 = S::NLOAD - 3 * NV;
+    interleave_half<NRB + NRA + EXTRA_DS, NMG, NV0, QMAX>();
+    interleave_half<NRA, NMG, NV, QMAX>();
+    interleave_half<NRA, NMG, NV, QMAX>();
+    interleave_half<NRA, NMG, NV, QMAX>();
+    interleave_half<NRB + NRA, NMG, 0>();
+    interleave_half<NRA, NMG, 0>();
+    interleave_half<NRA, NMG, 0>();
     interleave_half<NRA, NMG, 0>();
   }
 }
@@ -191,7 +203,8 @@ __device__ __forceinline__ void interleave() {
 // wave for stage t into (sa, sb), out of range when t >= nk, and no other
 // vector-memory loads; `issue.prefetch(t)` (called while stage t is
 // multiplied) may issue Issue::kDsReads LDS reads whose results the next issue
-// uses; Issue::kLoadGap caps the MFMAs between two stage loads of the 2-stage
+// uses; Issue::kWideAGroups sets the A-fragment groups of a 320-wide tile;
+// Issue::kLoadGap caps the MFMAs between two stage loads of the 2-stage
 // tile (0: spread evenly). The stage buffers are distinct LDS objects so the
 // compiler can tell them apart when it places its own waits.
 //
@@ -204,15 +217,15 @@ __device__ __forceinline__ void mainloop(int nk, Issue &issue, lds_u16 *a0, lds_
                                          lds_u16 *a2, lds_u16 *b2, Acc<S> &acc, int wm, int wn, int lane) {
   constexpr int NL = S::NLOAD;
   int t = 0;
-#define WIDE_STEP(WAITN, CA, CB, NA, NB, AHEAD)                         \
-  {                                                                     \
-    WIDE_WAIT_VM_LGKM0(WAITN);                                          \
-    WIDE_BARRIER();                                                     \
-    issue(t + AHEAD, NA, NB);                                           \
-    compute_stage<S, BN, SPLIT>(CA, CB, acc, wm, wn, lane, issue, t);   \
-    interleave<S, Issue::kDsReads, Issue::kLoadGap>();                  \
-    __builtin_amdgcn_sched_barrier(0);                                  \
-    ++t;                                                                \
+#define WIDE_STEP(WAITN, CA, CB, NA, NB, AHEAD)                              \
+  {                                                                          \
+    WIDE_WAIT_VM_LGKM0(WAITN);                                               \
+    WIDE_BARRIER();                                                          \
+    issue(t + AHEAD, NA, NB);                                                \
+    compute_stage<S, BN, SPLIT>(CA, CB, acc, wm, wn, lane, issue, t);        \
+    interleave<S, a_groups<S, Issue>(), Issue::kDsReads, Issue::kLoadGap>(); \
+    __builtin_amdgcn_sched_barrier(0);                                       \
+    ++t;                                                                     \
   }
   if constexpr (S::STAGES == 3) {
     issue(0, a0, b0);

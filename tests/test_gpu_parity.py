@@ -444,6 +444,52 @@ def test_gemm_k_ksplit(M, N, K, G, beta):
         assert (results[0].cpu().numpy()[:3] == 0).all()
 
 
+WIDE_K_CASES = [  # M, N, K, G, activity; N a multiple of 320
+    # 8 x 32 = 256 tiles of 256 x 320 fill one round on 256 CUs: the 320-wide
+    # kernel, with a ragged last row tile
+    (2000, 10240, 512, 64, 0.5),
+    (2048, 10240, 1280, 128, 0.3),
+    (2000, 10240, 256 * 64, 64, 0.5),   # 256 groups: the most its bit table holds
+    (2000, 10240, 1024, 256, 0.0),      # nothing active: exact zeros
+    # the same shape past the 320-wide kernel's limits: 256 x 256 tiles
+    (2000, 10240, 257 * 64, 64, 0.5),   # 257 groups
+    (2000, 10240, 512, 32, 0.5),        # groups narrower than a 64-deep stage
+]
+
+
+@pytest.mark.parametrize("M,N,K,G,p", WIDE_K_CASES)
+@pytest.mark.parametrize("beta", [0, 1])
+def test_gemm_k_320_wide_tiles(M, N, K, G, p, beta):
+    """Shapes whose 256 x 320 tiles fill whole rounds of the 256 compute units
+    run the 320-wide kernel alone; rows across every row tile, the ragged tail
+    and boundary rows are compared with the oracle; two runs agree bit for bit."""
+    if torch.cuda.get_device_properties(0).multi_processor_count != 256:
+        pytest.skip("tile rounds counted for 256 compute units")
+    A = wl.random_bf16(M + K + 90, (M, K))
+    B = wl.random_bf16(N + 91, (N, K), 0.05)
+    mask = wl.random_mask(M + K + G + 92, (M, K // G), p)
+    mask[:2] = 0  # rows with no active group
+    C0 = wl.random_bf16(93, (M, N))
+    say("gemm_k 320-wide tiles", M, N, K, G, p, "beta", beta)
+    Ad, Bd, md = to_dev(A, torch), to_dev(B, torch), to_dev(mask, torch)
+    outs = []
+    for _ in range(2):
+        out = to_dev(ref.from_bf16(C0).astype(np.float32), torch) if beta else \
+            torch.full((M, N), float("nan"), device="cuda")
+        W().gemm_k(Ad, Bd, G, md, out=out, beta=beta)
+        outs.append(out)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1]), "GEMM-K is not bitwise reproducible"
+    rng = np.random.default_rng(M + N + K)
+    rows = np.unique(np.concatenate([[0, 1, 2, 255, 256, 511, 1023, 1024, 1791, 1792, M - 2, M - 1],
+                                     rng.integers(0, M, 16)]))
+    got = f32_of(outs[0][torch.from_numpy(rows).cuda()])
+    want = ref.gemm_k(A[rows], B, mask[rows], G) + (ref.from_bf16(C0[rows]) if beta else 0)
+    check_gemm(got, want, f"gemm_k 320-wide {M}x{N}x{K} G{G} p{p} beta={beta}")
+    if not beta:
+        assert (got[:2] == 0).all()
+
+
 @pytest.mark.parametrize("p", [0.0, 1.0])
 def test_gemm_k_all_or_nothing(p):
     M, N, K, G = 150, 128, 512, 128
