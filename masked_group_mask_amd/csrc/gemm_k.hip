@@ -31,7 +31,6 @@
 namespace wide {
 
 constexpr int kKMaxGroups = 512;
-constexpr int kKMaxGroups320 = 256;  // K-groups the 256 x 320 tile takes
 constexpr int kKRasterM = 32;  // m-tiles per raster group (eng::tile_of)
 
 // Tile order of the kernel over pattern-sorted rows. Sorted row tiles differ
@@ -192,16 +191,18 @@ struct KLoader {
 template <int BN, int W, bool SMALLG>
 __global__ __launch_bounds__(64 * W) void gemm_k_kernel(KArgs a) {
   using S = eng::Shape<BN, W>;
+  // third-stage buffers only for 3 stages (unused placeholders, which the
+  // compiler drops, else: the 320-wide tile's two stages and its 16 KB bit
+  // table fill the 160 KB of LDS exactly)
   constexpr int A3 = S::STAGES == 3 ? S::A_ELEMS : 8, B3 = S::STAGES == 3 ? S::B_ELEMS : 8;
-  // the 320-wide tile's two stages take 144 KB of LDS: its table holds 256 groups
-  constexpr int KG = BN == 320 ? kKMaxGroups320 : kKMaxGroups;
+  constexpr int AL3 = S::STAGES == 3 ? 1024 : 16;
   __shared__ __attribute__((aligned(1024))) uint16_t sA0[S::A_ELEMS];
   __shared__ __attribute__((aligned(1024))) uint16_t sB0[S::B_ELEMS];
   __shared__ __attribute__((aligned(1024))) uint16_t sA1[S::A_ELEMS];
   __shared__ __attribute__((aligned(1024))) uint16_t sB1[S::B_ELEMS];
-  __shared__ __attribute__((aligned(1024))) uint16_t sA2[A3];
-  __shared__ __attribute__((aligned(1024))) uint16_t sB2[B3];
-  __shared__ __attribute__((aligned(16))) uint32_t sBits[KG][8];
+  __shared__ __attribute__((aligned(AL3))) uint16_t sA2[A3];
+  __shared__ __attribute__((aligned(AL3))) uint16_t sB2[B3];
+  __shared__ __attribute__((aligned(16))) uint32_t sBits[kKMaxGroups][8];
 
   const int MT = (a.M + eng::kBM - 1) / eng::kBM;
   int mt, tn, n0;
@@ -753,9 +754,9 @@ static void launch_k_tiles(const KArgs &a, dim3 grid, hipStream_t s) {
 
 // Tiled launches. When 256 x 320 tiles fill whole rounds of the compute
 // units (N = 5120 at M = 8192: 512 tiles, where 256 x 256 tiles make 640)
-// and G is a multiple of 64 over at most 256 groups, the 8-wave 320-wide
-// kernel runs alone (measured on MI355X at 50% activity: o_proj, K = 5120,
-// 0.39 ms against 0.41, down_proj, K = 17408, 1.07 against 1.16).
+// and G is a multiple of 64, the 8-wave 320-wide kernel runs alone
+// (measured on MI355X at 50% activity: o_proj, K = 5120, 0.39 ms against
+// 0.41, down_proj, K = 17408, 1.07 against 1.16).
 // Otherwise, with N a multiple of 256, the 8-wave 256 x 256 kernel runs.
 // When its tiles leave a last round at most half full (640 tiles on 256 CUs
 // run as 3 rounds, 2.5 of work) and the caller gave the workspace, each
@@ -793,8 +794,7 @@ int launch_gemm_k(const KArgs &a0, hipStream_t s) {
     } else {
       hipLaunchKernelGGL(gemm_k_ordered_kernel, dim3(mt * (a.N / 256)), dim3(512), 0, s, a);
     }
-  } else if (a.N % 320 == 0 && a.G % eng::kBK == 0 && a.K / a.G <= kKMaxGroups320 &&
-             (mt * (a.N / 320)) % cu_count() == 0) {
+  } else if (a.N % 320 == 0 && a.G % eng::kBK == 0 && (mt * (a.N / 320)) % cu_count() == 0) {
     a.order = nullptr;
     hipLaunchKernelGGL((gemm_k_kernel<320, 8, false>), dim3(mt * (a.N / 320)), dim3(512), 0, s, a);
   } else if (a.N % 256 == 0) {

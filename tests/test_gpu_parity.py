@@ -449,11 +449,10 @@ WIDE_K_CASES = [  # M, N, K, G, activity; N a multiple of 320
     # kernel, with a ragged last row tile
     (2000, 10240, 512, 64, 0.5),
     (2048, 10240, 1280, 128, 0.3),
-    (2000, 10240, 256 * 64, 64, 0.5),   # 256 groups: the most its bit table holds
+    (2000, 10240, 512 * 64, 64, 0.5),   # 512 groups: the most the bit table holds
     (2000, 10240, 1024, 256, 0.0),      # nothing active: exact zeros
-    # the same shape past the 320-wide kernel's limits: 256 x 256 tiles
-    (2000, 10240, 257 * 64, 64, 0.5),   # 257 groups
-    (2000, 10240, 512, 32, 0.5),        # groups narrower than a 64-deep stage
+    # groups narrower than a 64-deep stage: the same shape in 256 x 256 tiles
+    (2000, 10240, 512, 32, 0.5),
 ]
 
 
