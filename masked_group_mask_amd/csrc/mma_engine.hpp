@@ -32,24 +32,27 @@ namespace eng {
 #define WIDE_LDS __attribute__((address_space(3)))
 typedef WIDE_LDS uint16_t lds_u16;
 
-constexpr int kBM = 256;    // A rows per tile
+constexpr int kBM = 256;    // A rows per tile (320 for the 320 x 256 tile)
 constexpr int kBK = 64;     // reduction depth per stage
 
-template <int BN, int W>
+template <int BN, int W, int BM = kBM>
 struct Shape {
-  static_assert((W == 4 && (BN == 64 || BN == 128)) || (W == 8 && (BN == 256 || BN == 320)), "unsupported tile");
+  static_assert((W == 4 && BM == 256 && (BN == 64 || BN == 128)) ||
+                    (W == 8 && ((BM == 256 && (BN == 256 || BN == 320)) || (BM == 320 && BN == 256))),
+                "unsupported tile");
   static constexpr int WAVES = W;
   static constexpr int THREADS = 64 * W;
+  static constexpr int ROWS = BM;           // A rows of the tile
   static constexpr int WNW = W / 2;         // waves along n (2 along m)
   static constexpr int STAGES = W == 4 ? 3 : 2;
-  static constexpr int TM = 128;            // wave block rows
+  static constexpr int TM = BM / 2;         // wave block rows
   static constexpr int TN = BN / WNW;       // wave block columns
   static constexpr int FM = TM / 16;        // 16-row fragments of A per wave
   static constexpr int FN = TN / 16;        // 16-row fragments of B per wave
-  static constexpr int AI = kBM / 8 / W;    // A load instructions per wave per stage
+  static constexpr int AI = BM / 8 / W;     // A load instructions per wave per stage
   static constexpr int BI = BN / 8 / W;     // B load instructions per wave per stage
   static constexpr int NLOAD = AI + BI;
-  static constexpr int A_ELEMS = kBM * kBK;
+  static constexpr int A_ELEMS = BM * kBK;
   static constexpr int B_ELEMS = BN * kBK;
 };
 
@@ -102,10 +105,11 @@ __device__ __forceinline__ int b_frag_row(int wn, int i) {
 // MFMAs. With more than 4 B fragments per wave (BN = 320) the A fragments are
 // read and used in AG groups (Issue::kWideAGroups: 2 or 4), so fewer fragment
 // registers are live at once; a loader that keeps more registers of its own
-// across the step takes 4. `issue.prefetch(t)` runs after the first half's
-// first reads (the loader's own LDS reads, consumed at the next step).
+// across the step takes 4. With 10 A fragments (320 rows) they go in two
+// groups of 5. `issue.prefetch(t)` runs after the first half's first reads
+// (the loader's own LDS reads, consumed at the next step).
 template <class S, class Issue>
-constexpr int a_groups() { return S::FN > 4 ? Issue::kWideAGroups : 1; }
+constexpr int a_groups() { return S::FM > 8 ? 2 : S::FN > 4 ? Issue::kWideAGroups : 1; }
 
 template <class S, int BN, bool SPLIT, class Issue>
 __device__ __forceinline__ void compute_stage(const lds_u16 *sa, const lds_u16 *sb, Acc<S> &acc, int wm, int wn,

@@ -105,17 +105,18 @@ def mnw(lib, ws, wsb, M, N, K, G, swiglu=False, perm=True):
 
 
 def test_gemm_mn_workspace_plan(lib):
-    """Workspace of the scheduled GEMM-MN path: a header plus one fp32 tile of
-    256 rows x the tile width per compute unit (256 CUs when no device
-    answers), and none when K is too short for any split (fewer than 16
-    K-steps of 64)."""
+    """Workspace of the scheduled GEMM-MN path: a header plus one fp32 tile
+    (320 rows for the 256-wide tiles, else 256) x the tile width per compute
+    unit (256 CUs when no device answers), and none when K is too short for
+    any split (fewer than 16 K-steps of 64)."""
     f = lib.wide_gemm_mn_workspace_bytes
     hdr = 4 * 4 * 1025
     cus = f(8192, 5120, 5120, 640, 0) - hdr
     assert cus % (256 * 320 * 4) == 0 and cus > 0
     cus //= 256 * 320 * 4
     assert f(8192, 5120, 5120, 640, 0) == hdr + cus * 256 * 320 * 4    # 320-wide tiles
-    assert f(8192, 17408, 5120, 128, 1) == hdr + cus * 256 * 256 * 4   # fused SwiGLU tile
+    assert f(8192, 17408, 5120, 128, 1) == hdr + cus * 320 * 256 * 4   # fused SwiGLU tile
+    assert f(8192, 4096, 4096, 512, 0) == hdr + cus * 320 * 256 * 4    # 256-wide tiles
     assert f(1000, 512, 1000, 64, 0) == hdr + cus * 256 * 64 * 4       # 64-wide tiles
     assert f(1000, 512, 960, 64, 0) == 0                                # 15 K-steps
     assert f(0, 512, 4096, 64, 0) == 0 and f(10, 500, 4096, 64, 0) == 0  # bad sizes

@@ -207,11 +207,12 @@ def test_gemm_mn_swiglu(M, N, K, G, dt):
         assert (bits_of(out)[~keep] == 0).all()
 
 
-def _mn_active_tiles(mask2d, G, bn_out):
+def _mn_active_tiles(mask2d, G, bn_out, rows=256):
     """Active tiles of the scheduled GEMM-MN path, counted on the host from
-    the mask: ceil(count_g / 256) row tiles times G / bn_out column tiles."""
+    the mask: ceil(count_g / rows) row tiles times G / bn_out column tiles
+    (rows = 320 for the 256-wide tiles, plain or fused SwiGLU)."""
     counts = mask2d.astype(bool).sum(axis=0)
-    return int(((counts + 255) // 256).sum()) * (G // bn_out)
+    return int(((counts + rows - 1) // rows).sum()) * (G // bn_out)
 
 
 def _run_mn_ws(Ad, Bd, Bu, perm, counts, G, out_dtype, ws, M, N):
@@ -223,20 +224,21 @@ def _run_mn_ws(Ad, Bd, Bu, perm, counts, G, out_dtype, ws, M, N):
     return out
 
 
-# M, N, K, G, swiglu, bn_out of the tile the launcher picks, p(active)
+# M, N, K, G, swiglu, bn_out and rows of the tile the launcher picks, p(active)
 MN_WS_CASES = [
-    (1000, 1280, 1024, 640, False, 320, 0.5),  # 320-wide tiles, 2 column tiles per group
-    (700, 512, 2048, 128, True, 128, 0.5),     # fused SwiGLU tile
-    (300, 512, 1000, 64, False, 64, 0.5),      # 4-wave 64-wide tile, K tail inside the last slice
-    (4352, 4096, 1024, 128, True, 128, 0.5),   # more tiles than CUs, a short last round
-    (500, 640, 4096, 640, False, 320, 0.5),    # 2 tiles in 8 slices
-    (2000, 1024, 1536, 256, False, 256, 0.0),  # nothing active: the fixup finds no split tile
+    (1000, 1280, 1024, 640, False, 320, 256, 0.5),  # 320-wide tiles, 2 column tiles per group
+    (700, 512, 2048, 128, True, 128, 320, 0.5),     # fused SwiGLU tile, 320 rows
+    (300, 512, 1000, 64, False, 64, 256, 0.5),      # 4-wave 64-wide tile, K tail inside the last slice
+    (5440, 4096, 1024, 128, True, 128, 320, 0.5),   # more tiles than CUs, a short last round
+    (500, 640, 4096, 640, False, 320, 256, 0.5),    # 2 tiles in 8 slices
+    (1500, 1024, 2048, 256, False, 256, 320, 0.5),  # 256-wide plain tile, 320 rows
+    (2000, 1024, 1536, 256, False, 256, 320, 0.0),  # nothing active: the fixup finds no split tile
 ]
 
 
-@pytest.mark.parametrize("M,N,K,G,swiglu,bn_out,p", MN_WS_CASES)
+@pytest.mark.parametrize("M,N,K,G,swiglu,bn_out,rows,p", MN_WS_CASES)
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
-def test_gemm_mn_scheduled_ksplit(M, N, K, G, swiglu, bn_out, p, dt):
+def test_gemm_mn_scheduled_ksplit(M, N, K, G, swiglu, bn_out, rows, p, dt):
     """With a workspace the tiles are scheduled from counts on the device and
     the tiles of a partly filled last round are split along K (summed by a
     fixup kernel). The workspace starts as NaN garbage; entries of inactive
@@ -249,7 +251,7 @@ def test_gemm_mn_scheduled_ksplit(M, N, K, G, swiglu, bn_out, p, dt):
     need = W().gemm_mn_workspace_bytes(M, N, K, G, swiglu)
     assert need > 0
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    A_t = _mn_active_tiles(mask, G, bn_out)
+    A_t = _mn_active_tiles(mask, G, bn_out, rows)
     split = 0 < A_t % cus <= cus // 2
     if p > 0:
         assert split, f"{A_t} active tiles on {cus} CUs: this case must split its last round"
