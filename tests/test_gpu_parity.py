@@ -232,6 +232,7 @@ MN_WS_CASES = [
     (5440, 4096, 1024, 128, True, 128, 320, 0.5),   # more tiles than CUs, a short last round
     (500, 640, 4096, 640, False, 320, 256, 0.5),    # 2 tiles in 8 slices
     (1500, 1024, 2048, 256, False, 256, 320, 0.5),  # 256-wide plain tile, 320 rows
+    (900, 1024, 1000, 256, False, 256, 320, 0.5),   # 320 rows, K tail inside the last slice
     (2000, 1024, 1536, 256, False, 256, 320, 0.0),  # nothing active: the fixup finds no split tile
 ]
 
@@ -302,16 +303,19 @@ def test_gemm_mn_workspace_reused_across_shapes():
         assert (got.cpu().numpy().view(np.uint32)[~ref.expand(mask, G)] == 0).all()
 
 
-def test_gemm_mn_scheduled_equals_plain_without_split():
+@pytest.mark.parametrize("N,G,bn_out,rows", [(9216, 128, 128, 256), (20480, 256, 256, 320)])
+def test_gemm_mn_scheduled_equals_plain_without_split(N, G, bn_out, rows):
     """When the last round is more than half full nothing is split: the
     scheduled path computes every tile exactly as the plain call does, so the
-    two results agree bit for bit (only the tile order differs)."""
-    M, N, K, G = 700, 9216, 1024, 128
+    two results agree bit for bit (only the tile order differs, and for
+    256-wide tiles the scheduled path's 320 rows against the plain 256: each
+    output's sum runs over the same products in the same order)."""
+    M, K = 700, 1024
     A = wl.random_bf16(240, (M, K))
     B = wl.random_bf16(241, (N, K), 0.05)
     mask = wl.random_mask(242, (M, N // G), 0.5)
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    A_t = _mn_active_tiles(mask, G, 128)
+    A_t = _mn_active_tiles(mask, G, bn_out, rows)
     say("gemm_mn scheduled vs plain", M, N, K, G, "tiles", A_t, "cus", cus)
     if 0 < A_t % cus <= cus // 2:
         pytest.skip(f"{A_t} tiles on {cus} CUs would split")
