@@ -756,7 +756,9 @@ static void launch_k_tiles(const KArgs &a, dim3 grid, hipStream_t s) {
 // units (N = 5120 at M = 8192: 512 tiles, where 256 x 256 tiles make 640)
 // and G is a multiple of 64, the 8-wave 320-wide kernel runs alone
 // (measured on MI355X at 50% activity: o_proj, K = 5120, 0.39 ms against
-// 0.41, down_proj, K = 17408, 1.07 against 1.16).
+// 0.41, down_proj, K = 17408, 1.07 against 1.16). Likewise 256 x 192 tiles
+// when they fill whole rounds and 256 x 256 ones do not (N = 3072 at
+// M = 4096: 256 tiles where 256 x 256 ones leave 64 of 256 CUs idle).
 // Otherwise, with N a multiple of 256, the 8-wave 256 x 256 kernel runs.
 // When its tiles leave a last round at most half full (640 tiles on 256 CUs
 // run as 3 rounds, 2.5 of work) and the caller gave the workspace, each
@@ -797,6 +799,10 @@ int launch_gemm_k(const KArgs &a0, hipStream_t s) {
   } else if (a.N % 320 == 0 && a.G % eng::kBK == 0 && (mt * (a.N / 320)) % cu_count() == 0) {
     a.order = nullptr;
     hipLaunchKernelGGL((gemm_k_kernel<320, 8, false>), dim3(mt * (a.N / 320)), dim3(512), 0, s, a);
+  } else if (a.N % 192 == 0 && a.G % eng::kBK == 0 && (mt * (a.N / 192)) % cu_count() == 0 &&
+             (a.N % 256 != 0 || (mt * (a.N / 256)) % cu_count() != 0)) {
+    a.order = nullptr;
+    hipLaunchKernelGGL((gemm_k_kernel<192, 8, false>), dim3(mt * (a.N / 192)), dim3(512), 0, s, a);
   } else if (a.N % 256 == 0) {
     a.order = nullptr;
     const KSplitPlan p = ksplit_plan(a.M, a.N, a.K);

@@ -38,7 +38,7 @@ constexpr int kBK = 64;     // reduction depth per stage
 template <int BN, int W, int BM = kBM>
 struct Shape {
   static_assert((W == 4 && BM == 256 && (BN == 64 || BN == 128)) ||
-                    (W == 8 && ((BM == 256 && (BN == 256 || BN == 320)) || (BM == 320 && BN == 256))),
+                    (W == 8 && ((BM == 256 && (BN == 192 || BN == 256 || BN == 320)) || (BM == 320 && BN == 256))),
                 "unsupported tile");
   static constexpr int WAVES = W;
   static constexpr int THREADS = 64 * W;

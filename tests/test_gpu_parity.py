@@ -450,7 +450,7 @@ def test_gemm_k_ksplit(M, N, K, G, beta):
         assert (results[0].cpu().numpy()[:3] == 0).all()
 
 
-WIDE_K_CASES = [  # M, N, K, G, activity; N a multiple of 320
+WIDE_K_CASES = [  # M, N, K, G, activity
     # 8 x 32 = 256 tiles of 256 x 320 fill one round on 256 CUs: the 320-wide
     # kernel, with a ragged last row tile
     (2000, 10240, 512, 64, 0.5),
@@ -459,15 +459,21 @@ WIDE_K_CASES = [  # M, N, K, G, activity; N a multiple of 320
     (2000, 10240, 1024, 256, 0.0),      # nothing active: exact zeros
     # groups narrower than a 64-deep stage: the same shape in 256 x 256 tiles
     (2000, 10240, 512, 32, 0.5),
+    # 8 x 32 = 256 tiles of 256 x 192 fill one round where 256 x 256 tiles
+    # (192) would not: the 192-wide kernel
+    (2000, 6144, 512, 64, 0.5),
+    (2000, 6144, 1024, 128, 0.0),
+    (4096, 3072, 8192, 128, 0.5),       # the Llama3.2-3B down_proj shape
 ]
 
 
 @pytest.mark.parametrize("M,N,K,G,p", WIDE_K_CASES)
 @pytest.mark.parametrize("beta", [0, 1])
-def test_gemm_k_320_wide_tiles(M, N, K, G, p, beta):
-    """Shapes whose 256 x 320 tiles fill whole rounds of the 256 compute units
-    run the 320-wide kernel alone; rows across every row tile, the ragged tail
-    and boundary rows are compared with the oracle; two runs agree bit for bit."""
+def test_gemm_k_round_filling_tiles(M, N, K, G, p, beta):
+    """Shapes whose 256 x 320 (or 256 x 192) tiles fill whole rounds of the 256
+    compute units run that kernel alone; rows across every row tile, the
+    ragged tail and boundary rows are compared with the oracle; two runs agree
+    bit for bit."""
     if torch.cuda.get_device_properties(0).multi_processor_count != 256:
         pytest.skip("tile rounds counted for 256 compute units")
     A = wl.random_bf16(M + K + 90, (M, K))
