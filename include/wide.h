@@ -166,7 +166,9 @@ int wide_gemm_mn_swiglu_ws(const wide_bf16 *A, int64_t lda, const wide_bf16 *Wg,
 /* Bytes of device workspace wide_gemm_mn_ws (swiglu = 0) or
  * wide_gemm_mn_swiglu_ws (swiglu = 1) needs on the current device: a small
  * header plus one fp32 output tile (256 or 320 rows) per compute unit (0
- * when K is too short for any split, or for sizes out of range). */
+ * when K is too short for any split, for sizes out of range, and for the
+ * fused SwiGLU over groups of a multiple of 64 but not of 128 features, whose
+ * tiles run in the static order, faster there than the scheduled one). */
 size_t wide_gemm_mn_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t G, int swiglu);
 
 /*

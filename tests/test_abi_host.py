@@ -119,6 +119,8 @@ def test_gemm_mn_workspace_plan(lib):
     assert f(8192, 4096, 4096, 512, 0) == hdr + cus * 320 * 256 * 4    # 256-wide tiles
     assert f(1000, 512, 1000, 64, 0) == hdr + cus * 256 * 64 * 4       # 64-wide tiles
     assert f(1000, 512, 960, 64, 0) == 0                                # 15 K-steps
+    assert f(8192, 17408, 5120, 64, 1) == 0 and f(8192, 17408, 5120, 192, 1) == 0  # SwiGLU raster
+    assert f(8192, 17408, 5120, 32, 1) > 0                              # narrower: scheduled
     assert f(0, 512, 4096, 64, 0) == 0 and f(10, 500, 4096, 64, 0) == 0  # bad sizes
 
 
