@@ -73,21 +73,27 @@ def test_gemm_mn_rows_near_2gib(big):
     check_gemm(got, ref.gemm_mn(A[rows], B, mask[rows], G), "gemm_mn rows near 2 GiB")
 
 
-@pytest.mark.parametrize("form", ["token", "ordered", "grouped"])
-def test_gemm_k_rows_near_2gib(big, form):
+@pytest.mark.parametrize("form,N", [("token", 256), ("token", 640), ("token", 384), ("ordered", 256),
+                                    ("grouped", 256)])
+def test_gemm_k_rows_near_2gib(big, form, N):
+    """N = 640 and 384: 256 row tiles x two column tiles of 320 or 192 fill
+    two rounds of 256 CUs, so the 320- and 192-wide token-order kernels run."""
     A, B, Ad, Bd, rows = big
+    if N != 256:
+        B = wl.random_bf16(704 + N, (N, K_BIG), 0.05)
+        Bd = to_dev(B, torch)
     G = 128
     mask = wl.random_mask(703, (M_BIG, K_BIG // G), 0.5)
     mask[rows[-1]] = 1
     md = to_dev(mask, torch)
-    say("gemm_k, A of 2 GiB", form)
-    out = torch.full((M_BIG, 256), float("nan"), dtype=torch.float32, device="cuda")
+    say("gemm_k, A of 2 GiB", form, N)
+    out = torch.full((M_BIG, N), float("nan"), dtype=torch.float32, device="cuda")
     if form == "grouped":
         perm, counts = W().reorder(md[None])
         W().gemm_k_grouped(Ad, Bd, G, perm[0], counts[0], out=out)
     else:
         order = W().order_by_pattern(md) if form == "ordered" else None
-        need = W().gemm_k_workspace_bytes(M_BIG, 256, K_BIG)
+        need = W().gemm_k_workspace_bytes(M_BIG, N, K_BIG)
         ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
         W().gemm_k(Ad, Bd, G, md, out=out, workspace=ws if need else None, order=order)
     torch.cuda.synchronize()
