@@ -128,26 +128,31 @@ __global__ __launch_bounds__(kAThreads) void attn_prefill_kernel(AttnArgs a) {
   __shared__ int sPos[kAq];
 
   // Heads of one KV group run on one XCD (they stream the same K/V); the
-  // heaviest causal tiles (latest positions) start first.
+  // heaviest causal tiles (latest positions) start first. Tiles are cut from
+  // the end of the group's active rows: tile y holds sorted rows
+  // [cnt - 256 (y + 1), cnt - 256 y), so only the earliest tile, whose causal
+  // key range is the shortest, can be partial. A partial latest tile costs
+  // nearly a full one (its few rows see every key); measured on MI355X at the
+  // Qwen3-14B prefill shape with half the groups on, the kernel's span went
+  // from 441 to 419 us with this cut.
   const int x = blockIdx.x;
   const int h = a.Hq % 8 == 0 ? (x % 8) * (a.Hq / 8) + x / 8 : x;
-  const int ntile = (a.Tq + kAq - 1) / kAq;
-  const int tile = ntile - 1 - (int)blockIdx.y;
   const int b = blockIdx.z;
   const int rep = a.Hq / a.Hk;
   const int g = h / rep;                  // KV head
   const int grp = h / (a.Hq / a.NG);      // routing group of the head
   const int cnt = a.counts[(size_t)b * a.NG + grp];
-  const int s0 = tile * kAq;
-  if (s0 >= cnt) return;  // level 0
+  const int s1 = cnt - (int)blockIdx.y * kAq;
+  if (s1 <= 0) return;  // level 0
+  const int s0 = max(0, s1 - kAq);
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int c = lane % 16, q = lane / 16;
-  if (tid < kAq) sPos[tid] = s0 + tid < cnt ? a.perm[((size_t)b * a.NG + grp) * a.Tq + s0 + tid] : -1;
+  if (tid < kAq) sPos[tid] = s0 + tid < s1 ? a.perm[((size_t)b * a.NG + grp) * a.Tq + s0 + tid] : -1;
   __syncthreads();
 
   const int delta = a.Tk - a.Tq;
   const int jmin = a.leftpad ? a.leftpad[b] : 0;
-  const int nvalid = min(kAq, cnt - s0);
+  const int nvalid = s1 - s0;
   const int wg_maxpos = sPos[nvalid - 1];
   const int wlo = wave * kAqw, wvalid = max(0, min(kAqw, nvalid - wlo));
   const int w_maxpos = wvalid > 0 ? sPos[wlo + wvalid - 1] : -1;
