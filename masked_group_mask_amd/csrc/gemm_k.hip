@@ -9,9 +9,10 @@
 // or L2 atomics) costs more than the multiply-adds it saves while the group
 // is short (G = 128 needs 2G = 256 MFMA flops per scattered value; the LDS
 // moves a value in and out more slowly than that). Here C stays in registers:
-//   - a workgroup owns C[m0:m0+256, n0:n0+256] (or n0+128 when N is not a
-//     multiple of 256) in original row order and runs the shared MFMA main
-//     loop over the whole K range;
+//   - a workgroup owns C[m0:m0+256, n0:n0+BN] in original row order and
+//     runs the shared MFMA main loop over the whole K range; BN = 320 or 192
+//     where those tiles fill whole rounds of the compute units, else 256 (or
+//     128 when N is not a multiple of 256);
 //   - the A slice of a row whose group is off for that token is never read
 //     (level 1): its load offset is set out of range, the buffer load moves
 //     no data and the stage holds zeros there, so the product adds exactly 0;
