@@ -38,6 +38,24 @@ constexpr int kKRasterM = 32;  // m-tiles per raster group (eng::tile_of)
 // of them (measured on MI355X, Qwen3-14B down_proj at 50%: 1.08 against 1.09
 // ms at 32, and 1.11 against 1.20 ms on all-ones masks)
 constexpr int kKRasterM320 = 16;
+// likewise 8 for the other widths when the column tiles split evenly over the
+// XCDs (each XCD then owns its own column blocks; measured on MI355X at the
+// Llama3.1-8B prefill shapes, N = 4096: down_proj 1.50 against 1.61 ms
+// masked and 1.67 against 1.86 on all-ones masks; the 32 above was measured
+// at N = 5120, whose 20 column tiles do not split over the XCDs)
+constexpr int kKRasterMXcd = 8;
+
+// The raster of the token-order tiles of width BN over NT column tiles. The
+// K-split fixup and the half-width tail tiles use it with BN = 256, so every
+// kernel of a launch finds a tile at the same place.
+__device__ __forceinline__ void k_tile_of(int BN, int L, int MT, int NT, int &mt, int &tn) {
+  if (BN == 320)
+    eng::tile_of<kKRasterM320>(L, MT, NT, mt, tn);
+  else if (NT % 8 == 0)
+    eng::tile_of<kKRasterMXcd>(L, MT, NT, mt, tn);
+  else
+    eng::tile_of<kKRasterM>(L, MT, NT, mt, tn);
+}
 
 // Tile order of the kernel over pattern-sorted rows. Sorted row tiles differ
 // in cost (the number of groups their rows keep), and the plain raster gives
@@ -214,7 +232,7 @@ __global__ __launch_bounds__(64 * W) void gemm_k_kernel(KArgs a) {
   int mt, tn, n0;
   int part = 0, nparts = 1, slot = 0;  // K slice of this workgroup; slot: split tile index
   if (a.split_tail) {  // half of a 256 x 256 tile of the raster
-    eng::tile_of<kKRasterM>(a.tile_base + (int)blockIdx.x / 2, MT, a.N / 256, mt, tn);
+    k_tile_of(256, a.tile_base + (int)blockIdx.x / 2, MT, a.N / 256, mt, tn);
     n0 = tn * 256 + ((int)blockIdx.x % 2) * BN;
   } else {
     int L = (int)blockIdx.x;
@@ -224,7 +242,7 @@ __global__ __launch_bounds__(64 * W) void gemm_k_kernel(KArgs a) {
       nparts = a.ksplit;
       L = a.head + slot;
     }
-    eng::tile_of<BN == 320 ? kKRasterM320 : kKRasterM>(a.tile_base + L, MT, a.N / BN, mt, tn);
+    k_tile_of(BN, a.tile_base + L, MT, a.N / BN, mt, tn);
     n0 = tn * BN;
   }
   const int m0 = mt * eng::kBM;
@@ -705,7 +723,7 @@ __global__ __launch_bounds__(256) void gemm_k_fixup_kernel(KArgs a) {
   if (a.order)
     ord_tile_of(a.head + slot, a.head, MT, mt, tn);
   else
-    eng::tile_of<kKRasterM>(a.head + slot, MT, a.N / 256, mt, tn);
+    k_tile_of(256, a.head + slot, MT, a.N / 256, mt, tn);
   const int pos = mt * eng::kBM + r;
   if (pos >= a.M) return;
   const int m = a.order ? a.order[pos] : pos;
