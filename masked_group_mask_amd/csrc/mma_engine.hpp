@@ -262,7 +262,8 @@ __device__ __forceinline__ void mainloop(int nk, Issue &issue, lds_u16 *a0, lds_
 // concurrently running tiles share A rows and B rows in that XCD's L2.
 // Measured on MI355X (Qwen3-14B prefill shapes): GM = 8 suits the GEMM-MN
 // raster (gate/up on all-ones masks 2.27 ms against 2.36 at GM = 4 and 2.47
-// at GM = 32), GM = 32 the GEMM-K raster (down_proj 1.14 against 1.17 ms).
+// at GM = 32); the GEMM-K kernel picks GM per tile width and column split
+// (its own raster helper states the measured choices).
 template <int GM>
 __device__ __forceinline__ void tile_of(int L, int MT, int NT, int &mt, int &tn) {
   int x = 0, i = L, NX = NT;
