@@ -38,11 +38,11 @@ def log(*a):
 
 
 def time_steps(layer, which, steps, warmup, torch):
-    from masked_group_mask_amd.layer import PREFILL_OPS
+    ops = layer.ops
     for _ in range(warmup):
         layer.step(which)
     torch.cuda.synchronize()
-    n_ev = len(PREFILL_OPS) + 1
+    n_ev = len(ops) + 1
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -51,7 +51,7 @@ def time_steps(layer, which, steps, warmup, torch):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     per_op = {op: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(steps)]))
-              for j, op in enumerate(PREFILL_OPS)}
+              for j, op in enumerate(ops)}
     step_ms = [evs[i][0].elapsed_time(evs[i][-1]) for i in range(steps)]
     spread = {"p10": float(np.percentile(step_ms, 10)), "median": float(np.median(step_ms)),
               "p90": float(np.percentile(step_ms, 90))}
@@ -525,17 +525,19 @@ def cpu_baseline(s, host, rows: int):
         limiter = None
     rng = np.random.default_rng(123)
     sel = np.sort(rng.choice(s.M, size=min(rows, s.M), replace=False))
-    ma = host["mask_attn"].reshape(s.M, s.Hk)[sel]
     mf = host["mask_ffn"].reshape(s.M, s.NG_ffn)[sel]
     X = host["x"][sel]
+    fl = 0
     t0 = time.perf_counter()
-    q = ref.round_bf16(ref.gemm_mn(X, host["w_q"], ma, s.G_attn))
-    full_mask = host["mask_attn"]
-    # attention needs Q only at the sampled positions; other rows are unused
-    Qs = np.zeros((s.B, s.T, s.Hq, s.d), np.uint16)
-    Qs[0, sel] = ref.to_bf16_bits(q).reshape(len(sel), s.Hq, s.d)
-    o = ref.attention(Qs, host["k"], host["v"], full_mask, queries=[(0, int(t)) for t in sel])
-    ref.gemm_k(ref.to_bf16_bits(ref.round_bf16(o)).reshape(len(sel), -1), host["w_o"], ma, s.G_attn)
+    if s.Hq:
+        ma = host["mask_attn"].reshape(s.M, s.Hk)[sel]
+        q = ref.round_bf16(ref.gemm_mn(X, host["w_q"], ma, s.G_attn))
+        full_mask = host["mask_attn"]
+        # attention needs Q only at the sampled positions; other rows are unused
+        Qs = np.zeros((s.B, s.T, s.Hq, s.d), np.uint16)
+        Qs[0, sel] = ref.to_bf16_bits(q).reshape(len(sel), s.Hq, s.d)
+        o = ref.attention(Qs, host["k"], host["v"], full_mask, queries=[(0, int(t)) for t in sel])
+        ref.gemm_k(ref.to_bf16_bits(ref.round_bf16(o)).reshape(len(sel), -1), host["w_o"], ma, s.G_attn)
     hh = ref.round_bf16(ref.swiglu(ref.gemm_mn(X, host["w_gate"], mf, s.G_ffn),
                                    ref.gemm_mn(X, host["w_up"], mf, s.G_ffn)))
     ref.gemm_k(ref.to_bf16_bits(hh), host["w_down"], mf, s.G_ffn)
@@ -543,10 +545,11 @@ def cpu_baseline(s, host, rows: int):
     if limiter is not None:
         limiter.unregister()
     # active FLOPs of exactly the sampled rows
-    fl = (metrics.gemm_mn_flops(ma, s.D, s.G_attn) + metrics.gemm_k_flops(ma, s.D, s.G_attn)
-          + 2 * metrics.gemm_mn_flops(mf, s.D, s.G_ffn) + metrics.gemm_k_flops(mf, s.D, s.G_ffn))
-    rep = s.Hq // s.Hk
-    fl += int(sum(4 * s.d * rep * int(ma[i].sum()) * (int(t) + 1) for i, t in enumerate(sel)))
+    fl += 2 * metrics.gemm_mn_flops(mf, s.D, s.G_ffn) + metrics.gemm_k_flops(mf, s.D, s.G_ffn)
+    if s.Hq:
+        fl += metrics.gemm_mn_flops(ma, s.D, s.G_attn) + metrics.gemm_k_flops(ma, s.D, s.G_attn)
+        rep = s.Hq // s.Hk
+        fl += int(sum(4 * s.d * rep * int(ma[i].sum()) * (int(t) + 1) for i, t in enumerate(sel)))
     cpu = "unknown"
     try:
         with open("/proc/cpuinfo") as f:
@@ -565,14 +568,18 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="qwen14b_prefill")
-    ap.add_argument("--sparsity", type=float, default=0.5)
-    ap.add_argument("--g-ffn", type=int, default=128)
+    ap.add_argument("--sparsity", type=float, default=None,
+                    help="fraction of the attention and FFN groups off (default: the workload's own)")
+    ap.add_argument("--sparsity-attn", type=float, default=None, help="overrides --sparsity for attention")
+    ap.add_argument("--sparsity-ffn", type=float, default=None, help="overrides --sparsity for the FFN")
+    ap.add_argument("--g-ffn", type=int, default=None, help="FFN group size (default: the workload's own)")
     ap.add_argument("--cpu-rows", type=int, default=8192)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-router", action="store_true")
     ap.add_argument("--no-torch-dense", action="store_true")
+    ap.add_argument("--no-leftpad", action="store_true", help="skip the two left-padded sequences leg")
     ap.add_argument("--no-app-a", action="store_true",
                     help="skip the naive / grouped / fused GEMM pruning comparison (the page's Appendix A)")
     ap.add_argument("--ordered-k", default="", metavar="OPS",
@@ -619,9 +626,19 @@ def main():
             f"{2 * n * 4 / (ms * 1e-3) / 1e9:.0f} GB/s read + write")
         return
 
-    p = 1.0 - args.sparsity
-    s = wl.shape(args.workload, p_attn=p, p_ffn=p, G_ffn=args.g_ffn)
-    log(f"generating {s.name}: T={s.T} D={s.D} D'={s.Dff} Hq={s.Hq} Hk={s.Hk} G_ffn={s.G_ffn} p={p}")
+    over = {}
+    for key, v in (("p_attn", args.sparsity_attn), ("p_ffn", args.sparsity_ffn)):
+        v = args.sparsity if v is None else v
+        if v is not None:
+            over[key] = 1.0 - v
+    if args.g_ffn is not None:
+        over["G_ffn"] = args.g_ffn
+    s = wl.shape(args.workload, **over)
+    if s.T == 1:
+        print("bench.py times prefill workloads; the decode step is its own leg", file=sys.stderr)
+        sys.exit(2)
+    log(f"generating {s.name}: T={s.T} D={s.D} D'={s.Dff} Hq={s.Hq} Hk={s.Hk} G_ffn={s.G_ffn} "
+        f"p_attn={s.p_attn} p_ffn={s.p_ffn} ({s.ffn_rule})")
     t0 = time.perf_counter()
     host = wl.make_layer(s, seed=0)
     log(f"inputs ready in {time.perf_counter() - t0:.1f} s")
@@ -629,8 +646,8 @@ def main():
     ordered = tuple(o for o in args.ordered_k.split(",") if o)
     grouped = tuple(o for o in args.grouped_k.split(",") if o)
     layer = PrefillLayer(s, host, with_dense=not args.no_dense, ordered_k=ordered, grouped_k=grouped)
-    flops = metrics.layer_flops(s, host["mask_attn"], host["mask_ffn"])
-    ones_a = np.ones_like(host["mask_attn"])
+    flops = metrics.layer_flops(s, host.get("mask_attn"), host["mask_ffn"])
+    ones_a = np.ones_like(host["mask_attn"]) if s.Hq else None
     ones_f = np.ones_like(host["mask_ffn"])
     dense_flops = metrics.layer_flops(s, ones_a, ones_f)
     total_flops = sum(flops.values())
@@ -667,11 +684,11 @@ def main():
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": s.name, "B": s.B, "T": s.T, "hidden": s.D, "ffn": s.Dff,
                    "q_heads": s.Hq, "kv_heads": s.Hk, "head_dim": s.d, "G_attn": s.G_attn,
-                   "G_ffn": s.G_ffn, "sparsity_attn": args.sparsity, "sparsity_ffn": args.sparsity,
-                   "seed": 0,
+                   "G_ffn": s.G_ffn, "sparsity_attn": round(1.0 - s.p_attn, 6) if s.Hq else None,
+                   "sparsity_ffn": round(1.0 - s.p_ffn, 6), "ffn_mask_rule": s.ffn_rule, "seed": 0,
                    # GEMM-K form of o_proj / down_proj in the masked step (all-ones: token order)
                    "gemm_k": {op: ("pattern_order" if op in ordered else "per_group" if op in grouped
-                                   else "token_order") for op in ("o_proj", "down_proj")}},
+                                   else "token_order") for op in ("o_proj", "down_proj") if op in flops}},
         "speedup_vs_dense": (dense_ms / ms) if dense_ms else None,
         "ideal_speedup": sum(dense_flops.values()) / total_flops,
         "dense_ms_per_step": dense_ms,
@@ -690,7 +707,7 @@ def main():
     if not args.no_dense and not args.no_torch_dense and s.Hq:
         out["torch_dense"] = bench_torch_dense(torch, s, out["dense_per_op_ms"])
         log("torch dense GEMMs (ms): " + ", ".join(f"{k} {v:.3f}" for k, v in out["torch_dense"]["per_op_ms"].items()))
-    if not args.no_dense:
+    if not args.no_dense and not args.no_leftpad:
         log("timing two left-padded sequences")
         out["prefill_b2_leftpad"] = bench_batched_leftpad(torch, wl, metrics)
         log(f"B=2 leftpad: {out['prefill_b2_leftpad']['ms_per_step']:.3f} ms/step, "

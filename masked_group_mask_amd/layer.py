@@ -15,6 +15,8 @@ import torch
 from . import _lib as mg
 
 PREFILL_OPS = ("reorder", "q_proj", "attention", "o_proj", "gate_up_swiglu", "down_proj")
+# A shape without query heads is an FFN-only layer: the FFN reorder, gate/up, down.
+FFN_OPS = ("reorder", "gate_up_swiglu", "down_proj")
 DECODE_OPS = ("q_proj", "attention", "o_proj", "gate_up_swiglu", "down_proj")
 
 
@@ -27,7 +29,8 @@ def to_device(x: np.ndarray) -> torch.Tensor:
 
 
 class PrefillLayer:
-    """One masked layer of shape `s` (workloads.LayerShape) on the GPU."""
+    """One masked layer of shape `s` (workloads.LayerShape) on the GPU; with
+    s.Hq == 0 only its FFN (the ops in FFN_OPS)."""
 
     def __init__(self, s, host: dict, with_dense: bool = True, scheduled_mn: dict | None = None,
                  ordered_k: tuple = (), leftpad=None, grouped_k: tuple = ()):
@@ -60,18 +63,35 @@ class PrefillLayer:
         if scheduled_mn is None:
             scheduled_mn = {"masked": ("q_proj", "gate_up_swiglu"), "dense": ()}
         self.scheduled_mn = {k: tuple(v) for k, v in scheduled_mn.items()}
+        self.attn = s.Hq > 0
+        self.ops = PREFILL_OPS if self.attn else FFN_OPS
+        if not self.attn and (leftpad is not None or "o_proj" in self.ordered_k + self.grouped_k):
+            raise ValueError("an FFN-only layer has no o_proj and no left padding")
         d = lambda k: to_device(host[k])  # noqa: E731
         self.x = d("x")
-        self.wq, self.wo = d("w_q"), d("w_o")
         self.wg, self.wu, self.wd = d("w_gate"), d("w_up"), d("w_down")
-        self.k, self.v = d("k"), d("v")
-        ma, mf = d("mask_attn"), d("mask_ffn")
+        mf = d("mask_ffn")
+        ma = d("mask_attn") if self.attn else None
         self.masks = {"masked": (ma, mf)}
         if with_dense:
-            self.masks["dense"] = (torch.ones_like(ma), torch.ones_like(mf))
+            self.masks["dense"] = (None if ma is None else torch.ones_like(ma), torch.ones_like(mf))
         dev = self.x.device
         M, B, T = s.M, s.B, s.T
         i32 = torch.int32
+        self.perm_f = torch.empty((1, s.NG_ffn, M), dtype=i32, device=dev)
+        self.cnt_f = torch.empty((1, s.NG_ffn), dtype=i32, device=dev)
+        self.order_f = torch.empty(M, dtype=i32, device=dev)
+        # Every consumer reads only the active entries of its input (GEMM-K
+        # loads only the active (row, group) segments, attention gathers active
+        # rows), so the intermediate buffers need no zero-initialisation.
+        self.h = torch.empty((M, s.Dff), dtype=torch.bfloat16, device=dev)
+        self.y_ffn = torch.empty((M, s.D), dtype=torch.float32, device=dev)
+        wsb = max(mg.gemm_k_workspace_bytes(M, s.D, s.Dff), mg.gemm_mn_workspace_bytes(M, s.Dff, s.D, s.G_ffn, True))
+        if not self.attn:
+            self.ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
+            return
+        self.wq, self.wo = d("w_q"), d("w_o")
+        self.k, self.v = d("k"), d("v")
         # Attention reorders each sequence's routing columns (batch B, rows
         # T); the GEMMs reorder the flattened tokens (batch 1, rows B*T). With
         # B = 1 the two coincide and one reorder serves both.
@@ -84,22 +104,13 @@ class PrefillLayer:
             self.perm_q, self.cnt_q = self.perm_a, self.cnt_a
         # left padding of each sequence: keys before it are not attended
         self.leftpad = None if leftpad is None else torch.tensor(list(leftpad), dtype=i32, device=dev)
-        self.perm_f = torch.empty((1, s.NG_ffn, M), dtype=i32, device=dev)
-        self.cnt_f = torch.empty((1, s.NG_ffn), dtype=i32, device=dev)
         self.order_a = torch.empty(M, dtype=i32, device=dev)
-        self.order_f = torch.empty(M, dtype=i32, device=dev)
-        # Every consumer reads only the active entries of its input (GEMM-K
-        # loads only the active (row, group) segments, attention gathers active
-        # rows), so the intermediate buffers need no zero-initialisation.
         self.q = torch.empty((M, s.Hq * s.d), dtype=torch.bfloat16, device=dev)
         self.o = torch.empty((B, T, s.Hq, s.d), dtype=torch.bfloat16, device=dev)
-        self.h = torch.empty((M, s.Dff), dtype=torch.bfloat16, device=dev)
         self.y_attn = torch.empty((M, s.D), dtype=torch.float32, device=dev)
-        self.y_ffn = torch.empty((M, s.D), dtype=torch.float32, device=dev)
         # One workspace for every GEMM of the step (they run in turn on one stream).
-        wsb = max(mg.gemm_k_workspace_bytes(M, s.D, s.Hq * s.d), mg.gemm_k_workspace_bytes(M, s.D, s.Dff),
-                  mg.gemm_mn_workspace_bytes(M, s.Hq * s.d, s.D, s.G_attn, False),
-                  mg.gemm_mn_workspace_bytes(M, s.Dff, s.D, s.G_ffn, True))
+        wsb = max(wsb, mg.gemm_k_workspace_bytes(M, s.D, s.Hq * s.d),
+                  mg.gemm_mn_workspace_bytes(M, s.Hq * s.d, s.D, s.G_attn, False))
         self.ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
 
     def _ordered(self, op: str, which: str) -> bool:
@@ -113,19 +124,21 @@ class PrefillLayer:
 
     def run(self, op: str, which: str = "masked") -> None:
         """Enqueue one op of the step on the current stream; it reads whatever
-        the buffers hold (run the ops in PREFILL_OPS order for a layer pass)."""
+        the buffers hold (run the ops in `self.ops` order for a layer pass)."""
         s = self.s
         ma, mf = self.masks[which]
         if op == "reorder":
-            mg.reorder(ma, self.perm_a, self.cnt_a)
-            if s.B > 1:
-                mg.reorder(ma.view(1, s.M, s.Hk), self.perm_q, self.cnt_q)
+            if self.attn:
+                mg.reorder(ma, self.perm_a, self.cnt_a)
+                if s.B > 1:
+                    mg.reorder(ma.view(1, s.M, s.Hk), self.perm_q, self.cnt_q)
             mg.reorder(mf.view(1, s.M, s.NG_ffn), self.perm_f, self.cnt_f)
-            sorts = [(op, m, o) for op, m, o in (("o_proj", ma.view(s.M, s.Hk), self.order_a),
-                                                 ("down_proj", mf.view(s.M, s.NG_ffn), self.order_f))
-                     if self._ordered(op, which)]
-            for _, m, o in sorts:
-                mg.order_by_pattern(m, o)
+            if self._ordered("o_proj", which):
+                mg.order_by_pattern(ma.view(s.M, s.Hk), self.order_a)
+            if self._ordered("down_proj", which):
+                mg.order_by_pattern(mf.view(s.M, s.NG_ffn), self.order_f)
+        elif op not in self.ops:
+            raise ValueError(f"op {op!r} is not part of this layer")
         elif op == "q_proj":
             mg.gemm_mn(self.x, self.wq, s.G_attn, perm=self.perm_q[0], counts=self.cnt_q[0],
                        out=self.q, workspace=self._mn_ws("q_proj", which))
@@ -154,7 +167,7 @@ class PrefillLayer:
         """One pass of the routed path; events[i] / events[i + 1] bracket op i."""
         if events is not None:
             events[0].record()
-        for i, op in enumerate(PREFILL_OPS):
+        for i, op in enumerate(self.ops):
             self.run(op, which)
             if events is not None:
                 events[i + 1].record()

@@ -150,20 +150,23 @@ def test_prefill_layer_batched_leftpad():
 
 
 def test_llama3b_ffn_full_size():
-    """Llama3.2-3B-shaped FFN, T=4096, per-group Beta(2,2) activation rates."""
-    import masked_group_mask_amd as mg
+    """Llama3.2-3B-shaped FFN, T=4096, per-group Beta(2,2) activation rates,
+    through the FFN-only layer driver (the launch sequence bench.py times for
+    this workload: reorder, scheduled gate/up + SwiGLU, down_proj)."""
+    from masked_group_mask_amd.layer import FFN_OPS, PrefillLayer
     s = wl.shape("llama3b_ffn")
     say("full-size ffn", s.name)
-    host = wl.make_layer(s, seed=0, parts=("ffn",))
-    md = to_dev(host["mask_ffn"], torch)
-    perm, counts = mg.reorder(md)
-    h = mg.gemm_mn_swiglu(to_dev(host["x"], torch), to_dev(host["w_gate"], torch),
-                          to_dev(host["w_up"], torch), s.G_ffn, perm=perm[0], counts=counts[0])
-    y = mg.gemm_k(h, to_dev(host["w_down"], torch), s.G_ffn, md.view(s.M, s.NG_ffn))
+    host = wl.make_layer(s, seed=0)
+    assert "mask_attn" not in host
+    layer = PrefillLayer(s, host, with_dense=False)
+    assert layer.ops == FFN_OPS
+    layer.step("masked")
     torch.cuda.synchronize()
-    check_reorder(host["mask_ffn"][0], perm.cpu().numpy()[0], counts.cpu().numpy()[0])
+    check_reorder(host["mask_ffn"][0], layer.perm_f.cpu().numpy()[0], layer.cnt_f.cpu().numpy()[0])
     rows = sample_rows(s.M, 12)
-    check_ffn(s, host, rows, bits_of(h)[rows], y.cpu().numpy()[rows].astype(np.float64))
+    check_ffn(s, host, rows, bits_of(layer.h)[rows], layer.y_ffn.cpu().numpy()[rows].astype(np.float64))
+    with pytest.raises(ValueError):
+        layer.run("attention")
 
 
 def test_tiny_ffn_every_entry():
