@@ -62,29 +62,34 @@ def check_ffn(s, host, rows, h_gpu_bits, y_gpu):
     check_gemm(y_gpu, want_y, f"{s.name} down_proj")
 
 
+# (workload, shape overrides, GEMM-K ops over pattern-sorted rows)
 PREFILL = [
-    ("llama8b_prefill", {}),
-    ("qwen14b_prefill", {"p_attn": 0.5, "p_ffn": 0.5, "G_ffn": 128}),
-    ("qwen14b_prefill", {"p_attn": 0.5, "p_ffn": 0.5, "G_ffn": 64}),
-    ("qwen14b_prefill", {"p_attn": 0.5, "p_ffn": 0.5, "G_ffn": 256}),
-    ("qwen14b_prefill", {"p_attn": 0.75, "p_ffn": 0.75, "G_ffn": 64}),
-    ("qwen14b_prefill", {"p_attn": 0.75, "p_ffn": 0.75, "G_ffn": 128}),
-    ("qwen14b_prefill", {"p_attn": 0.75, "p_ffn": 0.75, "G_ffn": 256}),
+    ("llama8b_prefill", {}, ()),
+    ("llama8b_prefill", {}, ("o_proj",)),
+    ("qwen14b_prefill", {"p_attn": 0.5, "p_ffn": 0.5, "G_ffn": 128}, ()),
+    ("qwen14b_prefill", {"p_attn": 0.5, "p_ffn": 0.5, "G_ffn": 64}, ()),
+    ("qwen14b_prefill", {"p_attn": 0.5, "p_ffn": 0.5, "G_ffn": 256}, ()),
+    ("qwen14b_prefill", {"p_attn": 0.75, "p_ffn": 0.75, "G_ffn": 64}, ()),
+    ("qwen14b_prefill", {"p_attn": 0.75, "p_ffn": 0.75, "G_ffn": 128}, ()),
+    ("qwen14b_prefill", {"p_attn": 0.75, "p_ffn": 0.75, "G_ffn": 256}, ()),
 ]
 
 
-@pytest.mark.parametrize("name,over", PREFILL, ids=lambda v: str(v))
-def test_prefill_layer_full_size(name, over):
+@pytest.mark.parametrize("name,over,ordered", PREFILL, ids=lambda v: str(v))
+def test_prefill_layer_full_size(name, over, ordered):
     from masked_group_mask_amd.layer import PrefillLayer
     s = wl.shape(name, **over)
-    say("full-size prefill", s.name, over)
+    say("full-size prefill", s.name, over, ordered)
     host = wl.make_layer(s, seed=0)
-    layer = PrefillLayer(s, host, with_dense=False)
+    layer = PrefillLayer(s, host, with_dense=False, ordered_k=ordered)
     layer.step("masked")
     torch.cuda.synchronize()
 
     check_reorder(host["mask_attn"][0], layer.perm_a.cpu().numpy()[0], layer.cnt_a.cpu().numpy()[0])
     check_reorder(host["mask_ffn"][0], layer.perm_f.cpu().numpy()[0], layer.cnt_f.cpu().numpy()[0])
+    if ordered:
+        # the row order the sorted GEMM-K ran over is a permutation of the tokens
+        assert np.array_equal(np.sort(layer.order_a.cpu().numpy()), np.arange(s.M))
 
     rows = sample_rows(s.M, 11)
     ma2 = host["mask_attn"].reshape(s.M, s.Hk)
