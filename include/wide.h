@@ -235,7 +235,8 @@ int wide_gemm_k(const wide_bf16 *A, int64_t lda, const wide_bf16 *B, int64_t ldb
  * split into slices of K computed by separate workgroups; the workspace holds
  * the partial tiles of all slices but the last, and a second kernel adds them
  * into C. Shapes whose 256 x 320 tiles fill whole rounds (N a multiple of 320,
- * G of 64) run those tiles instead, with no split, as wide_gemm_k does.
+ * G of 64) run those tiles instead, with no split, as wide_gemm_k does; so do
+ * shapes whose 256 x 192 tiles fill whole rounds where 256 x 256 ones do not.
  *   workspace: device memory of at least wide_gemm_k_workspace_bytes(M, N, K)
  *     bytes, 16-byte aligned, not overlapping A, B, C, mask or order. Its
  *     contents on entry are ignored and overwritten; calls that share a
