@@ -103,3 +103,40 @@ def test_prefill_and_decode_steps_on_a_side_stream():
     side.synchronize()
     for name, a, b in zip(outs, snap(dec, outs), want):
         assert np.array_equal(a, b), f"decode on a side stream: {name} differs"
+
+
+def test_two_streams_with_their_own_workspaces():
+    """Scheduled GEMM-MN (device-side tile schedule in the workspace) and K-split
+    GEMM-K on two streams at once, each with its own workspace: both results
+    equal the same calls made one after the other."""
+    import masked_group_mask_amd as mg
+    M, N, K, G = 2048, 1280, 1280, 640
+    cases = []
+    for seed in (21, 22):
+        A = to_dev(wl.random_bf16(seed, (M, K)), torch)
+        B = to_dev(wl.random_bf16(seed + 100, (N, K), 0.05), torch)
+        mask = to_dev(wl.random_mask(seed + 200, (1, M, N // G), 0.5), torch)
+        kmask = to_dev(wl.random_mask(seed + 300, (M, K // G), 0.5), torch)
+        perm, cnt = mg.reorder(mask)
+        ws_mn = torch.empty(max(mg.gemm_mn_workspace_bytes(M, N, K, G, False), 16), dtype=torch.uint8, device="cuda")
+        ws_k = torch.empty(max(mg.gemm_k_workspace_bytes(M, N, K), 16), dtype=torch.uint8, device="cuda")
+        c_ref = mg.gemm_mn(A, B, G, perm=perm[0], counts=cnt[0], workspace=ws_mn)
+        k_ref = mg.gemm_k(A, B, G, kmask, workspace=ws_k)
+        cases.append((A, B, perm, cnt, kmask, ws_mn, ws_k, c_ref, k_ref))
+    torch.cuda.synchronize()
+    say("two streams, own workspaces")
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = []
+    for st in streams:
+        st.wait_stream(torch.cuda.current_stream())
+    for st, (A, B, perm, cnt, kmask, ws_mn, ws_k, _, _) in zip(streams, cases):
+        with torch.cuda.stream(st):
+            ws_mn.fill_(255)  # stale workspace contents must not matter
+            ws_k.fill_(255)
+            outs.append((mg.gemm_mn(A, B, G, perm=perm[0], counts=cnt[0], workspace=ws_mn),
+                         mg.gemm_k(A, B, G, kmask, workspace=ws_k)))
+    for st in streams:
+        st.synchronize()
+    for (c, k), case in zip(outs, cases):
+        assert torch.equal(c, case[7]), "scheduled GEMM-MN differs when run beside another stream"
+        assert torch.equal(k, case[8]), "GEMM-K differs when run beside another stream"
